@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle (oracle/prism_oracle.c) against brute force on
+tiny inputs, a library routine (numpy integer / float64 matmul, torch
+scaled_dot_product_attention in float64), a closed form, an invariant of
+the method, or the hand-derived example in tests/golden.  Passages: Prism
+Attention page (arXiv 2610.22985) Sec. 4 Overview, Sec. 4.1, Sec. 4.2,
+Sec. 5.1 Implementation Details.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from token_level_sparse_prism_amd import workload as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- brute force helpers
+def argmax_select(scores, k):
+    """Repeated argmax (highest score, lowest index among equals), k times; ascending, unpadded."""
+    remaining = list(range(len(scores)))
+    chosen = []
+    for _ in range(min(k, len(scores))):
+        best = remaining[0]
+        for t in remaining[1:]:
+            if scores[t] > scores[best]:
+                best = t
+        chosen.append(best)
+        remaining.remove(best)
+    return sorted(chosen)
+
+
+def pad(lst, n):
+    return np.array(list(lst) + [-1] * (n - len(lst)), dtype=np.int32)
+
+
+def int_case(rng, G, D, T, ties=False):
+    """Integer-valued q (group amax exactly 127) and K rows (row amax exactly 127):
+    the quantizer is then the identity (scale 1), so the score is a plain integer dot product."""
+    q = rng.integers(-127, 128, size=(G, D)).astype(np.float32)
+    q[0, 0] = 127.0
+    K = rng.integers(-127, 128, size=(T, D)).astype(np.float32)
+    K[:, 0] = np.where(rng.random(T) < 0.5, 127.0, -127.0)
+    if ties and T > 2:
+        K[1::3] = K[0]  # duplicated rows -> equal scores
+    return q, K
+
+
+# ---------------------------------------------------------------- quantizer (O1, O2)
+def test_quantizer_bounds_and_extremes():
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((500, 128)).astype(np.float32)
+    K *= (10.0 ** rng.uniform(-6, 6, size=(500, 1))).astype(np.float32)
+    K[7] = 0.0
+    Kq, s = oracle.quantize_rows(K)
+    assert Kq.min() >= -127 and Kq.max() <= 127
+    assert s[7] == 0.0 and not Kq[7].any()
+    for r in range(500):
+        if r == 7:
+            continue
+        j = int(np.argmax(np.abs(K[r])))
+        assert Kq[r, j] == (127 if K[r, j] > 0 else -127)
+        amax = np.abs(K[r]).max()
+        err = np.abs(K[r].astype(np.float64) - float(s[r]) * Kq[r].astype(np.float64)).max()
+        assert err <= 0.5 * float(s[r]) * (1 + 1e-5) + 1e-6 * amax
+        assert s[r] == np.float32(amax) / np.float32(127.0)
+
+
+def test_quantizer_identity_and_power_of_two_scaling():
+    rng = np.random.default_rng(12)
+    _, K = int_case(rng, 1, 64, 40)
+    Kq, s = oracle.quantize_rows(K)
+    assert np.array_equal(Kq.astype(np.float32), K) and np.all(s == 1.0)
+    Kq2, s2 = oracle.quantize_rows(K * np.float32(2.0 ** -7))
+    assert np.array_equal(Kq2, Kq) and np.all(s2 == np.float32(2.0 ** -7))
+
+
+def test_quantizer_round_half_even():
+    # amax 127 -> 127/amax = 1, so codes are rint of the values themselves
+    K = np.array([[127.0, 62.5, -62.5, 63.5, 0.5, -1.5, 2.5, 3.49]], dtype=np.float32)
+    Kq, s = oracle.quantize_rows(K)
+    assert Kq[0].tolist() == [127, 62, -62, 64, 0, -2, 2, 3]
+
+
+def test_query_group_shares_one_scale():
+    rng = np.random.default_rng(13)
+    base = rng.standard_normal(128).astype(np.float32)
+    base[5] = 8.0  # the group's absmax sits in head 0
+    q = np.stack([base, base * np.float32(0.5), np.zeros(128, np.float32)])
+    qi, s = oracle.quantize_query(q)
+    assert qi[0, 5] == 127 and s == np.float32(8.0) / np.float32(127.0)
+    # one shared scale: head 1 codes are (about) half of head 0's, head 2 stays zero
+    assert np.abs(qi[1].astype(int) * 2 - qi[0].astype(int)).max() <= 2
+    assert not qi[2].any()
+
+
+# ---------------------------------------------------------------- hand-derived example
+def test_hand_example():
+    ex = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    q = np.array(ex["q"], dtype=np.float32)
+    K = np.array(ex["K"], dtype=np.float32)
+    qi, _ = oracle.quantize_query(q)
+    assert qi.tolist() == ex["q_codes"]
+    Kq, s = oracle.quantize_rows(K)
+    assert np.array_equal(Kq.astype(np.float32), K) and s.tolist() == ex["K_scales"]
+    for kp_s, expect in ex["pools"].items():
+        pool, scores = oracle.propose_unit(q, Kq, s, K.shape[0], int(kp_s))
+        assert scores.tolist() == ex["scores"]
+        assert pool.tolist() == expect, kp_s
+    f = ex["K_scaled"]["factor"]
+    Kq2, s2 = oracle.quantize_rows(K * np.float32(f))
+    assert np.array_equal(Kq2, Kq) and np.all(s2 == np.float32(ex["K_scaled"]["scales"]))
+    _, scores2 = oracle.propose_unit(q, Kq2, s2, K.shape[0], 3)
+    assert scores2.tolist() == [x * f for x in ex["scores"]]
+
+
+# ---------------------------------------------------------------- proposal (O3, O4)
+@pytest.mark.parametrize("G,agg", [(1, oracle.AGG_SUM), (4, oracle.AGG_SUM), (8, oracle.AGG_SUM),
+                                   (4, oracle.AGG_MAX), (8, oracle.AGG_MAX)])
+def test_proposal_scores_integer_case(G, agg):
+    rng = np.random.default_rng(20 + G + 10 * agg)
+    D, T = 128, 300
+    q, K = int_case(rng, G, D, T)
+    Kq, s = oracle.quantize_rows(K)
+    pool, scores = oracle.propose_unit(q, Kq, s, T, 50, agg)
+    per_head = K.astype(np.int64) @ q.astype(np.int64).T  # library integer matmul [T, G]
+    expect = per_head.sum(1) if agg == oracle.AGG_SUM else per_head.max(1)
+    assert np.array_equal(scores.astype(np.int64), expect)
+    assert pool.tolist() == pad(argmax_select(expect.tolist(), 50), 50).tolist()
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 17, 64, 257])
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_pool_equals_repeated_argmax(T, G, D):
+    rng = np.random.default_rng(T * 1000 + G * 10 + D)
+    if (T + G + D) % 2:
+        q, K = int_case(rng, G, D, T, ties=True)
+    else:
+        q = rng.standard_normal((G, D)).astype(np.float32)
+        K = rng.standard_normal((T, D)).astype(np.float32)
+        if T > 3:
+            K[2::4] = K[1]
+    Kq, s = oracle.quantize_rows(K)
+    for kp in sorted({1, max(T - 1, 1), T, T + 5, min(16, T)}):
+        for agg in (oracle.AGG_SUM, oracle.AGG_MAX):
+            pool, scores = oracle.propose_unit(q, Kq, s, T, kp, agg)
+            assert pool.tolist() == pad(argmax_select(scores.tolist(), kp), kp).tolist()
+
+
+def test_all_equal_scores_take_lowest_indices():
+    rng = np.random.default_rng(3)
+    K = np.tile(rng.standard_normal((1, 64)).astype(np.float32), (100, 1))
+    q = rng.standard_normal((4, 64)).astype(np.float32)
+    Kq, s = oracle.quantize_rows(K)
+    pool, scores = oracle.propose_unit(q, Kq, s, 100, 30)
+    assert len(set(scores.tolist())) == 1
+    assert pool.tolist() == list(range(30))
+
+
+def test_zero_query_gives_prefix_pool_and_mean():
+    """P7: q = 0 makes every score exactly 0; the pool and index set are the lowest indices."""
+    rng = np.random.default_rng(4)
+    T, D, G = 600, 128, 4
+    K = rng.standard_normal((T, D)).astype(np.float32)
+    V = rng.standard_normal((T, D)).astype(np.float32)
+    q = np.zeros((G, D), np.float32)
+    Kq, s = oracle.quantize_rows(K)
+    pool, scores = oracle.propose_unit(q, Kq, s, T, 256)
+    assert np.all(scores == 0) and not np.signbit(scores).any()
+    assert pool.tolist() == list(range(256))
+    r = oracle.refine_unit(q, K, V, T, pool, 64)
+    assert r["idx"].tolist() == list(range(64))
+    np.testing.assert_allclose(r["out"], np.tile(V[:64].astype(np.float64).mean(0), (G, 1)),
+                               rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], math.log(64), rtol=0, atol=1e-12)
+
+
+def test_pool_nesting():
+    """P11: the pool for kp1 < kp2 is contained in the pool for kp2."""
+    rng = np.random.default_rng(5)
+    T, D, G = 2000, 128, 4
+    q = rng.standard_normal((G, D)).astype(np.float32)
+    K = rng.standard_normal((T, D)).astype(np.float32)
+    K[::7] = K[3]
+    Kq, s = oracle.quantize_rows(K)
+    prev = set()
+    for kp in (16, 100, 256, 1000, 1999, 2000):
+        pool, _ = oracle.propose_unit(q, Kq, s, T, kp)
+        cur = set(pool.tolist()) - {-1}
+        assert prev <= cur and len(cur) == kp
+        prev = cur
+
+
+def test_head_to_kv_head_mapping():
+    """R5: query head h feeds KV head h // G.  Only head 5 is non-zero: KV head 1's pool equals a
+    one-head proposal with that head, KV head 0 sees a zero query."""
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, D, T, kp = 1, 8, 2, 64, 300, 40
+    q = np.zeros((B, Hq, D), np.float32)
+    q[0, 5] = rng.standard_normal(D)
+    K = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    Kq, s = oracle.quantize_rows(K)
+    pool = oracle.propose(q, Kq, s, kp)
+    assert pool[0, 0].tolist() == list(range(kp))
+    single, _ = oracle.propose_unit(q[0, 5:6], Kq[0, 1], s[0, 1], T, kp)
+    assert pool[0, 1].tolist() == single.tolist()
+
+
+def test_ragged_lengths_and_short_sequences():
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, D, T, kp = 3, 4, 2, 64, 256, 100
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    K = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    lens = np.array([256, 60, 0], np.int32)
+    Kq, s = oracle.quantize_rows(K)
+    pool = oracle.propose(q, Kq, s, kp, seq_lens=lens)
+    assert np.all(pool[0] >= 0) and pool[0].max() < 256
+    for g in range(Hkv):
+        assert pool[1, g].tolist() == list(range(60)) + [-1] * 40
+        assert pool[2, g].tolist() == [-1] * kp
+    idx, out, lse = oracle.refine(q, K, K, pool, 32, seq_lens=lens)
+    assert np.all(idx[2] == -1) and np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+    assert np.all((idx[1] >= 0) & (idx[1] < 60))
+
+
+def test_nonfinite_rejected():
+    K = np.ones((4, 64), np.float32)
+    K[2, 3] = np.nan
+    with pytest.raises(RuntimeError):
+        oracle.quantize_rows(K)
+
+
+# ---------------------------------------------------------------- refine (O5-O7) and dense (O8)
+def _sdpa64(q_group, Krows, Vrows, scale):
+    qt = torch.from_numpy(q_group.astype(np.float64))[None, :, None, :]          # [1,G,1,D]
+    kt = torch.from_numpy(Krows.astype(np.float64))[None, None].expand(1, q_group.shape[0], -1, -1)
+    vt = torch.from_numpy(Vrows.astype(np.float64))[None, None].expand(1, q_group.shape[0], -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(),
+                                                          scale=scale)
+    logits = (torch.from_numpy(q_group.astype(np.float64)) @ torch.from_numpy(
+        Krows.astype(np.float64)).T) * scale
+    return o[0, :, 0].numpy(), torch.logsumexp(logits, dim=1).numpy()
+
+
+@pytest.mark.parametrize("G,D,agg", [(1, 128, 0), (4, 128, 0), (8, 64, 0), (4, 256, 1), (8, 128, 1)])
+def test_refine_against_library(G, D, agg):
+    rng = np.random.default_rng(30 + G + D + agg)
+    T, kp, kappa = 900, 300, 70
+    q = W.bf16_round(rng.standard_normal((G, D)).astype(np.float32))
+    K = W.bf16_round(rng.standard_normal((T, D)).astype(np.float32))
+    V = W.bf16_round(rng.standard_normal((T, D)).astype(np.float32))
+    pool = np.sort(rng.choice(T, size=kp - 20, replace=False)).astype(np.int32)
+    pool = np.concatenate([pool, -np.ones(20, np.int32)])
+    r = oracle.refine_unit(q, K, V, T, pool, kappa, agg)
+    valid = pool[pool >= 0]
+    per_head = K[valid].astype(np.float64) @ q.astype(np.float64).T     # library float64 matmul
+    S_lib = per_head.sum(1) if agg == 0 else per_head.max(1)
+    np.testing.assert_allclose(r["S"][: len(valid)], S_lib, rtol=1e-12, atol=1e-9)
+    assert np.all(np.isnan(r["S"][len(valid):]))
+    chosen = argmax_select(S_lib.tolist(), kappa)
+    assert r["idx"].tolist() == pad([int(valid[c]) for c in chosen], kappa).tolist()
+    sel = r["idx"][r["idx"] >= 0]
+    o_lib, lse_lib = _sdpa64(q, K[sel], V[sel], 1.0 / math.sqrt(D))
+    np.testing.assert_allclose(r["out"], o_lib, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse_lib, rtol=0, atol=1e-12)
+
+
+def test_dense_against_sdpa():
+    rng = np.random.default_rng(40)
+    G, D, T = 4, 128, 1500
+    q = rng.standard_normal((G, D)).astype(np.float32)
+    K = rng.standard_normal((T, D)).astype(np.float32)
+    V = rng.standard_normal((T, D)).astype(np.float32)
+    out, lse = oracle.dense_unit(q, K, V, T)
+    o_lib, lse_lib = _sdpa64(q, K, V, 1.0 / math.sqrt(D))
+    np.testing.assert_allclose(out, o_lib, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_lib, rtol=0, atol=1e-12)
+
+
+def test_full_pool_full_budget_is_dense():
+    """P5: kappa = kp = T_b reproduces dense attention."""
+    rng = np.random.default_rng(41)
+    G, D, T = 4, 64, 700
+    q = rng.standard_normal((G, D)).astype(np.float32)
+    K = rng.standard_normal((T, D)).astype(np.float32)
+    V = rng.standard_normal((T, D)).astype(np.float32)
+    Kq, s = oracle.quantize_rows(K)
+    pool, _ = oracle.propose_unit(q, Kq, s, T, T)
+    assert pool.tolist() == list(range(T))
+    r = oracle.refine_unit(q, K, V, T, pool, T)
+    out, lse = oracle.dense_unit(q, K, V, T)
+    np.testing.assert_allclose(r["out"], out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["lse"], lse, rtol=0, atol=1e-13)
+
+
+def test_kappa_one_returns_argmax_row():
+    """P6: with kappa = 1 the output is exactly the V row of the best token."""
+    rng = np.random.default_rng(42)
+    G, D, T = 4, 128, 400
+    q = rng.standard_normal((G, D)).astype(np.float32)
+    K = rng.standard_normal((T, D)).astype(np.float32)
+    V = rng.standard_normal((T, D)).astype(np.float32)
+    pool = np.arange(T, dtype=np.int32)
+    r = oracle.refine_unit(q, K, V, T, pool, 1)
+    t_star = int(np.argmax(K.astype(np.float64) @ q.astype(np.float64).sum(0)))
+    assert r["idx"].tolist() == [t_star]
+    assert np.array_equal(r["out"], np.tile(V[t_star].astype(np.float64), (G, 1)))
+
+
+def test_static_reuse_when_pool_equals_budget():
+    """P9: kp = kappa leaves nothing to refine: the index set is the pool (static reuse)."""
+    rng = np.random.default_rng(43)
+    G, D, T, kappa = 4, 128, 2000, 128
+    q0, q1 = (rng.standard_normal((G, D)).astype(np.float32) for _ in range(2))
+    K0, K1, V1 = (rng.standard_normal((T, D)).astype(np.float32) for _ in range(3))
+    Kq, s = oracle.quantize_rows(K0)
+    pool, _ = oracle.propose_unit(q0, Kq, s, T, kappa)
+    r = oracle.refine_unit(q1, K1, V1, T, pool, kappa)
+    assert r["idx"].tolist() == pool.tolist()
+
+
+def test_refined_recall_equals_pool_coverage():
+    """P4: with E the exact full-context top-kappa of the refined layer,
+    idx & E == pool & E."""
+    rng = np.random.default_rng(44)
+    G, D, T, kp, kappa = 4, 128, 3000, 512, 128
+    q0, q1 = (rng.standard_normal((G, D)).astype(np.float32) for _ in range(2))
+    K0, K1, V1 = (rng.standard_normal((T, D)).astype(np.float32) for _ in range(3))
+    K1[: T // 2] = K0[: T // 2]  # correlate the layers so that the sets overlap
+    q1 = q0.copy()
+    Kq, s = oracle.quantize_rows(K0)
+    pool, _ = oracle.propose_unit(q0, Kq, s, T, kp)
+    r = oracle.refine_unit(q1, K1, V1, T, pool, kappa)
+    E = set(oracle.refine_unit(q1, K1, V1, T, np.arange(T, dtype=np.int32), kappa)["idx"].tolist())
+    idx, P = set(r["idx"].tolist()), set(pool.tolist())
+    assert len(E & P) > 0
+    assert idx & E == P & E
+    assert idx <= P
+
+
+def test_planted_recovery_cfg1():
+    """P8 on the tiny single-head workload: every planted token is in the pool and the index set."""
+    c = W.CONFIGS["cfg1"]
+    w = W.generate(c)
+    Kq, s = oracle.quantize_rows(w.K[0])
+    pool = oracle.propose(w.q[0], Kq, s, c.kp)
+    idx, out, lse = oracle.refine(w.q[1], w.K[1], w.V[1], pool, c.kappa)
+    S0, Sl = w.salient[(0, 0)]
+    assert len(S0) == 16
+    assert np.isin(S0, pool[0, 0]).all() and np.isin(Sl[0], idx[0, 0]).all()
+    assert set(idx[0, 0].tolist()) <= set(pool[0, 0].tolist())
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg3"])
+def test_planted_recovery_scaled(name):
+    """P8 on reduced-context versions of the GQA workloads with localized shift.  Unshifted
+    salient tokens sit at the anchor's top and are always kept; a shifted target sits at anchor
+    rank r ~ U[kappa, 3 kappa), so a pool of rho*kappa keeps it when r < rho*kappa (all of them
+    for rho = 4, about half for rho = 2) and static reuse (kp = kappa) keeps none.  A target in
+    the pool is planted in its own layer, so refinement always selects it."""
+    c = W.CONFIGS[name].with_(B=1, Hq=8, Hkv=2, T=16384)
+    rho = c.kp // c.kappa
+    w = W.generate(c)
+    Kq, s = oracle.quantize_rows(w.K[0])
+    pool = oracle.propose(w.q[0], Kq, s, c.kp)
+    static = oracle.propose(w.q[0], Kq, s, c.kappa)
+    for l in range(1, c.n_refined + 1):
+        idx, _, _ = oracle.refine(w.q[l], w.K[l], w.V[l], pool, c.kappa)
+        for g in range(c.Hkv):
+            S0, Sl = w.salient[(0, g)]
+            kept = np.intersect1d(Sl[l - 1], S0)
+            shifted = np.setdiff1d(Sl[l - 1], S0)
+            assert len(shifted) > 0
+            assert np.isin(kept, pool[0, g]).all() and np.isin(kept, idx[0, g]).all()
+            cover = np.isin(shifted, pool[0, g])
+            expect = min(1.0, (rho - 1) / 2.0)
+            assert abs(cover.mean() - expect) < 0.2 if rho < 4 else cover.all()
+            assert np.isin(shifted[cover], idx[0, g]).all()
+            assert not np.isin(shifted, static[0, g]).any()
+
+
+# ---------------------------------------------------------------- pages' parameters
+def test_configs_follow_pages_parameters():
+    p = {e["name"]: e for e in json.load(open(os.path.join(GOLDEN, "pages_parameters.json")))["entries"]}
+    c3 = W.CONFIGS["cfg3"]
+    assert c3.kappa == p["kappa_main"]["value"]
+    assert c3.kp == p["rho_long_context"]["value"] * c3.kappa == p["rho_long_context"]["pool"]
+    assert c3.n_refined == p["group_g4_refined_per_proposal"]["value"]
+    assert c3.T == p["context_headline"]["value"]
+    assert W.CONFIGS["cfg2"].kp == p["rho_reasoning"]["value"] * W.CONFIGS["cfg2"].kappa
+    assert p["rho1_accuracy"]["value"] == pytest.approx(64.43 - 5.21)
