@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark of the Prism Attention decode hot path on one MI355X.
+
+A step is one decode step of the hot path at the 128K-context GQA workload: the proposal layer
+(int8 key scan over 131072 tokens + top-8192 pool) followed by three refined layers (pool
+scoring + top-2048 + sparse softmax.V), B=1, 32 query / 8 KV heads, head dim 128, bf16.
+
+Inputs are resident in HBM before timing starts.  R copies of every per-step buffer sit at
+distinct addresses and the steps cycle through them, so that the 256 MB Infinity Cache cannot
+serve one step's data to the next.  Prints ONE JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn steps/s + achieved HBM GB/s at 128K ctx, proposal+3 refined layers"
+PEAK_HBM_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "k_scan_128k_pmc.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--config", default="cfg3")
+    p.add_argument("--rotate", type=int, default=6, help="buffer sets cycled by the steps")
+    p.add_argument("--profile-steps", type=int, default=100, help="steps of the per-kernel event pass")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("k_propose.hip", "prism_device.hpp", "prism_internal.hpp"):
+        with open(os.path.join(ROOT, "token_level_sparse_prism_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the hot path needs no exchange between GPUs "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from token_level_sparse_prism_amd import binding as PB
+    from token_level_sparse_prism_amd import workload as W
+    from token_level_sparse_prism_amd.step import LayerInputs, PrismStep
+
+    PB.load()  # fail loudly if the HIP library is missing
+    cfg = W.CONFIGS[args.config]
+    t0 = time.time()
+    w = W.generate(cfg)
+    gen_s = time.time() - t0
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def dev(x):
+        return torch.from_numpy(x).to(device="cuda", dtype=dt)
+
+    lens_d = torch.from_numpy(w.seq_lens).cuda()
+    K0 = dev(w.K[0])
+    Kq, sc = PB.quantize_keys(K0, seq_lens=lens_d)
+    del K0
+    base = {"q0": dev(w.q[0]), "Kq": Kq, "sc": sc,
+            "layers": [(dev(w.q[l]), dev(w.K[l]), dev(w.V[l])) for l in range(1, w.layers)]}
+    torch.cuda.synchronize()
+
+    R = max(1, args.rotate)
+    sets = [base]
+    for _ in range(R - 1):
+        sets.append({"q0": base["q0"].clone(), "Kq": base["Kq"].clone(), "sc": base["sc"].clone(),
+                     "layers": [tuple(t.clone() for t in L) for L in base["layers"]]})
+    steps = []
+    ws_p = ws_r = None
+    for s in sets:
+        layers = [LayerInputs(*L) for L in s["layers"]]
+        st = PrismStep(s["q0"], s["Kq"], s["sc"], layers, cfg.kp, cfg.kappa, seq_lens=lens_d,
+                       ws_propose=ws_p, ws_refine=ws_r)
+        ws_p, ws_r = st.ws_p, st.ws_r
+        steps.append(st)
+    torch.cuda.synchronize()
+
+    # sanity outside the timed region: every refined index set lies inside its pool
+    steps[0]()
+    torch.cuda.synchronize()
+    pool = steps[0].pool.cpu().numpy()
+    for idx in steps[0].idx:
+        ii = idx.cpu().numpy()
+        for b in range(cfg.B):
+            for g in range(cfg.Hkv):
+                assert set(ii[b, g][ii[b, g] >= 0].tolist()) <= set(pool[b, g].tolist())
+
+    for i in range(args.warmup):
+        steps[i % R]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        steps[i % R]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+
+    # per-kernel durations: a separate pass with HIP events around every launch (same work)
+    PB.profile_reset()
+    PB.profile_enable(True)
+    for i in range(args.profile_steps):
+        steps[i % R]()
+    torch.cuda.synchronize()
+    PB.profile_enable(False)
+    kernels = {}
+    for k in PB.KERNELS:
+        n, ms = PB.profile_query(k)
+        if n:
+            kernels[k] = {"launches": n, "avg_us": 1000.0 * ms / n}
+    PB.profile_reset()
+
+    ab = W.algorithmic_bytes(cfg, w.seq_lens)
+    e = 2 if cfg.dtype == "bf16" else 4
+    scan_bytes = sum(int(w.seq_lens[b]) * (cfg.D + 4) + cfg.G * cfg.D * e
+                     for b in range(cfg.B) for _ in range(cfg.Hkv))
+    scan_us = kernels.get("k_scan", {}).get("avg_us")
+    achieved = scan_bytes / (scan_us * 1e-6) / 1e9 if scan_us else None
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        pmc = json.load(open(PMC_FILE))
+        if pmc.get("source_hash") == kernel_source_hash() and pmc.get("workload") == cfg.name:
+            traffic = pmc.get("traffic_bytes_per_launch")
+    roofline = {"kernel": "k_scan", "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4) if achieved else None,
+                "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
+                "avg_launch_us": round(scan_us, 3) if scan_us else None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oKq, osc = oracle.quantize_rows(w.K[0])
+        threads = min(len(os.sched_getaffinity(0)), cfg.units)
+        n = 0
+        c0 = time.perf_counter()
+        while True:
+            opool = oracle.propose(w.q[0], oKq, osc, cfg.kp, seq_lens=w.seq_lens, nthreads=threads)
+            for l in range(1, w.layers):
+                oracle.refine(w.q[l], w.K[l], w.V[l], opool, cfg.kappa, seq_lens=w.seq_lens, nthreads=threads)
+            n += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(n / cs, 3), "unit": "steps/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} full steps of the same workload ({cfg.units} units, proposal + "
+                         f"{cfg.n_refined} refined layers) in {cs:.1f} s, OpenMP over units"}
+        assert np.array_equal(opool, pool), "oracle and GPU pools differ"
+
+    steps_per_s = 1000.0 / ms_per_step
+    line = {
+        "metric": METRIC, "value": round(steps_per_s, 2), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8+bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: 128K-context GQA decode step, B={cfg.B}, Hq={cfg.Hq}, "
+                               f"Hkv={cfg.Hkv}, D={cfg.D}, T={cfg.T}, kp={cfg.kp}, kappa={cfg.kappa}, "
+                               f"1 proposal + {cfg.n_refined} refined layers, {cfg.dtype}",
+                   "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU",
+                   "rotate_sets": R},
+        "hbm_GBps": round(ab["step"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": int(ab["step"]),
+        "roofline": roofline,
+        "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3), "gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,170 @@
+/*
+ * prism.h -- C ABI of the MI355X (gfx950) decode hot path of Prism Attention.
+ *
+ * Method: "Prism Attention: Proposal-Refined Index Sharing Mechanism for
+ * Efficient LLMs Inference" (paperpeel page of arXiv 2610.22985).  An anchor
+ * (proposal) layer scores the whole context with a compressed key cache and
+ * emits an expanded candidate pool of n = rho*kappa tokens (Sec. 4 Overview,
+ * Sec. 4.1, Sec. 4.2, Sec. 5.1 Implementation Details); each following
+ * refined layer computes exact scores over that pool only, keeps its own
+ * top-kappa and attends to them (Sec. 4.1; Sec. 5.3 notes the refinement
+ * cost does not depend on the context length).
+ *
+ * Conventions shared by every entry point
+ *  - Shapes.  B sequences, Hq query heads, Hkv KV heads, G = Hq / Hkv query
+ *    heads per KV head (1 <= G <= 16), head dim D in {64, 128, 256},
+ *    capacity T_max tokens (1 <= T_max <= 2^23).  Query head h belongs to KV
+ *    head h / G.  A "unit" is one (b, g) pair: one pool and one index set
+ *    per KV head, shared by its G query heads.
+ *  - Layouts (row-major, contiguous, all on the device):
+ *      q          [B][Hq][D]            dtype (fp32 or bf16)
+ *      K, V       [B][Hkv][T_max][D]    dtype
+ *      Kq         [B][Hkv][T_max][D]    int8
+ *      scales     [B][Hkv][T_max]       fp32
+ *      pool       [B][Hkv][kp]          int32
+ *      idx        [B][Hkv][kappa]       int32
+ *      out        [B][Hq][D]            dtype
+ *      lse        [B][Hq]               fp32
+ *      seq_lens   [B]                   int32 (device) or NULL = all T_max;
+ *                 values are clamped to [0, T_max] on the device.
+ *  - Alignment: q, K, V, Kq and out 16-byte aligned; every other pointer
+ *    4-byte aligned; the workspace 256-byte aligned.
+ *  - Ownership: the caller owns every buffer.  The library allocates no
+ *    memory and keeps no state between calls.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Argument and launch errors are returned at once;
+ *    device faults surface at the next synchronisation.
+ *  - Errors: a call that fails validation writes nothing and launches
+ *    nothing.
+ *  - Workspace: query its size with prism_workspace_bytes.  It must be
+ *    zero-filled before its first use (prism_workspace_init does that);
+ *    every call that completes leaves its control words zero again, so a
+ *    workspace is reused without re-initialisation.  Calls that run at the
+ *    same time must use different workspaces.
+ *  - Determinism: pools and index sets are bit-identical from run to run;
+ *    attention outputs are too (fixed split and merge order).
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum prism_status {
+    PRISM_OK = 0,
+    PRISM_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad shape, kappa > kp, ... */
+    PRISM_ERR_UNSUPPORTED = 2, /* D not in {64,128,256}, G > 16, T_max > 2^23, ... */
+    PRISM_ERR_WORKSPACE = 3,   /* workspace smaller than prism_workspace_bytes() */
+    PRISM_ERR_HIP = 4          /* a HIP launch failed; see prism_last_hip_error() */
+} prism_status;
+
+typedef enum prism_dtype { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+/* How the G query heads of a KV head combine into one selection score. */
+typedef enum prism_agg { PRISM_AGG_SUM = 0, PRISM_AGG_MAX = 1 } prism_agg;
+
+typedef enum prism_op { PRISM_OP_PROPOSE = 0, PRISM_OP_REFINE = 1, PRISM_OP_DENSE = 2 } prism_op;
+
+typedef struct prism_shape {
+    int32_t B, Hq, Hkv, D;
+    int64_t T_max;
+    const int32_t* seq_lens; /* device [B] or NULL */
+} prism_shape;
+
+/* Workspace bytes needed by `op` for this shape (kp, kappa ignored where
+ * unused).  Returns 0 when the arguments are invalid. */
+size_t prism_workspace_bytes(int op, const prism_shape* s, int32_t kp, int32_t kappa);
+
+/* Zero-fills a workspace with a kernel on `stream` (safe to record in a
+ * HIP graph).  ws must be 256-byte aligned. */
+prism_status prism_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Key-cache compression for proposal scoring (Sec. 4.2 "Quantized Proposal
+ * Construction"; the page names INT2, this library uses int8).  For every
+ * (b, g, t < T_b): amax = max_d |K|; scale = amax / 127 (fp32, correctly
+ * rounded); codes = clamp(rint(K * (127 / amax)), -127, 127) with one fp32
+ * product and round-half-to-even; an all-zero row gives scale 0 and codes 0.
+ * Rows t >= T_b are not written.  In: K (dtype).  Out: Kq, scales.
+ */
+prism_status prism_quantize_keys(const void* K, prism_dtype dt, const prism_shape* s,
+                                 int8_t* Kq, float* scales, void* stream);
+
+/*
+ * Proposal layer (Sec. 4 Overview, Sec. 4.1 candidate pool C_t^F,
+ * Sec. 4.2; pool size n = rho*kappa, Sec. 5.1).  Per unit:
+ *   qi = int8 codes of the unit's G query heads under ONE shared absmax
+ *        (same quantizer as prism_quantize_keys);
+ *   A[t] = sum over heads (agg SUM) or max over heads (agg MAX) of the int32
+ *        dot products qi[h] . Kq[t];
+ *   score[t] = float(A[t]) * scales[t] (one fp32 product), -0 -> +0;
+ *   pool = the first min(kp, T_b) tokens under (score desc, t asc), written
+ *        in ascending t order, the rest of the kp slots = -1.
+ * In: q (qdt), Kq, scales.  Out: pool [B][Hkv][kp]; scores [B][Hkv][T_max]
+ * fp32 (optional, NULL to skip; entries t >= T_b untouched).
+ * Workspace: prism_workspace_bytes(PRISM_OP_PROPOSE, s, kp, 0).
+ */
+prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, const float* scales,
+                           const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool,
+                           float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Refined layer (Sec. 4.1: the refined layer re-selects its own top-kappa
+ * within the inherited pool; token-level sparse attention of Sec. 1 and
+ * Sec. 2.1).  Per unit, over the valid pool slots j (0 <= pool[j] < T_b):
+ *   l[h, j] = q[h] . K[pool[j]]  (fp32 accumulation of exact products);
+ *   S[j] = sum over the G heads (SUM) or max (MAX);
+ *   idx = the first min(kappa, #valid) slots under (S desc, slot asc) --
+ *        slot order is token order because pools are ascending -- written
+ *        as token ids in ascending order, -1 padded to kappa;
+ *   for each head h: out[h] = softmax(l[h, idx] * sm_scale) . V[idx],
+ *        lse[h] = natural-log sum-exp of the scaled logits;
+ *   no valid slot: out = 0, lse = -inf.
+ * sm_scale = 0 selects 1/sqrt(D).  pool must be ascending (as written by
+ * prism_propose); its entries are not otherwise checked -- out-of-range ones
+ * are skipped.  Out: out (dtype, rounded to nearest even), idx, lse
+ * (optional).  Workspace: prism_workspace_bytes(PRISM_OP_REFINE, s, kp, kappa).
+ */
+prism_status prism_refine_attend(const void* q, const void* K, const void* V, prism_dtype dt,
+                                 const prism_shape* s, const int32_t* pool, int32_t kp,
+                                 int32_t kappa, prism_agg agg, float sm_scale, void* out,
+                                 int32_t* idx, float* lse, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
+ * Dense decode attention over every t < T_b (the kappa = kp = T_b special
+ * case of the refined layer): out[h] = softmax(q[h] . K[0..T_b) * sm_scale)
+ * . V[0..T_b), lse as above.  A reference and a baseline, not part of the
+ * sparse path.  Workspace: prism_workspace_bytes(PRISM_OP_DENSE, s, 0, 0).
+ */
+prism_status prism_dense_ref(const void* q, const void* K, const void* V, prism_dtype dt,
+                             const prism_shape* s, float sm_scale, void* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Diagnostics: per-kernel timing with HIP events.  While enabled, every kernel launch made by
+ * the calls above is bracketed by two events recorded on its stream (this adds event packets
+ * between kernels, so it is for measurement passes, not for production steps).
+ * prism_profile_query synchronises the recorded events and returns, for one kernel name
+ * ("k_quantize_keys", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense"), the
+ * number of launches and their summed duration in milliseconds since the last reset.
+ */
+prism_status prism_profile_enable(int on);
+prism_status prism_profile_query(const char* name, int* launches, double* total_ms);
+void prism_profile_reset(void);
+
+/* The hipError_t of the last failed HIP call on this thread (0 if none). */
+int prism_last_hip_error(void);
+
+/* Static string naming a status code. */
+const char* prism_status_str(prism_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H */

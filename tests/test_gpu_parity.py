@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on seeded inputs.
+
+Sizes span several 1024-token chunks with a ragged tail; shapes cover D in {64, 128, 256},
+G in {1, 3 (padded to 4), 4, 8, 16}, fp32 and bf16, SUM and MAX aggregation, ragged and empty
+sequences, kp above T_b, heavy score ties and the q = 0 degenerate case.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.parity import (assert_pool_equal, check_dense_batch, check_refine_batch, dev, f32_bits, host)
+from token_level_sparse_prism_amd import binding as PB
+from token_level_sparse_prism_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+
+def seed_of(*parts):
+    return zlib.crc32(repr(parts).encode())
+
+
+def rnd(rng, shape, dtype):
+    x = rng.standard_normal(shape).astype(np.float32)
+    return W.bf16_round(x) if dtype == "bf16" else x
+
+
+def make_inputs(seed, Bn, Hq, Hkv, D, T, dtype, lens=None, ties=False, zero_q=False):
+    rng = np.random.default_rng(seed)
+    q = rnd(rng, (Bn, Hq, D), dtype)
+    K = rnd(rng, (Bn, Hkv, T, D), dtype)
+    V = rnd(rng, (Bn, Hkv, T, D), dtype)
+    if ties:
+        proto = rnd(rng, (7, D), dtype)
+        K[:] = proto[rng.integers(0, 7, size=(Bn, Hkv, T))]
+    if zero_q:
+        q[:] = 0.0
+    lens = np.full(Bn, T, np.int32) if lens is None else np.asarray(lens, np.int32)
+    for b in range(Bn):
+        K[b, :, lens[b]:] = 0.0
+        V[b, :, lens[b]:] = 0.0
+    return q, K, V, lens
+
+
+def gpu_quant(K, dtype, lens):
+    Kd = dev(K, dtype)
+    ld = torch.from_numpy(lens).cuda()
+    Kq, sc = PB.quantize_keys(Kd, seq_lens=ld)
+    torch.cuda.synchronize()
+    return Kq, sc, ld
+
+
+# ------------------------------------------------------------------------------------- quantize
+@pytest.mark.parametrize("D,dtype,T,lens", [(128, "f32", 4096, None), (64, "bf16", 3000, [3000, 1777]),
+                                            (256, "bf16", 2500, [0, 2500]), (128, "bf16", 5000, None)])
+def test_quantize_keys_bitexact(D, dtype, T, lens):
+    q, K, V, lens = make_inputs(D + T, 2 if lens else 1, 4, 2, D, T, dtype, lens)
+    K[0, 0, 5] = 0.0  # an all-zero row
+    Kq, sc, _ = gpu_quant(K, dtype, lens)
+    Kq, sc = Kq.cpu().numpy(), sc.cpu().numpy()
+    for b in range(K.shape[0]):
+        n = lens[b]
+        oq, os_ = oracle.quantize_rows(K[b, :, :n])
+        assert np.array_equal(Kq[b, :, :n], oq)
+        assert np.array_equal(f32_bits(sc[b, :, :n]), f32_bits(os_))
+
+
+# ------------------------------------------------------------------------------------- propose
+PROPOSE_CASES = [
+    # D, G, Hkv, agg, dtype, T, kp, lens
+    (128, 4, 2, PB.AGG_SUM, "bf16", 5000, 1024, None),
+    (64, 8, 2, PB.AGG_SUM, "bf16", 9000, 4096, [9000, 3000]),
+    (256, 1, 1, PB.AGG_SUM, "f32", 4096, 1024, None),
+    (128, 3, 2, PB.AGG_MAX, "bf16", 6000, 512, None),
+    (128, 4, 1, PB.AGG_MAX, "f32", 3000, 2999, None),
+    (64, 16, 1, PB.AGG_SUM, "bf16", 2500, 100, None),
+    (256, 8, 1, PB.AGG_MAX, "bf16", 2100, 2048, [2100, 1]),
+    (128, 4, 2, PB.AGG_SUM, "bf16", 1000, 1500, None),   # kp > T: take everything
+    (128, 4, 2, PB.AGG_SUM, "bf16", 3000, 700, [3000, 0]),  # an empty sequence
+    (128, 1, 1, PB.AGG_SUM, "bf16", 1, 4, None),          # a single token
+]
+
+
+@pytest.mark.parametrize("case", PROPOSE_CASES, ids=lambda c: f"D{c[0]}G{c[1]}a{c[3]}{c[4]}T{c[5]}kp{c[6]}")
+@pytest.mark.parametrize("variant", ["random", "ties", "zero_q"])
+def test_propose_bitexact(case, variant):
+    D, G, Hkv, agg, dtype, T, kp, lens = case
+    Bn = len(lens) if lens else 1
+    q, K, V, lens = make_inputs(seed_of(D, G, T, kp, variant), Bn, G * Hkv, Hkv, D, T, dtype, lens,
+                                ties=variant == "ties", zero_q=variant == "zero_q")
+    Kq, sc, ld = gpu_quant(K, dtype, lens)
+    scores = torch.zeros((Bn, Hkv, T), dtype=torch.float32, device="cuda")
+    pool = PB.propose(dev(q, dtype), Kq, sc, kp, agg, seq_lens=ld, scores=scores)
+    torch.cuda.synchronize()
+    oKq, osc = oracle.quantize_rows(K)
+    opool, oscores = oracle.propose(q, oKq, osc, kp, seq_lens=lens, agg=agg, want_scores=True)
+    gs = scores.cpu().numpy()
+    for b in range(Bn):
+        assert np.array_equal(f32_bits(gs[b, :, :lens[b]]), f32_bits(oscores[b, :, :lens[b]])), "scores differ"
+    assert_pool_equal(pool.cpu().numpy(), opool)
+
+
+def test_propose_large_candidate_set():
+    """Every score equal over 262144 tokens: the threshold bin holds the whole context."""
+    D, T, kp = 64, 262144, 65536
+    rng = np.random.default_rng(9)
+    K = np.tile(W.bf16_round(rng.standard_normal((1, 1, 1, D)).astype(np.float32)), (1, 1, T, 1))
+    q = W.bf16_round(rng.standard_normal((1, 8, D)).astype(np.float32))
+    Kq, sc, ld = gpu_quant(K, "bf16", np.array([T], np.int32))
+    pool = PB.propose(dev(q, "bf16"), Kq, sc, kp, seq_lens=ld)
+    torch.cuda.synchronize()
+    assert pool.cpu().numpy()[0, 0].tolist() == list(range(kp))
+
+
+# ------------------------------------------------------------------------------------- refine
+REFINE_CASES = [
+    # D, G, Hkv, agg, dtype, T, kp, kappa, lens
+    (128, 4, 2, PB.AGG_SUM, "bf16", 6000, 2048, 512, None),
+    (128, 1, 1, PB.AGG_SUM, "f32", 4096, 1024, 256, None),
+    (64, 8, 2, PB.AGG_SUM, "bf16", 5000, 1000, 300, [5000, 2222]),
+    (256, 4, 1, PB.AGG_MAX, "bf16", 3000, 1500, 700, None),
+    (128, 3, 2, PB.AGG_MAX, "f32", 2000, 512, 100, None),
+    (64, 16, 1, PB.AGG_SUM, "bf16", 3000, 600, 64, None),
+    (256, 2, 1, PB.AGG_SUM, "f32", 1500, 900, 900, None),     # kappa = kp: static reuse
+    (128, 4, 2, PB.AGG_SUM, "bf16", 1200, 2048, 1500, [1200, 0]),  # pool padding, empty sequence
+    (128, 4, 1, PB.AGG_SUM, "bf16", 3000, 400, 1, None),        # kappa = 1
+]
+
+
+@pytest.mark.parametrize("case", REFINE_CASES, ids=lambda c: f"D{c[0]}G{c[1]}a{c[3]}{c[4]}kp{c[6]}k{c[7]}")
+@pytest.mark.parametrize("variant", ["random", "zero_q"])
+def test_refine_parity(case, variant):
+    D, G, Hkv, agg, dtype, T, kp, kappa, lens = case
+    Bn = len(lens) if lens else 1
+    q, K, V, lens = make_inputs(seed_of(D, G, T, kp, kappa, variant), Bn, G * Hkv, Hkv, D, T, dtype, lens,
+                                zero_q=variant == "zero_q")
+    rng = np.random.default_rng(kp + kappa)
+    q0 = rnd(rng, q.shape, dtype)
+    oKq, osc = oracle.quantize_rows(K)
+    pool = oracle.propose(q0, oKq, osc, kp, seq_lens=lens)  # an oracle pool feeds both sides
+    ld = torch.from_numpy(lens).cuda()
+    out, idx, lse = PB.refine_attend(dev(q, dtype), dev(K, dtype), dev(V, dtype), torch.from_numpy(pool).cuda(),
+                                     kappa, agg, seq_lens=ld)
+    torch.cuda.synchronize()
+    check_refine_batch(idx.cpu().numpy(), host(out), lse.cpu().numpy(), q, K, V, lens, pool, kappa, agg, dtype)
+    if variant == "zero_q":  # every score ties: the lowest pool slots win
+        gi = idx.cpu().numpy()
+        for b in range(Bn):
+            for g in range(Hkv):
+                valid = pool[b, g][(pool[b, g] >= 0) & (pool[b, g] < lens[b])]
+                n = min(kappa, len(valid))
+                assert gi[b, g, :n].tolist() == valid[:n].tolist()
+
+
+def test_refine_full_budget_is_dense():
+    """kappa = kp = T_b: the refined layer reproduces dense attention (GPU sparse vs GPU dense vs oracle)."""
+    D, G, Hkv, T = 128, 4, 2, 3000
+    q, K, V, lens = make_inputs(77, 1, G * Hkv, Hkv, D, T, "bf16")
+    pool = np.tile(np.arange(T, dtype=np.int32), (1, Hkv, 1))
+    qd, Kd, Vd = dev(q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    out, idx, lse = PB.refine_attend(qd, Kd, Vd, torch.from_numpy(pool).cuda(), T)
+    dout, dlse = PB.dense_ref(qd, Kd, Vd)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), pool)
+    check_dense_batch(host(out), lse.cpu().numpy(), q, K, V, lens, "bf16")
+    check_dense_batch(host(dout), dlse.cpu().numpy(), q, K, V, lens, "bf16")
+
+
+@pytest.mark.parametrize("D,G,dtype,T,lens", [(128, 4, "bf16", 5000, [5000, 1234]), (64, 8, "f32", 3000, None),
+                                             (256, 1, "bf16", 2000, [0, 2000]), (128, 3, "f32", 1000, None)])
+def test_dense_parity(D, G, dtype, T, lens):
+    Hkv = 2
+    Bn = len(lens) if lens else 1
+    q, K, V, lens = make_inputs(D * G + T, Bn, G * Hkv, Hkv, D, T, dtype, lens)
+    out, lse = PB.dense_ref(dev(q, dtype), dev(K, dtype), dev(V, dtype), seq_lens=torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    check_dense_batch(host(out), lse.cpu().numpy(), q, K, V, lens, dtype)
+
+
+# ------------------------------------------------------------------------------------- whole steps
+def run_step_gpu(w, kp, kappa, agg=PB.AGG_SUM):
+    from token_level_sparse_prism_amd.step import LayerInputs, PrismStep
+    c = w.cfg
+    ld = torch.from_numpy(w.seq_lens).cuda()
+    Kq, sc = PB.quantize_keys(dev(w.K[0], c.dtype), seq_lens=ld)
+    layers = [LayerInputs(dev(w.q[l], c.dtype), dev(w.K[l], c.dtype), dev(w.V[l], c.dtype))
+              for l in range(1, w.layers)]
+    step = PrismStep(dev(w.q[0], c.dtype), Kq, sc, layers, kp, kappa, agg, seq_lens=ld)
+    pool, idx, out, lse = step()
+    torch.cuda.synchronize()
+    return step, Kq, sc
+
+
+@pytest.mark.parametrize("name,overrides", [("cfg1", {}), ("cfg2", {"B": 1, "T": 32768}),
+                                            ("cfg4", {"B": 2, "T": 24576, "ragged": (8192, 24576), "n_refined": 2}),
+                                            ("cfg5_D64_k512_r4", {"T": 16384}), ("cfg5_D256_k512_r2", {"T": 8192})])
+def test_config_step_parity(name, overrides):
+    c = W.CONFIGS[name].with_(**overrides)
+    w = W.generate(c)
+    step, Kq, sc = run_step_gpu(w, c.kp, c.kappa)
+    oKq, osc = oracle.quantize_rows(w.K[0])
+    for b in range(c.B):
+        n = w.seq_lens[b]
+        assert np.array_equal(Kq.cpu().numpy()[b, :, :n], oKq[b, :, :n])
+    opool = oracle.propose(w.q[0], oKq, osc, c.kp, seq_lens=w.seq_lens)
+    assert_pool_equal(step.pool.cpu().numpy(), opool)
+    for l in range(1, w.layers):
+        check_refine_batch(step.idx[l - 1].cpu().numpy(), host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(),
+                           w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype)
+        # planted recovery: each refined layer's salient tokens that the pool holds are selected
+        for b in range(c.B):
+            for g in range(c.Hkv):
+                S0, Sl = w.salient[(b, g)]
+                inpool = Sl[l - 1][np.isin(Sl[l - 1], opool[b, g])]
+                assert np.isin(inpool, step.idx[l - 1].cpu().numpy()[b, g]).all()
+                assert np.isin(S0, opool[b, g]).all()
+
+
+def test_determinism_and_workspace_reuse():
+    """Ten steps with the same workspaces give bit-identical pools, index sets and outputs."""
+    c = W.CONFIGS["cfg2"].with_(B=1, Hkv=4, Hq=16, T=20000)
+    w = W.generate(c)
+    step, _, _ = run_step_gpu(w, c.kp, c.kappa)
+    ref = [step.pool.clone()] + [t.clone() for t in step.idx] + [t.clone() for t in step.out]
+    for _ in range(10):
+        step()
+        torch.cuda.synchronize()
+        cur = [step.pool] + list(step.idx) + list(step.out)
+        for a, b in zip(ref, cur):
+            assert torch.equal(a, b)
+
+
+def test_full_size_128k_sampled_units():
+    """The 128K-context workload at full size, in the launch configuration the benchmark times:
+    every unit's pool, two units' refined layers in full against the oracle, and index sets
+    inside the pools everywhere."""
+    c = W.CONFIGS["cfg3"]
+    w = W.generate(c)
+    step, Kq, sc = run_step_gpu(w, c.kp, c.kappa)
+    oKq, osc = oracle.quantize_rows(w.K[0])
+    assert np.array_equal(Kq.cpu().numpy(), oKq)
+    assert np.array_equal(f32_bits(sc.cpu().numpy()), f32_bits(osc))
+    opool = oracle.propose(w.q[0], oKq, osc, c.kp, seq_lens=w.seq_lens)
+    gpool = step.pool.cpu().numpy()
+    assert_pool_equal(gpool, opool)
+    for l in range(1, w.layers):
+        gidx = step.idx[l - 1].cpu().numpy()
+        for g in range(c.Hkv):
+            assert set(gidx[0, g].tolist()) <= set(gpool[0, g].tolist())
+        check_refine_batch(gidx, host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(), w.q[l], w.K[l], w.V[l],
+                           w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype, units={(0, 0), (0, 5)})

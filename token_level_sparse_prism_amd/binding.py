@@ -1,0 +1,223 @@
+"""ctypes binding of libprism.so (C ABI in include/prism.h).
+
+Argument marshalling only: torch tensors supply device memory and the current HIP stream; every
+step of the computation runs in the library's kernels.  There is no fallback: if the library is
+missing or a call fails, this raises.
+"""
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libprism.so")
+
+PRISM_F32, PRISM_BF16 = 0, 1
+AGG_SUM, AGG_MAX = 0, 1
+OP_PROPOSE, OP_REFINE, OP_DENSE = 0, 1, 2
+STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_INVALID_ARG", 2: "PRISM_ERR_UNSUPPORTED",
+          3: "PRISM_ERR_WORKSPACE", 4: "PRISM_ERR_HIP"}
+EXPORTS = ("prism_workspace_bytes", "prism_workspace_init", "prism_quantize_keys", "prism_propose",
+           "prism_refine_attend", "prism_dense_ref", "prism_profile_enable", "prism_profile_query",
+           "prism_profile_reset", "prism_last_hip_error", "prism_status_str")
+KERNELS = ("k_quantize_keys", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense")
+
+
+class PrismError(RuntimeError):
+    def __init__(self, fn: str, code: int, hip: int = 0):
+        super().__init__(f"{fn} -> {STATUS.get(code, code)}" + (f" (hipError {hip})" if hip else ""))
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("T_max", ctypes.c_int64), ("seq_lens", ctypes.c_void_p)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+
+
+def load():
+    """Load libprism.so (built by token_level_sparse_prism_amd/build.py); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library {LIB_PATH} is not built; run token_level_sparse_prism_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    sp = ctypes.POINTER(Shape)
+    lib.prism_workspace_bytes.argtypes = [ctypes.c_int, sp, ctypes.c_int32, ctypes.c_int32]
+    lib.prism_workspace_bytes.restype = ctypes.c_size_t
+    lib.prism_workspace_init.argtypes = [_vp, ctypes.c_size_t, _vp]
+    lib.prism_quantize_keys.argtypes = [_vp, ctypes.c_int, sp, _vp, _vp, _vp]
+    lib.prism_propose.argtypes = [_vp, ctypes.c_int, _vp, _vp, sp, ctypes.c_int32, ctypes.c_int, _vp, _vp,
+                                  _vp, ctypes.c_size_t, _vp]
+    lib.prism_refine_attend.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, _vp, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.prism_dense_ref.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, ctypes.c_float, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _vp]
+    for fn in ("prism_workspace_init", "prism_quantize_keys", "prism_propose", "prism_refine_attend",
+               "prism_dense_ref", "prism_last_hip_error"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.prism_profile_enable.argtypes = [ctypes.c_int]
+    lib.prism_profile_enable.restype = ctypes.c_int
+    lib.prism_profile_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]
+    lib.prism_profile_query.restype = ctypes.c_int
+    lib.prism_profile_reset.argtypes = []
+    lib.prism_profile_reset.restype = None
+    lib.prism_status_str.argtypes = [ctypes.c_int]
+    lib.prism_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise PrismError(fn, rc, load().prism_last_hip_error() if rc == 4 else 0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PRISM_F32
+    if t.dtype == torch.bfloat16:
+        return PRISM_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def make_shape(q: torch.Tensor, K: torch.Tensor, seq_lens: Optional[torch.Tensor] = None) -> Shape:
+    B, Hq, D = q.shape
+    B2, Hkv, T_max, D2 = K.shape
+    if B != B2 or D != D2:
+        raise ValueError("q [B,Hq,D] and K [B,Hkv,T_max,D] disagree")
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens")
+        if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+            raise ValueError("seq_lens must be int32 [B]")
+    return Shape(B, Hq, Hkv, D, T_max, None if seq_lens is None else seq_lens.data_ptr())
+
+
+def workspace_bytes(op: int, shape: Shape, kp: int = 0, kappa: int = 0) -> int:
+    return int(load().prism_workspace_bytes(op, ctypes.byref(shape), kp, kappa))
+
+
+def new_workspace(op: int, shape: Shape, kp: int = 0, kappa: int = 0, device=None, stream=None) -> torch.Tensor:
+    """Allocate (through torch) and zero-fill (with the library's kernel) a workspace."""
+    n = workspace_bytes(op, shape, kp, kappa)
+    if n == 0:
+        raise PrismError("prism_workspace_bytes", 1)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device or "cuda")
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    _check("prism_workspace_init", load().prism_workspace_init(_ptr(ws), n, _stream(stream)))
+    return ws
+
+
+def quantize_keys(K: torch.Tensor, seq_lens: Optional[torch.Tensor] = None, Kq: Optional[torch.Tensor] = None,
+                  scales: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    _need(K, "K")
+    B, Hkv, T_max, D = K.shape
+    q_dummy = torch.empty((B, Hkv, D), device=K.device, dtype=K.dtype)
+    shape = make_shape(q_dummy, K, seq_lens)
+    if Kq is None:
+        Kq = torch.zeros((B, Hkv, T_max, D), dtype=torch.int8, device=K.device)
+    if scales is None:
+        scales = torch.zeros((B, Hkv, T_max), dtype=torch.float32, device=K.device)
+    _check("prism_quantize_keys", load().prism_quantize_keys(_ptr(K), _dtype_code(K), ctypes.byref(shape),
+                                                             _ptr(Kq), _ptr(scales), _stream(stream)))
+    return Kq, scales
+
+
+def propose(q: torch.Tensor, Kq: torch.Tensor, scales: torch.Tensor, kp: int, agg: int = AGG_SUM,
+            seq_lens: Optional[torch.Tensor] = None, pool: Optional[torch.Tensor] = None,
+            scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """Proposal layer: returns pool [B,Hkv,kp] int32 (and fills `scores` if given)."""
+    for t, n in ((q, "q"), (Kq, "Kq"), (scales, "scales")):
+        _need(t, n)
+    shape = make_shape(q, Kq, seq_lens)
+    if pool is None:
+        pool = torch.empty((shape.B, shape.Hkv, kp), dtype=torch.int32, device=q.device)
+    if ws is None:
+        ws = new_workspace(OP_PROPOSE, shape, kp, 0, device=q.device, stream=stream)
+    _check("prism_propose", load().prism_propose(_ptr(q), _dtype_code(q), _ptr(Kq), _ptr(scales),
+                                                 ctypes.byref(shape), kp, agg, _ptr(pool), _ptr(scores),
+                                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return pool
+
+
+def refine_attend(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool: torch.Tensor, kappa: int,
+                  agg: int = AGG_SUM, sm_scale: float = 0.0, seq_lens: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, want_lse: bool = True, ws: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Refined layer: returns (out [B,Hq,D], idx [B,Hkv,kappa], lse [B,Hq] or None)."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V"), (pool, "pool")):
+        _need(t, n)
+    if not (q.dtype == K.dtype == V.dtype):
+        raise TypeError("q, K and V must share one dtype")
+    shape = make_shape(q, K, seq_lens)
+    kp = pool.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    if idx is None:
+        idx = torch.empty((shape.B, shape.Hkv, kappa), dtype=torch.int32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((shape.B, shape.Hq), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = new_workspace(OP_REFINE, shape, kp, kappa, device=q.device, stream=stream)
+    _check("prism_refine_attend", load().prism_refine_attend(
+        _ptr(q), _ptr(K), _ptr(V), _dtype_code(q), ctypes.byref(shape), _ptr(pool), kp, kappa, agg,
+        float(sm_scale), _ptr(out), _ptr(idx), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, idx, lse
+
+
+def dense_ref(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sm_scale: float = 0.0,
+              seq_lens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """Dense decode attention: returns (out [B,Hq,D], lse [B,Hq])."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V")):
+        _need(t, n)
+    shape = make_shape(q, K, seq_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((shape.B, shape.Hq), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = new_workspace(OP_DENSE, shape, device=q.device, stream=stream)
+    _check("prism_dense_ref", load().prism_dense_ref(_ptr(q), _ptr(K), _ptr(V), _dtype_code(q),
+                                                     ctypes.byref(shape), float(sm_scale), _ptr(out),
+                                                     _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def profile_enable(on: bool = True):
+    """Bracket every kernel launch with HIP events on its stream (measurement passes only)."""
+    load().prism_profile_enable(1 if on else 0)
+
+
+def profile_reset():
+    load().prism_profile_reset()
+
+
+def profile_query(name: str) -> Tuple[int, float]:
+    """(launches, total milliseconds) of kernel `name` since the last reset; synchronises."""
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _check("prism_profile_query", load().prism_profile_query(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

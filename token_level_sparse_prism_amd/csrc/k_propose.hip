@@ -1,0 +1,439 @@
+// k_propose.hip -- proposal layer of Prism Attention on gfx950 (Prism Attention page, Sec. 4
+// Overview and Sec. 4.1: the anchor layer scores the whole context and emits an expanded pool;
+// Sec. 4.2: the scoring uses the compressed key cache; Sec. 5.1: pool size n = rho * kappa).
+//
+// Three launches per call, each over (chunk of 1024 tokens) x (unit = batch, KV head):
+//   k_scan     streams the int8 keys once (the HBM-bound pass), writes a 32-bit order key per
+//              token and a histogram of the keys' top 12 bits; the unit's last workgroup finds
+//              the bin that holds the kp-th largest key.
+//   k_cand     counts, per chunk, the keys above that bin and appends the keys inside it to a
+//              candidate list; the unit's last workgroup finishes the exact threshold on the
+//              remaining 20 bits and turns the counts into per-chunk output offsets.
+//   k_compact  writes the pool in ascending token order: every key above the threshold, and the
+//              lowest-index keys equal to it.
+// The selection is exact integer work, so the pool is bit-identical to a full sort by
+// (score desc, token asc).
+#include "prism_device.hpp"
+#include "prism_prof.hpp"
+
+namespace prism {
+
+enum { kModeEmpty = 0, kModeAll = 1, kModeSelect = 2 };
+enum { kStMode = 0, kStBin = 1, kStAbove = 2, kStHbin = 3, kStTau = 4, kStNeed = 5, kStKpEff = 6 };
+
+// ---------------------------------------------------------------------------------------------
+// k_scan.  NQ int8 query vectors are dotted with each key row:
+//   agg SUM, G == 1: NQ = 1, the head's codes;
+//   agg SUM, G  > 1: NQ = 2, the group's code sums split as qsum = 16*hi + lo with lo in
+//                    [-8, 7] and |hi| <= 127, so A = 16*(hi.K) + lo.K exactly in int32;
+//   agg MAX:         NQ = GP (G rounded up to a power of two), one vector per head.
+// A lane holds 16 bytes of a key row (D/16 lanes per token); a wave reads 1 KiB of
+// consecutive rows per load.
+template <int D, int NQ, bool kMax>
+__global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
+    constexpr int LPT = D / 16;            // lanes per token
+    constexpr int TPW = 64 / LPT;          // tokens per wave per load
+    constexpr int TPR = TPW * (kThreads / 64);
+    constexpr int ROUNDS = kChunk / TPR;
+    constexpr int U = 8;                   // loads in flight per lane
+    static_assert(ROUNDS % U == 0, "chunk must hold whole unrolled rounds");
+
+    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ uint32_t s_key[kChunk];
+    __shared__ float s_scale[kChunk];
+    __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
+    __shared__ float s_red[kThreads / 64];
+    __shared__ uint32_t s_tmp[kThreads / 64];
+    __shared__ uint32_t s_res[4];
+    __shared__ uint32_t s_flag;
+
+    const Dims& d = a.d;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int unit = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const int b = unit / d.Hkv, g = unit % d.Hkv;
+    const int G = d.G;
+    const int64_t Tb = seq_len_of(d, b);
+    const int64_t c0 = int64_t(chunk) * kChunk;
+    const int nvalid = int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
+
+    for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;
+
+    // ---- query quantization: one absmax over the group's G*D values ----
+    const int64_t qoff = (int64_t(b) * d.Hq + int64_t(g) * G) * D;
+    auto qval = [&](int i) -> float {
+        return a.q_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[qoff + i])
+                        : static_cast<const float*>(a.q)[qoff + i];
+    };
+    float amax = 0.0f;
+    for (int i = tid; i < G * D; i += kThreads) amax = fmaxf(amax, fabsf(qval(i)));
+    amax = wave_max(amax);
+    if (lane == 0) s_red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    auto code = [&](float x) -> int {
+        float r = __builtin_rintf(x * inv);
+        return int(fminf(fmaxf(r, -127.0f), 127.0f));
+    };
+    for (int dd = tid; dd < D; dd += kThreads) {
+        if constexpr (kMax) {
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) s_q[h][dd] = int8_t(h < G ? code(qval(h * D + dd)) : 0);
+        } else if constexpr (NQ == 1) {
+            s_q[0][dd] = int8_t(code(qval(dd)));
+        } else {
+            int qs = 0;
+            for (int h = 0; h < G; ++h) qs += code(qval(h * D + dd));
+            const int lo = ((qs + 8) & 15) - 8;
+            const int hi = (qs - lo) >> 4;
+            s_q[0][dd] = int8_t(hi);
+            s_q[1][dd] = int8_t(lo);
+        }
+    }
+    const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
+    for (int i = tid; i < nvalid; i += kThreads) s_scale[i] = scl[i];
+    __syncthreads();
+
+    // ---- streaming int8 scan ----
+    const int sub = lane % LPT;
+    int qv[NQ][4];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * 16]);
+        qv[n][0] = int(w.x); qv[n][1] = int(w.y); qv[n][2] = int(w.z); qv[n][3] = int(w.w);
+    }
+    const int8_t* base = a.Kq + (int64_t(unit) * d.T_max + c0) * D + sub * 16;
+    const int tok_lane = wave * TPW + lane / LPT;
+    if (nvalid > 0) {
+        for (int r0 = 0; r0 < ROUNDS; r0 += U) {
+            uint4 kv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int tok = (r0 + u) * TPR + tok_lane;
+                kv[u] = tok < nvalid ? load16_stream(base + int64_t(tok) * D) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int tok = (r0 + u) * TPR + tok_lane;
+                const int k4[4] = {int(kv[u].x), int(kv[u].y), int(kv[u].z), int(kv[u].w)};
+                int A;
+                if constexpr (kMax) {
+                    int best = 0;
+#pragma unroll
+                    for (int h = 0; h < NQ; ++h) {
+                        int acc = 0;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_sdot4(qv[h][i], k4[i], acc, false);
+#pragma unroll
+                        for (int o = LPT / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+                        if (h < G) best = (h == 0 || acc > best) ? acc : best;
+                    }
+                    A = best;
+                } else {
+                    int acc0 = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc0 = __builtin_amdgcn_sdot4(qv[0][i], k4[i], acc0, false);
+                    if constexpr (NQ == 2) {
+                        int acc1 = 0;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc1 = __builtin_amdgcn_sdot4(qv[1][i], k4[i], acc1, false);
+                        acc0 = acc0 * 16 + acc1;
+                    }
+#pragma unroll
+                    for (int o = LPT / 2; o >= 1; o >>= 1) acc0 += __shfl_xor(acc0, o);
+                    A = acc0;
+                }
+                if (sub == 0 && tok < nvalid) {
+                    const float score = float(A) * s_scale[tok];  // one fp32 product
+                    s_key[tok] = order_key(score);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- keys out (coalesced), top-digit histogram ----
+    uint32_t* kout = a.keys + int64_t(unit) * d.T_max + c0;
+    float* sout = a.scores ? a.scores + int64_t(unit) * d.T_max + c0 : nullptr;
+    for (int i = tid; i < nvalid; i += kThreads) {
+        const uint32_t k = s_key[i];
+        atomicAdd(&s_hist[k >> kKeyShift], 1u);
+        kout[i] = k;
+        if (sout) sout[i] = key_to_float(k);
+    }
+    __syncthreads();
+    uint32_t* gh = a.ghist + int64_t(unit) * kHistBins;
+    for (int i = tid; i < kHistBins; i += kThreads) {
+        const uint32_t c = s_hist[i];
+        if (c) atomicAdd(&gh[i], c);
+    }
+
+    if (!arrive_last(&a.done_scan[unit], gridDim.x, &s_flag)) return;
+
+    // ---- last workgroup of the unit: bin of the kp-th largest key ----
+    const int64_t kp_eff = Tb < a.kp ? Tb : a.kp;
+    uint32_t* st = a.state + int64_t(unit) * 8;
+    if (Tb == 0 || kp_eff == Tb) {
+        if (tid == 0) {
+            st[kStMode] = Tb == 0 ? kModeEmpty : kModeAll;
+            st[kStKpEff] = uint32_t(kp_eff);
+        }
+    } else {
+        for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = gh[i];
+        __syncthreads();
+        find_crossing<kHistBins>(s_hist, uint32_t(kp_eff), s_tmp, s_res);
+        if (tid == 0) {
+            st[kStMode] = kModeSelect;
+            st[kStBin] = s_res[0];
+            st[kStAbove] = s_res[1];
+            st[kStHbin] = s_res[2];
+            st[kStKpEff] = uint32_t(kp_eff);
+        }
+    }
+    for (int i = tid; i < kHistBins; i += kThreads) gh[i] = 0u;
+    if (tid == 0) a.done_scan[unit] = 0u;
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_cand.  Dynamic LDS: 2 * nchunks words (per-chunk counts of candidates above / equal to the
+// threshold), used only by the unit's last workgroup.
+__global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
+    extern __shared__ uint32_t s_dyn[];
+    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ uint32_t s_tmp[kThreads / 64];
+    __shared__ uint32_t s_res[4];
+    __shared__ uint32_t s_base;
+    __shared__ uint32_t s_flag;
+
+    const Dims& d = a.d;
+    const int tid = threadIdx.x;
+    const int unit = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const int b = unit / d.Hkv;
+    const uint32_t* st = a.state + int64_t(unit) * 8;
+    if (st[kStMode] != kModeSelect) return;  // uniform over the unit: nobody arrives
+    const uint32_t bin = st[kStBin];
+    const int64_t Tb = seq_len_of(d, b);
+    const int64_t c0 = int64_t(chunk) * kChunk;
+    const int nvalid = int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
+    const uint32_t* keys = a.keys + int64_t(unit) * d.T_max;
+    uint2* cand = a.cand + int64_t(unit) * d.T_max;
+
+    // 4 consecutive tokens per thread
+    uint32_t k[4];
+    uint32_t ngt = 0, ncand = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = tid * 4 + i;
+        k[i] = tok < nvalid ? keys[c0 + tok] : 0u;
+        const uint32_t kb = k[i] >> kKeyShift;
+        if (tok < nvalid) {
+            ngt += kb > bin ? 1u : 0u;
+            ncand += kb == bin ? 1u : 0u;
+        }
+    }
+    const uint32_t chunk_gt = block_sum_u32(ngt, s_tmp);
+    uint32_t ctot;
+    uint32_t cpre = block_excl_scan(ncand, s_tmp, &ctot);
+    if (tid == 0) {
+        a.cnt_gt[int64_t(unit) * a.nchunks + chunk] = chunk_gt;
+        s_base = ctot ? atomicAdd(&a.cand_cnt[unit], ctot) : 0u;
+    }
+    __syncthreads();
+    const uint32_t base = s_base;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = tid * 4 + i;
+        if (tok < nvalid && (k[i] >> kKeyShift) == bin) {
+            const uint32_t pos = base + cpre++;
+            if (pos < uint32_t(d.T_max)) cand[pos] = make_uint2(k[i], uint32_t(c0 + tok));
+        }
+    }
+
+    if (!arrive_last(&a.done_cand[unit], gridDim.x, &s_flag)) return;
+
+    // ---- last workgroup: exact threshold among the candidates, then per-chunk offsets ----
+    uint32_t* stw = a.state + int64_t(unit) * 8;
+    const uint32_t c = min(a.cand_cnt[unit], uint32_t(d.T_max));
+    const uint32_t kp_eff = st[kStKpEff];
+    const uint32_t need_bin = kp_eff - st[kStAbove];
+
+    // digit A: key bits 19..8
+    for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < c; i += kThreads) atomicAdd(&s_hist[(cand[i].x >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    find_crossing<kHistBins>(s_hist, need_bin, s_tmp, s_res);
+    const uint32_t da = s_res[0], above_a = s_res[1];
+    // digit B: key bits 7..0 among keys whose digit A matches
+    for (int i = tid; i < 256; i += kThreads) s_hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < c; i += kThreads) {
+        const uint32_t kk = cand[i].x;
+        if (((kk >> 8) & 0xFFFu) == da) atomicAdd(&s_hist[kk & 0xFFu], 1u);
+    }
+    __syncthreads();
+    find_crossing<256>(s_hist, need_bin - above_a, s_tmp, s_res);
+    const uint32_t tau = (bin << kKeyShift) | (da << 8) | s_res[0];
+    const uint32_t need = need_bin - above_a - s_res[1];  // keys equal to tau to take, >= 1
+
+    // per-chunk counts of candidates above / equal to tau
+    const int nch = a.nchunks;
+    uint32_t* s_cg = s_dyn;
+    uint32_t* s_ce = s_dyn + nch;
+    for (int i = tid; i < 2 * nch; i += kThreads) s_dyn[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < c; i += kThreads) {
+        const uint2 e = cand[i];
+        const int ch = int(e.y / kChunk);
+        if (e.x > tau) atomicAdd(&s_cg[ch], 1u);
+        else if (e.x == tau) atomicAdd(&s_ce[ch], 1u);
+    }
+    __syncthreads();
+
+    // eq_before[ch] = equal keys in earlier chunks; take[ch] = equal keys of ch inside the budget;
+    // offset[ch] = selected tokens in earlier chunks.  Each thread owns CPT consecutive chunks.
+    const int CPT = (nch + kThreads - 1) / kThreads;
+    const int ch0 = tid * CPT;
+    const uint32_t* cgt = a.cnt_gt + int64_t(unit) * nch;
+    uint32_t esum = 0;
+    for (int j = 0; j < CPT; ++j) {
+        const int ch = ch0 + j;
+        if (ch < nch) esum += s_ce[ch];
+    }
+    uint32_t tot;
+    uint32_t eq_run = block_excl_scan(esum, s_tmp, &tot);
+    uint32_t ssum = 0;
+    for (int j = 0; j < CPT; ++j) {
+        const int ch = ch0 + j;
+        if (ch < nch) {
+            const uint32_t ce = s_ce[ch];
+            const uint32_t take = eq_run >= need ? 0u : min(ce, need - eq_run);
+            const uint32_t selc = cgt[ch] + s_cg[ch] + take;
+            s_cg[ch] = selc;  // reuse: selected count of the chunk
+            s_ce[ch] = eq_run; // reuse: equal keys before the chunk
+            eq_run += ce;
+            ssum += selc;
+        }
+    }
+    uint32_t off_run = block_excl_scan(ssum, s_tmp, &tot);
+    uint2* offs = a.offs + int64_t(unit) * nch;
+    for (int j = 0; j < CPT; ++j) {
+        const int ch = ch0 + j;
+        if (ch < nch) {
+            offs[ch] = make_uint2(off_run, s_ce[ch]);
+            off_run += s_cg[ch];
+        }
+    }
+    if (tid == 0) {
+        stw[kStTau] = tau;
+        stw[kStNeed] = need;
+        a.cand_cnt[unit] = 0u;
+        a.done_cand[unit] = 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_compact: ascending pool; chunk 0 also writes the -1 padding.
+__global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
+    __shared__ uint32_t s_tmp[kThreads / 64];
+    const Dims& d = a.d;
+    const int tid = threadIdx.x;
+    const int unit = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const int b = unit / d.Hkv;
+    const uint32_t* st = a.state + int64_t(unit) * 8;
+    const uint32_t mode = st[kStMode];
+    const int64_t Tb = seq_len_of(d, b);
+    const int64_t c0 = int64_t(chunk) * kChunk;
+    const int nvalid = int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
+    int32_t* pool = a.pool + int64_t(unit) * a.kp;
+    const int64_t kp_eff = mode == kModeEmpty ? 0 : int64_t(st[kStKpEff]);
+
+    if (chunk == 0)
+        for (int64_t j = kp_eff + tid; j < a.kp; j += kThreads) pool[j] = -1;
+    if (mode == kModeEmpty) return;
+    if (mode == kModeAll) {
+        for (int i = tid; i < nvalid; i += kThreads) pool[c0 + i] = int32_t(c0 + i);
+        return;
+    }
+    const uint32_t tau = st[kStTau], need = st[kStNeed];
+    const uint2 off = a.offs[int64_t(unit) * a.nchunks + chunk];
+    const uint32_t* keys = a.keys + int64_t(unit) * d.T_max + c0;
+    uint32_t k[4];
+    uint32_t neq = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = tid * 4 + i;
+        k[i] = tok < nvalid ? keys[tok] : 0u;
+        neq += (tok < nvalid && k[i] == tau) ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t eqr = off.y + block_excl_scan(neq, s_tmp, &tot);
+    bool sel[4];
+    uint32_t nsel = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = tid * 4 + i;
+        bool s = false;
+        if (tok < nvalid) {
+            if (k[i] > tau) s = true;
+            else if (k[i] == tau) { s = eqr < need; ++eqr; }
+        }
+        sel[i] = s;
+        nsel += s ? 1u : 0u;
+    }
+    uint32_t pos = off.x + block_excl_scan(nsel, s_tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (sel[i] && pos < uint32_t(a.kp)) pool[pos] = int32_t(c0 + tid * 4 + i);
+        pos += sel[i] ? 1u : 0u;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <int D>
+static hipError_t launch_scan(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
+    const int G = a.d.G;
+    ProfScope prof("k_scan", st);
+    if (!agg_max) {
+        if (G == 1) hipLaunchKernelGGL((k_scan<D, 1, false>), grid, dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_scan<D, 2, false>), grid, dim3(kThreads), 0, st, a);
+    } else {
+        switch (padded_g(G)) {
+            case 1: hipLaunchKernelGGL((k_scan<D, 1, true>), grid, dim3(kThreads), 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_scan<D, 2, true>), grid, dim3(kThreads), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_scan<D, 4, true>), grid, dim3(kThreads), 0, st, a); break;
+            case 8: hipLaunchKernelGGL((k_scan<D, 8, true>), grid, dim3(kThreads), 0, st, a); break;
+            case 16: hipLaunchKernelGGL((k_scan<D, 16, true>), grid, dim3(kThreads), 0, st, a); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_propose(const ProposeArgs& a, int agg_max, hipStream_t st) {
+    const int units = a.d.B * a.d.Hkv;
+    const dim3 grid(a.nchunks, units);
+    hipError_t e;
+    switch (a.d.D) {
+        case 64: e = launch_scan<64>(a, agg_max, grid, st); break;
+        case 128: e = launch_scan<128>(a, agg_max, grid, st); break;
+        case 256: e = launch_scan<256>(a, agg_max, grid, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    {
+        ProfScope prof("k_cand", st);
+        hipLaunchKernelGGL(k_cand, grid, dim3(kThreads), size_t(2) * a.nchunks * 4, st, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        ProfScope prof("k_compact", st);
+        hipLaunchKernelGGL(k_compact, grid, dim3(kThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace prism

@@ -1,0 +1,211 @@
+// prism_api.hip -- the C ABI declared in include/prism.h: argument validation, workspace carving
+// and kernel launches.  Validation touches no HIP API, so invalid calls return before any device
+// work (and can be exercised on a host without a GPU).
+#include <math.h>
+
+#include "../../include/prism.h"
+#include "prism_internal.hpp"
+
+using namespace prism;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+prism_status check_shape(const prism_shape* s) {
+    if (!s) return PRISM_ERR_INVALID_ARG;
+    if (s->B < 1 || s->Hq < 1 || s->Hkv < 1 || s->T_max < 1) return PRISM_ERR_INVALID_ARG;
+    if (s->Hq % s->Hkv != 0) return PRISM_ERR_INVALID_ARG;
+    if (s->Hq / s->Hkv > kMaxG) return PRISM_ERR_UNSUPPORTED;
+    if (s->D != 64 && s->D != 128 && s->D != 256) return PRISM_ERR_UNSUPPORTED;
+    if (s->T_max > kMaxT) return PRISM_ERR_UNSUPPORTED;
+    if (int64_t(s->B) * s->Hkv > 65535) return PRISM_ERR_UNSUPPORTED;  // grid.y bound
+    if (s->seq_lens && !aligned(s->seq_lens, 4)) return PRISM_ERR_INVALID_ARG;
+    return PRISM_OK;
+}
+
+bool valid_dtype(int dt) { return dt == PRISM_F32 || dt == PRISM_BF16; }
+bool valid_agg(int ag) { return ag == PRISM_AGG_SUM || ag == PRISM_AGG_MAX; }
+
+Dims dims_of(const prism_shape* s) {
+    Dims d;
+    d.B = s->B;
+    d.Hq = s->Hq;
+    d.Hkv = s->Hkv;
+    d.G = s->Hq / s->Hkv;
+    d.D = s->D;
+    d.T_max = s->T_max;
+    d.seq_lens = s->seq_lens;
+    return d;
+}
+
+prism_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return PRISM_OK;
+    g_last_hip_error = int(e);
+    return PRISM_ERR_HIP;
+}
+
+uint8_t* carve(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + off; }
+
+}  // namespace
+
+extern "C" {
+
+size_t prism_workspace_bytes(int op, const prism_shape* s, int32_t kp, int32_t kappa) {
+    if (check_shape(s) != PRISM_OK) return 0;
+    const int64_t units = int64_t(s->B) * s->Hkv;
+    const int GP = padded_g(s->Hq / s->Hkv);
+    switch (op) {
+        case PRISM_OP_PROPOSE:
+            if (kp < 1) return 0;
+            return propose_ws(units, s->T_max).total;
+        case PRISM_OP_REFINE:
+            if (kp < 1 || kappa < 1 || kappa > kp) return 0;
+            return refine_ws(units, kp, kappa, GP, s->D).total;
+        case PRISM_OP_DENSE:
+            return dense_ws(units, s->T_max, GP, s->D).total;
+        default:
+            return 0;
+    }
+}
+
+prism_status prism_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws || !aligned(ws, 256)) return PRISM_ERR_INVALID_ARG;
+    return hip_status(launch_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+prism_status prism_quantize_keys(const void* K, prism_dtype dt, const prism_shape* s, int8_t* Kq,
+                                 float* scales, void* stream) {
+    prism_status st = check_shape(s);
+    if (st != PRISM_OK) return st;
+    if (!valid_dtype(dt)) return PRISM_ERR_INVALID_ARG;
+    if (!K || !Kq || !scales) return PRISM_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Kq, 16) || !aligned(scales, 4)) return PRISM_ERR_INVALID_ARG;
+    const Dims d = dims_of(s);
+    return hip_status(launch_quantize_keys(K, dt == PRISM_BF16, d, Kq, scales, static_cast<hipStream_t>(stream)));
+}
+
+prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, const float* scales,
+                           const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool, float* scores,
+                           void* ws, size_t ws_bytes, void* stream) {
+    prism_status st = check_shape(s);
+    if (st != PRISM_OK) return st;
+    if (!valid_dtype(qdt) || !valid_agg(agg) || kp < 1) return PRISM_ERR_INVALID_ARG;
+    if (!q || !Kq || !scales || !pool || !ws) return PRISM_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(Kq, 16) || !aligned(scales, 4) || !aligned(pool, 4) ||
+        (scores && !aligned(scores, 4)) || !aligned(ws, 256))
+        return PRISM_ERR_INVALID_ARG;
+    const int64_t units = int64_t(s->B) * s->Hkv;
+    const ProposeWs L = propose_ws(units, s->T_max);
+    if (ws_bytes < L.total) return PRISM_ERR_WORKSPACE;
+
+    ProposeArgs a{};
+    a.d = dims_of(s);
+    a.q = q;
+    a.q_bf16 = qdt == PRISM_BF16;
+    a.Kq = Kq;
+    a.scales = scales;
+    a.kp = kp;
+    a.nchunks = int((s->T_max + kChunk - 1) / kChunk);
+    a.pool = pool;
+    a.scores = scores;
+    a.ghist = reinterpret_cast<uint32_t*>(carve(ws, L.ghist));
+    a.done_scan = reinterpret_cast<uint32_t*>(carve(ws, L.done_scan));
+    a.done_cand = reinterpret_cast<uint32_t*>(carve(ws, L.done_cand));
+    a.cand_cnt = reinterpret_cast<uint32_t*>(carve(ws, L.cand_cnt));
+    a.state = reinterpret_cast<uint32_t*>(carve(ws, L.state));
+    a.cnt_gt = reinterpret_cast<uint32_t*>(carve(ws, L.cnt_gt));
+    a.offs = reinterpret_cast<uint2*>(carve(ws, L.offs));
+    a.keys = reinterpret_cast<uint32_t*>(carve(ws, L.keys));
+    a.cand = reinterpret_cast<uint2*>(carve(ws, L.cand));
+    return hip_status(launch_propose(a, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream)));
+}
+
+prism_status prism_refine_attend(const void* q, const void* K, const void* V, prism_dtype dt,
+                                 const prism_shape* s, const int32_t* pool, int32_t kp, int32_t kappa,
+                                 prism_agg agg, float sm_scale, void* out, int32_t* idx, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream) {
+    prism_status st = check_shape(s);
+    if (st != PRISM_OK) return st;
+    if (!valid_dtype(dt) || !valid_agg(agg)) return PRISM_ERR_INVALID_ARG;
+    if (kp < 1 || kappa < 1 || kappa > kp || !(sm_scale >= 0.0f) || isinf(sm_scale)) return PRISM_ERR_INVALID_ARG;
+    if (!q || !K || !V || !pool || !out || !idx || !ws) return PRISM_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16) || !aligned(pool, 4) ||
+        !aligned(idx, 4) || (lse && !aligned(lse, 4)) || !aligned(ws, 256))
+        return PRISM_ERR_INVALID_ARG;
+    const int64_t units = int64_t(s->B) * s->Hkv;
+    const int GP = padded_g(s->Hq / s->Hkv);
+    const RefineWs L = refine_ws(units, kp, kappa, GP, s->D);
+    if (ws_bytes < L.total) return PRISM_ERR_WORKSPACE;
+    if ((int64_t(kp) + kScoreSlice - 1) / kScoreSlice > 65535) return PRISM_ERR_UNSUPPORTED;
+
+    RefineArgs a{};
+    a.d = dims_of(s);
+    a.q = q;
+    a.K = K;
+    a.V = V;
+    a.pool = pool;
+    a.kp = kp;
+    a.kappa = kappa;
+    const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf(float(s->D));
+    a.y_scale = scale * 1.4426950408889634f;
+    a.out = out;
+    a.idx = idx;
+    a.lse = lse;
+    a.ghist = reinterpret_cast<uint32_t*>(carve(ws, L.ghist));
+    a.done_s = reinterpret_cast<uint32_t*>(carve(ws, L.done_s));
+    a.done_a = reinterpret_cast<uint32_t*>(carve(ws, L.done_a));
+    a.state = reinterpret_cast<uint32_t*>(carve(ws, L.state));
+    a.skey = reinterpret_cast<uint32_t*>(carve(ws, L.skey));
+    a.logits = reinterpret_cast<float*>(carve(ws, L.logits));
+    a.sel = reinterpret_cast<int32_t*>(carve(ws, L.sel));
+    a.part_ml = reinterpret_cast<float*>(carve(ws, L.part_ml));
+    a.part_acc = reinterpret_cast<float*>(carve(ws, L.part_acc));
+    return hip_status(launch_refine(a, dt == PRISM_BF16, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream)));
+}
+
+prism_status prism_dense_ref(const void* q, const void* K, const void* V, prism_dtype dt, const prism_shape* s,
+                             float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    prism_status st = check_shape(s);
+    if (st != PRISM_OK) return st;
+    if (!valid_dtype(dt) || !(sm_scale >= 0.0f) || isinf(sm_scale)) return PRISM_ERR_INVALID_ARG;
+    if (!q || !K || !V || !out || !ws) return PRISM_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16) || (lse && !aligned(lse, 4)) ||
+        !aligned(ws, 256))
+        return PRISM_ERR_INVALID_ARG;
+    const int64_t units = int64_t(s->B) * s->Hkv;
+    const int GP = padded_g(s->Hq / s->Hkv);
+    const DenseWs L = dense_ws(units, s->T_max, GP, s->D);
+    if (ws_bytes < L.total) return PRISM_ERR_WORKSPACE;
+
+    DenseArgs a{};
+    a.d = dims_of(s);
+    a.q = q;
+    a.K = K;
+    a.V = V;
+    const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf(float(s->D));
+    a.y_scale = scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse = lse;
+    a.done = reinterpret_cast<uint32_t*>(carve(ws, L.done));
+    a.part_ml = reinterpret_cast<float*>(carve(ws, L.part_ml));
+    a.part_acc = reinterpret_cast<float*>(carve(ws, L.part_acc));
+    return hip_status(launch_dense(a, dt == PRISM_BF16, static_cast<hipStream_t>(stream)));
+}
+
+int prism_last_hip_error(void) { return g_last_hip_error; }
+
+const char* prism_status_str(prism_status st) {
+    switch (st) {
+        case PRISM_OK: return "PRISM_OK";
+        case PRISM_ERR_INVALID_ARG: return "PRISM_ERR_INVALID_ARG";
+        case PRISM_ERR_UNSUPPORTED: return "PRISM_ERR_UNSUPPORTED";
+        case PRISM_ERR_WORKSPACE: return "PRISM_ERR_WORKSPACE";
+        case PRISM_ERR_HIP: return "PRISM_ERR_HIP";
+        default: return "PRISM_ERR_UNKNOWN";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,186 @@
+// prism_attend.hpp -- shared pieces of sparse and dense decode attention on gfx950: per-row
+// logits for the G query heads of a KV head, a workgroup's softmax(.)V partial over up to 256
+// rows, and the log-sum-exp merge of the partials (token-level sparse attention, Prism Attention
+// page Sec. 1 and Sec. 2.1; split-K over rows with a merge of (max, sum, weighted V)).
+#pragma once
+
+#include "prism_device.hpp"
+
+namespace prism {
+
+// Query registers: lane `sub` of a row group holds dims [sub*EPL, sub*EPL + EPL) of each head.
+template <typename T, int D, int GP>
+struct QRegs {
+    static constexpr int EPL = Elem<T>::kPerLane;
+    float v[GP][EPL];
+    __device__ __forceinline__ void load(const T* qg, int G, int sub) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            if (h < G) {
+                unpack16<T>(load16(qg + int64_t(h) * D + sub * EPL), v[h]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) v[h][e] = 0.0f;
+            }
+        }
+    }
+};
+
+// Full-row dot products for every head: partial over the lane's EPL dims, then an all-reduce
+// over the LPR lanes of the row group (every lane of the group ends with all GP logits).
+template <typename T, int D, int GP>
+__device__ __forceinline__ void row_logits(const QRegs<T, D, GP>& q, const float* x, float* l) {
+    constexpr int EPL = Elem<T>::kPerLane;
+    constexpr int LPR = D / EPL;
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(q.v[h][e], x[e], acc);
+        l[h] = acc;
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) l[h] += __shfl_xor(l[h], o);
+    }
+}
+
+// softmax(y) V partial of one workgroup over n <= NROWS rows (NROWS <= kThreads).
+//   s_t[r]      token id of row r (rows of the unit's V)
+//   s_y[r][h]   base-2 exponent-domain logits (logit * sm_scale * log2 e); padded heads unused
+// Writes g_ml[h] = (max_r y, sum_r 2^(y - max)) and g_acc[h][d] = sum_r 2^(y - max) V[r][d]
+// for h < G.  Uses s_stat[2*GP] and s_acc[GP*D] as LDS scratch.
+template <typename T, int D, int GP, int NROWS>
+__device__ void softmax_v_partial(const T* __restrict__ Vu, const int32_t* s_t, float (*s_y)[GP], int n,
+                                  int G, float* s_stat, float* s_red, float* s_acc,
+                                  float* __restrict__ g_acc, float* __restrict__ g_ml) {
+    constexpr int EPL = Elem<T>::kPerLane;
+    constexpr int LPR = D / EPL;
+    constexpr int RPW = 64 / LPR;
+    constexpr int RPR = RPW * (kThreads / 64);
+    constexpr int ROUNDS = (NROWS + RPR - 1) / RPR;
+    constexpr int U = ROUNDS < 8 ? ROUNDS : 8;
+    static_assert(NROWS <= kThreads, "one row per thread in the softmax statistics");
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+
+    // max and sum per head over the rows (row r on thread r)
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        if (h >= G) break;
+        float y = tid < n ? s_y[tid][h] : -INFINITY;
+        y = wave_max(y);
+        if (lane == 0) s_red[wave * GP + h] = y;
+    }
+    __syncthreads();
+    if (tid < GP) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) m = fmaxf(m, s_red[w * GP + tid]);
+        s_stat[tid] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        if (h >= G) break;
+        float p = 0.0f;
+        if (tid < n) {
+            p = exp2f(s_y[tid][h] - s_stat[h]);
+            s_y[tid][h] = p;
+        }
+        p = wave_sum(p);
+        if (lane == 0) s_red[wave * GP + h] = p;
+    }
+    __syncthreads();
+    if (tid < GP) {
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) l += s_red[w * GP + tid];
+        s_stat[GP + tid] = l;
+    }
+
+    // weighted V accumulation; lane group = one row, lane = EPL consecutive dims
+    const int sub = lane % LPR;
+    const int rl = wave * RPW + lane / LPR;
+    float acc[GP][EPL];
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+    for (int r0 = 0; r0 < ROUNDS; r0 += U) {
+        uint4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = (r0 + u) * RPR + rl;
+            raw[u] = (r0 + u < ROUNDS && row < n) ? load16(Vu + int64_t(s_t[row]) * D + sub * EPL)
+                                                   : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = (r0 + u) * RPR + rl;
+            if (r0 + u < ROUNDS && row < n) {
+                float x[EPL];
+                unpack16<T>(raw[u], x);
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    if (h < G) {
+                        const float p = s_y[row][h];
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
+                    }
+                }
+            }
+        }
+    }
+    // reduce the row groups of a wave, then the waves in a fixed order (deterministic)
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
+    for (int w = 0; w < kThreads / 64; ++w) {
+        if (wave == w && lane < LPR) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                if (h < G) {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        float* dst = &s_acc[h * D + sub * EPL + e];
+                        *dst = (w == 0) ? acc[h][e] : *dst + acc[h][e];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < G * D; i += kThreads) g_acc[i] = s_acc[i];
+    if (tid < G) {
+        g_ml[2 * tid] = s_stat[tid];
+        g_ml[2 * tid + 1] = s_stat[GP + tid];
+    }
+}
+
+// Log-sum-exp merge of `np` partials (partial s at g_ml + s*GP*2, g_acc + s*GP*D).  Writes
+// out[h][d] (dtype T) and lse[h] (natural log) for h < G; np == 0 gives out = 0, lse = -inf.
+template <typename T, int D, int GP>
+__device__ void merge_partials(const float* __restrict__ g_ml, const float* __restrict__ g_acc, int np, int G,
+                               T* __restrict__ out, float* __restrict__ lse) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    for (int i = threadIdx.x; i < G * D; i += kThreads) {
+        const int h = i / D, dd = i % D;
+        float M = -INFINITY;
+        for (int s = 0; s < np; ++s) M = fmaxf(M, g_ml[(s * GP + h) * 2]);
+        float L = 0.0f, acc = 0.0f;
+        for (int s = 0; s < np; ++s) {
+            const float w = exp2f(g_ml[(s * GP + h) * 2] - M);
+            L = fmaf(g_ml[(s * GP + h) * 2 + 1], w, L);
+            acc = fmaf(g_acc[(int64_t(s) * GP + h) * D + dd], w, acc);
+        }
+        const bool empty = np == 0;
+        store_elem<T>(&out[int64_t(h) * D + dd], empty ? 0.0f : acc / L);
+        if (dd == 0 && lse) lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+    }
+}
+
+}  // namespace prism

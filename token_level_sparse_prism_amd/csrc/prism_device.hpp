@@ -1,0 +1,185 @@
+// prism_device.hpp -- device helpers for the gfx950 kernels: element loads, order keys, wave and
+// workgroup reductions/scans, radix-digit crossing search and the last-workgroup handshake.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "prism_internal.hpp"
+
+namespace prism {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// ---- element access ------------------------------------------------------------------------
+// Rows are read 16 bytes per lane: 8 bf16 values (stored as their uint16 bit patterns) or 4 fp32.
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> { static constexpr int kPerLane = 8; };
+template <> struct Elem<float> { static constexpr int kPerLane = 4; };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+    v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+    return make_uint4(uint32_t(v.x), uint32_t(v.y), uint32_t(v.z), uint32_t(v.w));
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& r, float* x);
+
+template <>
+__device__ __forceinline__ void unpack16<uint16_t>(const uint4& r, float* x) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& r, float* x) {
+    x[0] = __uint_as_float(r.x);
+    x[1] = __uint_as_float(r.y);
+    x[2] = __uint_as_float(r.z);
+    x[3] = __uint_as_float(r.w);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p);
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
+
+template <typename T>
+__device__ __forceinline__ void store_elem(T* p, float v);
+template <>
+__device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
+template <>
+__device__ __forceinline__ void store_elem<float>(float* p, float v) { *p = v; }
+
+// ---- order keys ----------------------------------------------------------------------------
+// Monotone map float -> uint32: a > b  <=>  key(a) > key(b) for non-NaN values, with -0 first
+// mapped to +0 so equal values get equal keys.  Finite values never map to key 0, which marks an
+// empty slot.
+__device__ __forceinline__ float canon_zero(float f) { return f == 0.0f ? 0.0f : f; }
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(canon_zero(f));
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// ---- wave / workgroup primitives -----------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Exclusive prefix sum over the workgroup (kThreads lanes, thread order).  s_tmp holds
+// kThreads/64 words.  Returns the thread's exclusive prefix; *total gets the workgroup sum.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+    const int lane = lane_id(), w = wave_id();
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+        const uint32_t c = s_tmp[i];
+        before += (i < w) ? c : 0u;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + x - v;
+}
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* s_tmp) {
+    uint32_t tot;
+    block_excl_scan(v, s_tmp, &tot);
+    return tot;
+}
+
+// Radix-digit crossing search.  s_hist (LDS) holds NB bin counts.  Finds the bin b such that
+// above(b) < target <= above(b) + hist[b], where above(b) counts the bins above b; requires
+// 1 <= target <= sum(hist).  Result in s_res[0..2] = (b, above(b), hist[b]).
+template <int NB>
+__device__ __forceinline__ void find_crossing(const uint32_t* s_hist, uint32_t target, uint32_t* s_tmp,
+                                              uint32_t* s_res) {
+    constexpr int BPT = NB >= kThreads ? NB / kThreads : 1;
+    const int tid = threadIdx.x;
+    uint32_t c[BPT];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+        const int bin = NB - 1 - (tid * BPT + k);  // thread order = descending bins
+        c[k] = (bin >= 0) ? s_hist[bin] : 0u;
+        sum += c[k];
+    }
+    uint32_t tot;
+    uint32_t acc = block_excl_scan(sum, s_tmp, &tot);
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+        const int bin = NB - 1 - (tid * BPT + k);
+        if (bin >= 0 && acc < target && acc + c[k] >= target) {
+            s_res[0] = uint32_t(bin);
+            s_res[1] = acc;
+            s_res[2] = c[k];
+        }
+        acc += c[k];
+    }
+    __syncthreads();
+}
+
+// Last-workgroup handshake.  Every workgroup of a unit calls this once after its global writes;
+// exactly one (the last to arrive) gets true, after an agent-scope acquire, and then sees every
+// write the others made before arriving.  Each thread releases its own writes first (the
+// workgroup barrier alone does not wait for other waves' stores).
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, uint32_t* s_flag) {
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = (prev == total - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0u;
+    if (last) __threadfence();
+    return last;
+}
+
+__device__ __forceinline__ int64_t seq_len_of(const Dims& d, int b) {
+    if (!d.seq_lens) return d.T_max;
+    int64_t t = d.seq_lens[b];
+    return t < 0 ? 0 : (t > d.T_max ? d.T_max : t);
+}
+
+}  // namespace prism

@@ -1,0 +1,65 @@
+"""One decode step of the Prism hot path on the GPU: the proposal layer, then each refined layer
+(Prism Attention page, Sec. 4 Overview: one anchor layer feeds the following shared layers;
+Sec. 5.3 / Table 3 caption: g4 = one proposal layer and three refined layers).
+
+Holds preallocated outputs and workspaces so that repeated steps allocate nothing; every step
+runs through the C ABI of libprism.so on one stream.
+"""
+from dataclasses import dataclass
+from typing import List, Optional
+
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class LayerInputs:
+    q: torch.Tensor                 # [B, Hq, D]
+    K: torch.Tensor                 # [B, Hkv, T_max, D]
+    V: Optional[torch.Tensor]       # [B, Hkv, T_max, D] (None for the anchor unless it attends)
+
+
+class PrismStep:
+    """Proposal on layer 0 (int8 keys Kq/scales), then refine_attend on layers 1..L."""
+
+    def __init__(self, q0: torch.Tensor, Kq: torch.Tensor, scales: torch.Tensor, refined: List[LayerInputs],
+                 kp: int, kappa: int, agg: int = B.AGG_SUM, seq_lens: Optional[torch.Tensor] = None,
+                 want_lse: bool = True, stream=None, ws_propose: Optional[torch.Tensor] = None,
+                 ws_refine: Optional[torch.Tensor] = None):
+        self.q0, self.Kq, self.scales = q0, Kq, scales
+        self.refined = refined
+        self.kp, self.kappa, self.agg = kp, kappa, agg
+        self.seq_lens = seq_lens
+        self.stream = stream
+        dev = q0.device
+        shape = B.make_shape(q0, Kq, seq_lens)
+        Bn, Hkv = shape.B, shape.Hkv
+        self.pool = torch.empty((Bn, Hkv, kp), dtype=torch.int32, device=dev)
+        # workspaces may be shared by steps that run one after another on the same stream
+        self.ws_p = ws_propose if ws_propose is not None else B.new_workspace(
+            B.OP_PROPOSE, shape, kp, 0, device=dev, stream=stream)
+        self.ws_r = ws_refine
+        if self.ws_r is None and refined:
+            self.ws_r = B.new_workspace(B.OP_REFINE, B.make_shape(refined[0].q, refined[0].K, seq_lens), kp, kappa,
+                                        device=dev, stream=stream)
+        self.out = [torch.empty_like(L.q) for L in refined]
+        self.idx = [torch.empty((Bn, Hkv, kappa), dtype=torch.int32, device=dev) for _ in refined]
+        self.lse = [torch.empty((Bn, L.q.shape[1]), dtype=torch.float32, device=dev) if want_lse else None
+                    for L in refined]
+
+    def propose(self):
+        return B.propose(self.q0, self.Kq, self.scales, self.kp, self.agg, seq_lens=self.seq_lens, pool=self.pool,
+                         ws=self.ws_p, stream=self.stream)
+
+    def refine(self, i: int):
+        L = self.refined[i]
+        return B.refine_attend(L.q, L.K, L.V, self.pool, self.kappa, self.agg, seq_lens=self.seq_lens,
+                               out=self.out[i], idx=self.idx[i], lse=self.lse[i], want_lse=self.lse[i] is not None,
+                               ws=self.ws_r, stream=self.stream)
+
+    def __call__(self):
+        self.propose()
+        for i in range(len(self.refined)):
+            self.refine(i)
+        return self.pool, self.idx, self.out, self.lse

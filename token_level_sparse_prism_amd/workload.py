@@ -36,6 +36,9 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from statistics import NormalDist
 from typing import Dict, List, Optional, Sequence, Tuple
@@ -129,17 +132,21 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 _ROPE_CACHE: Dict[Tuple[int, int, float], Tuple[np.ndarray, np.ndarray]] = {}
+_ROPE_LOCK = threading.Lock()
 
 
 def _rope_tables(n: int, D: int, base: float) -> Tuple[np.ndarray, np.ndarray]:
     key = (n, D, base)
-    if key not in _ROPE_CACHE:
-        j = np.arange(D // 2, dtype=np.float64)
-        theta = base ** (-2.0 * j / D)
-        ang = np.arange(n, dtype=np.float64)[:, None] * theta[None, :]
-        _ROPE_CACHE.clear()
-        _ROPE_CACHE[key] = (np.cos(ang), np.sin(ang))
-    return _ROPE_CACHE[key]
+    with _ROPE_LOCK:
+        tab = _ROPE_CACHE.get(key)
+        if tab is None:
+            j = np.arange(D // 2, dtype=np.float64)
+            theta = base ** (-2.0 * j / D)
+            ang = np.arange(n, dtype=np.float64)[:, None] * theta[None, :]
+            tab = (np.cos(ang), np.sin(ang))
+            _ROPE_CACHE.clear()
+            _ROPE_CACHE[key] = tab
+    return tab
 
 
 def rope_rotate(x: np.ndarray, positions: np.ndarray, base: float, cos_sin=None) -> np.ndarray:
@@ -278,22 +285,29 @@ class Workload:
         return len(self.q)
 
 
-def generate(cfg: Config, layers: Optional[Sequence[int]] = None) -> Workload:
-    """Generate every layer (anchor + refined) of a config on the host."""
+def generate(cfg: Config, layers: Optional[Sequence[int]] = None, threads: int = 0) -> Workload:
+    """Generate every layer (anchor + refined) of a config on the host.  Units are generated in
+    a thread pool (each unit's draws are keyed independently, so the result does not depend on
+    the thread count)."""
     lens = cfg.lengths()
     layers = list(range(cfg.n_refined + 1)) if layers is None else list(layers)
+    threads = threads or min(16, os.cpu_count() or 1)
     qs, Ks, Vs = [], [], []
     for l in layers:
         q = queries(cfg, l, lens)
         K = np.zeros((cfg.B, cfg.Hkv, cfg.T, cfg.D), dtype=np.float32)
         want_v = l >= 1 or cfg.anchor_v
         V = np.zeros_like(K) if want_v else None
-        for b in range(cfg.B):
-            for g in range(cfg.Hkv):
-                k, v = unit_tensors(cfg, b, g, l, q, int(lens[b]))
-                K[b, g] = k
-                if V is not None:
-                    V[b, g] = v
+
+        def one(bg):
+            b, g = bg
+            k, v = unit_tensors(cfg, b, g, l, q, int(lens[b]))
+            K[b, g] = k
+            if V is not None:
+                V[b, g] = v
+
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, [(b, g) for b in range(cfg.B) for g in range(cfg.Hkv)]))
         qs.append(q)
         Ks.append(K)
         Vs.append(V)
