@@ -34,6 +34,7 @@ def parse():
     p.add_argument("--profile-steps", type=int, default=100, help="steps of the per-kernel event pass")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="time stream launches instead of HIP graphs")
     return p.parse_args()
 
 
@@ -105,18 +106,29 @@ def main():
     for i in range(args.warmup):
         steps[i % R]()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        steps[i % R]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / args.steps
+
+    def timed(run):
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(args.steps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - w0
+
+    ms_stream, wall_stream = timed(lambda i: steps[i % R]())
+    ms_graph = wall_graph = None
+    if not args.no_graph:
+        graphs = [st.capture() for st in steps]
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        ms_graph, wall_graph = timed(lambda i: graphs[i % R].replay())
+    ms_per_step = ms_graph if ms_graph is not None else ms_stream
+    wall = wall_graph if wall_graph is not None else wall_stream
 
     # per-kernel durations: a separate pass with HIP events around every launch (same work)
     PB.profile_reset()
@@ -184,6 +196,8 @@ def main():
         "hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(ab["step"]),
         "roofline": roofline,
+        "launch": "hip_graph" if ms_graph is not None else "stream",
+        "ms_per_step_stream_launch": round(ms_stream, 5),
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3), "gen_s": round(gen_s, 1),

@@ -251,3 +251,22 @@ def test_full_size_128k_sampled_units():
             assert set(gidx[0, g].tolist()) <= set(gpool[0, g].tolist())
         check_refine_batch(gidx, host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(), w.q[l], w.K[l], w.V[l],
                            w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype, units={(0, 0), (0, 5)})
+
+
+def test_graph_replay_matches_eager():
+    """A HIP graph of one whole step, replayed several times with eager work in between, gives the
+    eager step's pools, index sets and outputs bit for bit every time."""
+    c = W.CONFIGS["cfg2"].with_(B=1, Hkv=2, Hq=8, T=12000)
+    w = W.generate(c)
+    step, _, _ = run_step_gpu(w, c.kp, c.kappa)
+    ref = [step.pool.clone()] + [t.clone() for t in step.idx] + [t.clone() for t in step.out]
+    graph = step.capture()
+    for i in range(5):
+        for t in [step.pool] + list(step.idx) + list(step.out):
+            t.fill_(7)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        cur = [step.pool] + list(step.idx) + list(step.out)
+        for a, b in zip(ref, cur):
+            assert torch.equal(a, b), f"replay {i}"

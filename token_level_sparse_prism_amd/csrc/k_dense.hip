@@ -71,13 +71,13 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
                                                   part_ml + int64_t(chunk) * GP * 2);
     }
 
-    if (!arrive_last(&a.done[unit], gridDim.x, &s_flag)) return;
+    if (!arrive_last(&a.done[int64_t(unit) * kCtrStride], gridDim.x, &s_flag)) return;
 
     const int np = int((Tb + kDenseChunk - 1) / kDenseChunk);
     const int64_t hq0 = int64_t(b) * d.Hq + int64_t(g) * G;
     merge_partials<T, D, GP>(part_ml, part_acc, np, G, static_cast<T*>(a.out) + hq0 * D,
                              a.lse ? a.lse + hq0 : nullptr);
-    if (tid == 0) a.done[unit] = 0u;
+    if (tid == 0) a.done[int64_t(unit) * kCtrStride] = 0u;
 }
 
 template <typename T, int D>

@@ -2,15 +2,17 @@
 // Overview and Sec. 4.1: the anchor layer scores the whole context and emits an expanded pool;
 // Sec. 4.2: the scoring uses the compressed key cache; Sec. 5.1: pool size n = rho * kappa).
 //
-// Three launches per call, each over (chunk of 1024 tokens) x (unit = batch, KV head):
+// Three launches per call, none of which waits on another workgroup:
 //   k_scan     streams the int8 keys once (the HBM-bound pass), writes a 32-bit order key per
-//              token and a histogram of the keys' top 12 bits; the unit's last workgroup finds
-//              the bin that holds the kp-th largest key.
-//   k_cand     counts, per chunk, the keys above that bin and appends the keys inside it to a
-//              candidate list; the unit's last workgroup finishes the exact threshold on the
-//              remaining 20 bits and turns the counts into per-chunk output offsets.
-//   k_compact  writes the pool in ascending token order: every key above the threshold, and the
-//              lowest-index keys equal to it.
+//              token and adds each workgroup's histogram of the keys' top 12 bits into the unit's
+//              histogram (hist1).
+//   k_cand     (per 1024-token chunk) finds from hist1 the bin that holds the kp-th largest key,
+//              counts the chunk's keys above that bin, appends the keys inside it to the unit's
+//              candidate list and histograms their bits 19..8 (hist2).
+//   k_compact  (per chunk) finishes the exact threshold from hist2 and the candidate list, derives
+//              the chunk's output offset from the counts of the chunks before it, and writes the
+//              pool in ascending token order: every key above the threshold and the lowest-index
+//              keys equal to it.
 // The selection is exact integer work, so the pool is bit-identical to a full sort by
 // (score desc, token asc).
 #include "prism_device.hpp"
@@ -18,8 +20,11 @@
 
 namespace prism {
 
-enum { kModeEmpty = 0, kModeAll = 1, kModeSelect = 2 };
-enum { kStMode = 0, kStBin = 1, kStAbove = 2, kStHbin = 3, kStTau = 4, kStNeed = 5, kStKpEff = 6 };
+enum { kStBin = 0, kStAbove = 1, kStKpEff = 2 };
+
+__device__ __forceinline__ int chunk_tokens(int64_t Tb, int64_t c0) {
+    return int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
+}
 
 // ---------------------------------------------------------------------------------------------
 // k_scan.  NQ int8 query vectors are dotted with each key row:
@@ -28,7 +33,7 @@ enum { kStMode = 0, kStBin = 1, kStAbove = 2, kStHbin = 3, kStTau = 4, kStNeed =
 //                    [-8, 7] and |hi| <= 127, so A = 16*(hi.K) + lo.K exactly in int32;
 //   agg MAX:         NQ = GP (G rounded up to a power of two), one vector per head.
 // A lane holds 16 bytes of a key row (D/16 lanes per token); a wave reads 1 KiB of
-// consecutive rows per load.
+// consecutive rows per load.  Workgroup x of unit y handles chunks x, x + gridDim.x, ...
 template <int D, int NQ, bool kMax>
 __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     constexpr int LPT = D / 16;            // lanes per token
@@ -43,21 +48,20 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     __shared__ float s_scale[kChunk];
     __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
     __shared__ float s_red[kThreads / 64];
-    __shared__ uint32_t s_tmp[kThreads / 64];
-    __shared__ uint32_t s_res[4];
-    __shared__ uint32_t s_flag;
 
     const Dims& d = a.d;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int unit = blockIdx.y;
-    const int chunk = blockIdx.x;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
     const int64_t Tb = seq_len_of(d, b);
-    const int64_t c0 = int64_t(chunk) * kChunk;
-    const int nvalid = int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
 
     for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;
+    if (blockIdx.x == 0) {  // per-call state of the later kernels
+        uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
+        for (int i = tid; i < kHistBins; i += kThreads) h2[i] = 0u;
+        if (tid == 0) a.cand_cnt[int64_t(unit) * kCtrStride] = 0u;
+    }
 
     // ---- query quantization: one absmax over the group's G*D values ----
     const int64_t qoff = (int64_t(b) * d.Hq + int64_t(g) * G) * D;
@@ -91,11 +95,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
             s_q[1][dd] = int8_t(lo);
         }
     }
-    const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
-    for (int i = tid; i < nvalid; i += kThreads) s_scale[i] = scl[i];
     __syncthreads();
-
-    // ---- streaming int8 scan ----
     const int sub = lane % LPT;
     int qv[NQ][4];
 #pragma unroll
@@ -103,9 +103,20 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * 16]);
         qv[n][0] = int(w.x); qv[n][1] = int(w.y); qv[n][2] = int(w.z); qv[n][3] = int(w.w);
     }
-    const int8_t* base = a.Kq + (int64_t(unit) * d.T_max + c0) * D + sub * 16;
     const int tok_lane = wave * TPW + lane / LPT;
-    if (nvalid > 0) {
+
+    for (int chunk = blockIdx.x; chunk < a.nchunks; chunk += gridDim.x) {
+        const int64_t c0 = int64_t(chunk) * kChunk;
+        const int nvalid = chunk_tokens(Tb, c0);
+        if (nvalid == 0) break;  // later chunks of this workgroup are past T_b too
+        const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
+#pragma unroll 4
+        for (int i = tid; i < nvalid; i += kThreads) s_scale[i] = scl[i];
+        __syncthreads();
+
+        // ---- streaming int8 scan ----
+        const int8_t* base = a.Kq + (int64_t(unit) * d.T_max + c0) * D + sub * 16;
+#pragma unroll 1
         for (int r0 = 0; r0 < ROUNDS; r0 += U) {
             uint4 kv[U];
 #pragma unroll
@@ -150,85 +161,70 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
                 }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- keys out (coalesced), top-digit histogram ----
-    uint32_t* kout = a.keys + int64_t(unit) * d.T_max + c0;
-    float* sout = a.scores ? a.scores + int64_t(unit) * d.T_max + c0 : nullptr;
-    for (int i = tid; i < nvalid; i += kThreads) {
-        const uint32_t k = s_key[i];
-        atomicAdd(&s_hist[k >> kKeyShift], 1u);
-        kout[i] = k;
-        if (sout) sout[i] = key_to_float(k);
+        // ---- keys out (coalesced), top-digit histogram ----
+        uint32_t* kout = a.keys + int64_t(unit) * a.kstride + c0;
+        float* sout = a.scores ? a.scores + int64_t(unit) * d.T_max + c0 : nullptr;
+        for (int i = tid; i < nvalid; i += kThreads) {
+            const uint32_t k = s_key[i];
+            atomicAdd(&s_hist[k >> kKeyShift], 1u);
+            kout[i] = k;
+            if (sout) sout[i] = key_to_float(k);
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    uint32_t* gh = a.ghist + int64_t(unit) * kHistBins;
+    uint32_t* gh = a.hist1 + int64_t(unit) * kHistBins;
     for (int i = tid; i < kHistBins; i += kThreads) {
         const uint32_t c = s_hist[i];
         if (c) atomicAdd(&gh[i], c);
     }
-
-    if (!arrive_last(&a.done_scan[unit], gridDim.x, &s_flag)) return;
-
-    // ---- last workgroup of the unit: bin of the kp-th largest key ----
-    const int64_t kp_eff = Tb < a.kp ? Tb : a.kp;
-    uint32_t* st = a.state + int64_t(unit) * 8;
-    if (Tb == 0 || kp_eff == Tb) {
-        if (tid == 0) {
-            st[kStMode] = Tb == 0 ? kModeEmpty : kModeAll;
-            st[kStKpEff] = uint32_t(kp_eff);
-        }
-    } else {
-        for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = gh[i];
-        __syncthreads();
-        find_crossing<kHistBins>(s_hist, uint32_t(kp_eff), s_tmp, s_res);
-        if (tid == 0) {
-            st[kStMode] = kModeSelect;
-            st[kStBin] = s_res[0];
-            st[kStAbove] = s_res[1];
-            st[kStHbin] = s_res[2];
-            st[kStKpEff] = uint32_t(kp_eff);
-        }
-    }
-    for (int i = tid; i < kHistBins; i += kThreads) gh[i] = 0u;
-    if (tid == 0) a.done_scan[unit] = 0u;
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_cand.  Dynamic LDS: 2 * nchunks words (per-chunk counts of candidates above / equal to the
-// threshold), used only by the unit's last workgroup.
+// k_cand: grid (chunks, units).
 __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
-    extern __shared__ uint32_t s_dyn[];
-    __shared__ uint32_t s_hist[kHistBins];
     __shared__ uint32_t s_tmp[kThreads / 64];
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_base;
-    __shared__ uint32_t s_flag;
 
     const Dims& d = a.d;
     const int tid = threadIdx.x;
     const int unit = blockIdx.y;
     const int chunk = blockIdx.x;
     const int b = unit / d.Hkv;
-    const uint32_t* st = a.state + int64_t(unit) * 8;
-    if (st[kStMode] != kModeSelect) return;  // uniform over the unit: nobody arrives
-    const uint32_t bin = st[kStBin];
     const int64_t Tb = seq_len_of(d, b);
+    const int64_t kp_eff = Tb < a.kp ? Tb : a.kp;
+    if (Tb == 0 || kp_eff == Tb) return;  // empty sequence / take-all: nothing to select
     const int64_t c0 = int64_t(chunk) * kChunk;
-    const int nvalid = int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
-    const uint32_t* keys = a.keys + int64_t(unit) * d.T_max;
-    uint2* cand = a.cand + int64_t(unit) * d.T_max;
+    const int nvalid = chunk_tokens(Tb, c0);
 
-    // 4 consecutive tokens per thread
+    // keys of the chunk (4 consecutive tokens per thread) and the unit's top-digit histogram
+    const uint32_t* keys = a.keys + int64_t(unit) * a.kstride + c0;
     uint32_t k[4];
+    if (tid * 4 + 3 < nvalid) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + tid * 4);
+        k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k[i] = tid * 4 + i < nvalid ? keys[tid * 4 + i] : 0u;
+    }
+    uint32_t h[16];
+    load_hist_desc(a.hist1 + int64_t(unit) * kHistBins, h);
+    find_crossing_regs<16>(h, kHistBins, uint32_t(kp_eff), s_tmp, s_res);
+    const uint32_t bin = s_res[0];
+    if (chunk == 0 && tid == 0) {
+        uint32_t* st = a.state + int64_t(unit) * 8;
+        st[kStBin] = bin;
+        st[kStAbove] = s_res[1];
+        st[kStKpEff] = uint32_t(kp_eff);
+    }
+
     uint32_t ngt = 0, ncand = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int tok = tid * 4 + i;
-        k[i] = tok < nvalid ? keys[c0 + tok] : 0u;
-        const uint32_t kb = k[i] >> kKeyShift;
-        if (tok < nvalid) {
+        if (tid * 4 + i < nvalid) {
+            const uint32_t kb = k[i] >> kKeyShift;
             ngt += kb > bin ? 1u : 0u;
             ncand += kb == bin ? 1u : 0u;
         }
@@ -238,153 +234,131 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
     uint32_t cpre = block_excl_scan(ncand, s_tmp, &ctot);
     if (tid == 0) {
         a.cnt_gt[int64_t(unit) * a.nchunks + chunk] = chunk_gt;
-        s_base = ctot ? atomicAdd(&a.cand_cnt[unit], ctot) : 0u;
+        s_base = ctot ? atomicAdd(&a.cand_cnt[int64_t(unit) * kCtrStride], ctot) : 0u;
     }
     __syncthreads();
-    const uint32_t base = s_base;
+    if (ncand) {
+        uint2* cand = a.cand + int64_t(unit) * d.T_max;
+        uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
+        const uint32_t base = s_base;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tok = tid * 4 + i;
-        if (tok < nvalid && (k[i] >> kKeyShift) == bin) {
-            const uint32_t pos = base + cpre++;
-            if (pos < uint32_t(d.T_max)) cand[pos] = make_uint2(k[i], uint32_t(c0 + tok));
+        for (int i = 0; i < 4; ++i) {
+            if (tid * 4 + i < nvalid && (k[i] >> kKeyShift) == bin) {
+                const uint32_t pos = base + cpre++;
+                if (pos < uint32_t(d.T_max)) cand[pos] = make_uint2(k[i], uint32_t(c0 + tid * 4 + i));
+                atomicAdd(&h2[(k[i] >> 8) & 0xFFFu], 1u);
+            }
         }
-    }
-
-    if (!arrive_last(&a.done_cand[unit], gridDim.x, &s_flag)) return;
-
-    // ---- last workgroup: exact threshold among the candidates, then per-chunk offsets ----
-    uint32_t* stw = a.state + int64_t(unit) * 8;
-    const uint32_t c = min(a.cand_cnt[unit], uint32_t(d.T_max));
-    const uint32_t kp_eff = st[kStKpEff];
-    const uint32_t need_bin = kp_eff - st[kStAbove];
-
-    // digit A: key bits 19..8
-    for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < c; i += kThreads) atomicAdd(&s_hist[(cand[i].x >> 8) & 0xFFFu], 1u);
-    __syncthreads();
-    find_crossing<kHistBins>(s_hist, need_bin, s_tmp, s_res);
-    const uint32_t da = s_res[0], above_a = s_res[1];
-    // digit B: key bits 7..0 among keys whose digit A matches
-    for (int i = tid; i < 256; i += kThreads) s_hist[i] = 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < c; i += kThreads) {
-        const uint32_t kk = cand[i].x;
-        if (((kk >> 8) & 0xFFFu) == da) atomicAdd(&s_hist[kk & 0xFFu], 1u);
-    }
-    __syncthreads();
-    find_crossing<256>(s_hist, need_bin - above_a, s_tmp, s_res);
-    const uint32_t tau = (bin << kKeyShift) | (da << 8) | s_res[0];
-    const uint32_t need = need_bin - above_a - s_res[1];  // keys equal to tau to take, >= 1
-
-    // per-chunk counts of candidates above / equal to tau
-    const int nch = a.nchunks;
-    uint32_t* s_cg = s_dyn;
-    uint32_t* s_ce = s_dyn + nch;
-    for (int i = tid; i < 2 * nch; i += kThreads) s_dyn[i] = 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < c; i += kThreads) {
-        const uint2 e = cand[i];
-        const int ch = int(e.y / kChunk);
-        if (e.x > tau) atomicAdd(&s_cg[ch], 1u);
-        else if (e.x == tau) atomicAdd(&s_ce[ch], 1u);
-    }
-    __syncthreads();
-
-    // eq_before[ch] = equal keys in earlier chunks; take[ch] = equal keys of ch inside the budget;
-    // offset[ch] = selected tokens in earlier chunks.  Each thread owns CPT consecutive chunks.
-    const int CPT = (nch + kThreads - 1) / kThreads;
-    const int ch0 = tid * CPT;
-    const uint32_t* cgt = a.cnt_gt + int64_t(unit) * nch;
-    uint32_t esum = 0;
-    for (int j = 0; j < CPT; ++j) {
-        const int ch = ch0 + j;
-        if (ch < nch) esum += s_ce[ch];
-    }
-    uint32_t tot;
-    uint32_t eq_run = block_excl_scan(esum, s_tmp, &tot);
-    uint32_t ssum = 0;
-    for (int j = 0; j < CPT; ++j) {
-        const int ch = ch0 + j;
-        if (ch < nch) {
-            const uint32_t ce = s_ce[ch];
-            const uint32_t take = eq_run >= need ? 0u : min(ce, need - eq_run);
-            const uint32_t selc = cgt[ch] + s_cg[ch] + take;
-            s_cg[ch] = selc;  // reuse: selected count of the chunk
-            s_ce[ch] = eq_run; // reuse: equal keys before the chunk
-            eq_run += ce;
-            ssum += selc;
-        }
-    }
-    uint32_t off_run = block_excl_scan(ssum, s_tmp, &tot);
-    uint2* offs = a.offs + int64_t(unit) * nch;
-    for (int j = 0; j < CPT; ++j) {
-        const int ch = ch0 + j;
-        if (ch < nch) {
-            offs[ch] = make_uint2(off_run, s_ce[ch]);
-            off_run += s_cg[ch];
-        }
-    }
-    if (tid == 0) {
-        stw[kStTau] = tau;
-        stw[kStNeed] = need;
-        a.cand_cnt[unit] = 0u;
-        a.done_cand[unit] = 0u;
     }
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_compact: ascending pool; chunk 0 also writes the -1 padding.
+// k_compact: grid (chunks, units).  Chunk 0 also writes the -1 padding and clears hist1.
 __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
     __shared__ uint32_t s_tmp[kThreads / 64];
+    __shared__ uint32_t s_res[4];
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint2 s_cand[kLdsCand];
+
     const Dims& d = a.d;
     const int tid = threadIdx.x;
     const int unit = blockIdx.y;
     const int chunk = blockIdx.x;
     const int b = unit / d.Hkv;
-    const uint32_t* st = a.state + int64_t(unit) * 8;
-    const uint32_t mode = st[kStMode];
     const int64_t Tb = seq_len_of(d, b);
+    const int64_t kp_eff = Tb < a.kp ? Tb : a.kp;
     const int64_t c0 = int64_t(chunk) * kChunk;
-    const int nvalid = int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
+    const int nvalid = chunk_tokens(Tb, c0);
     int32_t* pool = a.pool + int64_t(unit) * a.kp;
-    const int64_t kp_eff = mode == kModeEmpty ? 0 : int64_t(st[kStKpEff]);
 
-    if (chunk == 0)
+    if (chunk == 0) {
         for (int64_t j = kp_eff + tid; j < a.kp; j += kThreads) pool[j] = -1;
-    if (mode == kModeEmpty) return;
-    if (mode == kModeAll) {
+        uint32_t* h1 = a.hist1 + int64_t(unit) * kHistBins;
+        for (int i = tid; i < kHistBins; i += kThreads) h1[i] = 0u;  // zero for the next call
+    }
+    if (Tb == 0 || nvalid == 0) return;
+    if (kp_eff == Tb) {  // take all
         for (int i = tid; i < nvalid; i += kThreads) pool[c0 + i] = int32_t(c0 + i);
         return;
     }
-    const uint32_t tau = st[kStTau], need = st[kStNeed];
-    const uint2 off = a.offs[int64_t(unit) * a.nchunks + chunk];
-    const uint32_t* keys = a.keys + int64_t(unit) * d.T_max + c0;
+
+    // loads: state, hist2 (descending layout), candidate count, counts of the earlier chunks, keys
+    const uint32_t* st = a.state + int64_t(unit) * 8;
+    const uint32_t bin = st[kStBin];
+    const uint32_t above = st[kStAbove];
+    const uint32_t c = min(a.cand_cnt[int64_t(unit) * kCtrStride], uint32_t(d.T_max));
+    uint32_t h[16];
+    load_hist_desc(a.hist2 + int64_t(unit) * kHistBins, h);
+    uint32_t gt_before = 0;
+    const uint32_t* cg = a.cnt_gt + int64_t(unit) * a.nchunks;
+#pragma unroll 4
+    for (int i = tid; i < chunk; i += kThreads) gt_before += cg[i];
+    const uint32_t* keys = a.keys + int64_t(unit) * a.kstride + c0;
     uint32_t k[4];
+    if (tid * 4 + 3 < nvalid) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + tid * 4);
+        k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k[i] = tid * 4 + i < nvalid ? keys[tid * 4 + i] : 0u;
+    }
+    const uint2* cand = a.cand + int64_t(unit) * d.T_max;
+    const bool in_lds = c <= uint32_t(kLdsCand);
+    if (in_lds) {
+#pragma unroll 8
+        for (uint32_t i = tid; i < c; i += kThreads) s_cand[i] = cand[i];
+    }
+
+    // digit A (bits 19..8) of the threshold
+    const uint32_t need_bin = uint32_t(kp_eff) - above;
+    find_crossing_regs<16>(h, kHistBins, need_bin, s_tmp, s_res);
+    const uint32_t da = s_res[0], above_a = s_res[1];
+    const uint32_t pre = (bin << 12) | da;
+    // digit B (bits 7..0) among the candidates whose top 24 bits match
+    s_hist[tid] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < c; i += kThreads) {
+        const uint32_t kk = in_lds ? s_cand[i].x : cand[i].x;
+        if ((kk >> 8) == pre) atomicAdd(&s_hist[kk & 0xFFu], 1u);
+    }
+    __syncthreads();
+    find_crossing<256>(s_hist, need_bin - above_a, s_tmp, s_res);
+    const uint32_t tau = (pre << 8) | s_res[0];
+    const uint32_t need = need_bin - above_a - s_res[1];  // keys equal to tau to take, >= 1
+
+    // candidates of the earlier chunks above / equal to tau
+    uint32_t cgt = 0, ceq = 0;
+    for (uint32_t i = tid; i < c; i += kThreads) {
+        const uint2 e = in_lds ? s_cand[i] : cand[i];
+        if (e.y < uint32_t(c0)) {
+            cgt += e.x > tau ? 1u : 0u;
+            ceq += e.x == tau ? 1u : 0u;
+        }
+    }
+    gt_before = block_sum_u32(gt_before, s_tmp);
+    cgt = block_sum_u32(cgt, s_tmp);
+    const uint32_t eq_before = block_sum_u32(ceq, s_tmp);
+    const uint32_t offset = gt_before + cgt + min(eq_before, need);
+
+    // ordered compaction of the chunk
     uint32_t neq = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tok = tid * 4 + i;
-        k[i] = tok < nvalid ? keys[tok] : 0u;
-        neq += (tok < nvalid && k[i] == tau) ? 1u : 0u;
-    }
+    for (int i = 0; i < 4; ++i) neq += (tid * 4 + i < nvalid && k[i] == tau) ? 1u : 0u;
     uint32_t tot;
-    uint32_t eqr = off.y + block_excl_scan(neq, s_tmp, &tot);
+    uint32_t eqr = eq_before + block_excl_scan(neq, s_tmp, &tot);
     bool sel[4];
     uint32_t nsel = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int tok = tid * 4 + i;
         bool s = false;
-        if (tok < nvalid) {
+        if (tid * 4 + i < nvalid) {
             if (k[i] > tau) s = true;
             else if (k[i] == tau) { s = eqr < need; ++eqr; }
         }
         sel[i] = s;
         nsel += s ? 1u : 0u;
     }
-    uint32_t pos = off.x + block_excl_scan(nsel, s_tmp, &tot);
+    uint32_t pos = offset + block_excl_scan(nsel, s_tmp, &tot);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (sel[i] && pos < uint32_t(a.kp)) pool[pos] = int32_t(c0 + tid * 4 + i);
@@ -416,17 +390,20 @@ static hipError_t launch_scan(const ProposeArgs& a, int agg_max, dim3 grid, hipS
 hipError_t launch_propose(const ProposeArgs& a, int agg_max, hipStream_t st) {
     const int units = a.d.B * a.d.Hkv;
     const dim3 grid(a.nchunks, units);
+    int per_unit = (kScanWgs + units - 1) / units;
+    per_unit = per_unit < 1 ? 1 : (per_unit > a.nchunks ? a.nchunks : per_unit);
+    const dim3 sgrid(per_unit, units);
     hipError_t e;
     switch (a.d.D) {
-        case 64: e = launch_scan<64>(a, agg_max, grid, st); break;
-        case 128: e = launch_scan<128>(a, agg_max, grid, st); break;
-        case 256: e = launch_scan<256>(a, agg_max, grid, st); break;
+        case 64: e = launch_scan<64>(a, agg_max, sgrid, st); break;
+        case 128: e = launch_scan<128>(a, agg_max, sgrid, st); break;
+        case 256: e = launch_scan<256>(a, agg_max, sgrid, st); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
     {
         ProfScope prof("k_cand", st);
-        hipLaunchKernelGGL(k_cand, grid, dim3(kThreads), size_t(2) * a.nchunks * 4, st, a);
+        hipLaunchKernelGGL(k_cand, grid, dim3(kThreads), 0, st, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {

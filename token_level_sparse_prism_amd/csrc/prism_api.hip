@@ -109,15 +109,14 @@ prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, con
     a.scales = scales;
     a.kp = kp;
     a.nchunks = int((s->T_max + kChunk - 1) / kChunk);
+    a.kstride = key_stride(s->T_max);
     a.pool = pool;
     a.scores = scores;
-    a.ghist = reinterpret_cast<uint32_t*>(carve(ws, L.ghist));
-    a.done_scan = reinterpret_cast<uint32_t*>(carve(ws, L.done_scan));
-    a.done_cand = reinterpret_cast<uint32_t*>(carve(ws, L.done_cand));
+    a.hist1 = reinterpret_cast<uint32_t*>(carve(ws, L.hist1));
+    a.hist2 = reinterpret_cast<uint32_t*>(carve(ws, L.hist2));
     a.cand_cnt = reinterpret_cast<uint32_t*>(carve(ws, L.cand_cnt));
     a.state = reinterpret_cast<uint32_t*>(carve(ws, L.state));
     a.cnt_gt = reinterpret_cast<uint32_t*>(carve(ws, L.cnt_gt));
-    a.offs = reinterpret_cast<uint2*>(carve(ws, L.offs));
     a.keys = reinterpret_cast<uint32_t*>(carve(ws, L.keys));
     a.cand = reinterpret_cast<uint2*>(carve(ws, L.cand));
     return hip_status(launch_propose(a, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream)));
@@ -149,18 +148,16 @@ prism_status prism_refine_attend(const void* q, const void* K, const void* V, pr
     a.pool = pool;
     a.kp = kp;
     a.kappa = kappa;
+    a.kstride = key_stride(kp);
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf(float(s->D));
     a.y_scale = scale * 1.4426950408889634f;
     a.out = out;
     a.idx = idx;
     a.lse = lse;
     a.ghist = reinterpret_cast<uint32_t*>(carve(ws, L.ghist));
-    a.done_s = reinterpret_cast<uint32_t*>(carve(ws, L.done_s));
     a.done_a = reinterpret_cast<uint32_t*>(carve(ws, L.done_a));
-    a.state = reinterpret_cast<uint32_t*>(carve(ws, L.state));
     a.skey = reinterpret_cast<uint32_t*>(carve(ws, L.skey));
     a.logits = reinterpret_cast<float*>(carve(ws, L.logits));
-    a.sel = reinterpret_cast<int32_t*>(carve(ws, L.sel));
     a.part_ml = reinterpret_cast<float*>(carve(ws, L.part_ml));
     a.part_acc = reinterpret_cast<float*>(carve(ws, L.part_acc));
     return hip_status(launch_refine(a, dt == PRISM_BF16, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream)));

@@ -154,28 +154,46 @@ __device__ void softmax_v_partial(const T* __restrict__ Vu, const int32_t* s_t, 
         }
         __syncthreads();
     }
-    for (int i = tid; i < G * D; i += kThreads) g_acc[i] = s_acc[i];
+    // partials are read by another workgroup of the same kernel: write through to device scope
+    for (int i = tid; i < G * D; i += kThreads) st_dev(&g_acc[i], s_acc[i]);
     if (tid < G) {
-        g_ml[2 * tid] = s_stat[tid];
-        g_ml[2 * tid + 1] = s_stat[GP + tid];
+        st_dev(&g_ml[2 * tid], s_stat[tid]);
+        st_dev(&g_ml[2 * tid + 1], s_stat[GP + tid]);
     }
 }
 
-// Log-sum-exp merge of `np` partials (partial s at g_ml + s*GP*2, g_acc + s*GP*D).  Writes
-// out[h][d] (dtype T) and lse[h] (natural log) for h < G; np == 0 gives out = 0, lse = -inf.
+// Log-sum-exp merge of `np` partials (partial s at g_ml + s*GP*2, g_acc + s*GP*D), read at
+// device scope, eight partials per batch of independent loads.  Writes out[h][d] (dtype T) and
+// lse[h] (natural log) for h < G; np == 0 gives out = 0, lse = -inf.
 template <typename T, int D, int GP>
 __device__ void merge_partials(const float* __restrict__ g_ml, const float* __restrict__ g_acc, int np, int G,
                                T* __restrict__ out, float* __restrict__ lse) {
     constexpr float kLn2 = 0.6931471805599453f;
+    constexpr int BATCH = 8;
     for (int i = threadIdx.x; i < G * D; i += kThreads) {
         const int h = i / D, dd = i % D;
-        float M = -INFINITY;
-        for (int s = 0; s < np; ++s) M = fmaxf(M, g_ml[(s * GP + h) * 2]);
-        float L = 0.0f, acc = 0.0f;
-        for (int s = 0; s < np; ++s) {
-            const float w = exp2f(g_ml[(s * GP + h) * 2] - M);
-            L = fmaf(g_ml[(s * GP + h) * 2 + 1], w, L);
-            acc = fmaf(g_acc[(int64_t(s) * GP + h) * D + dd], w, acc);
+        float M = -INFINITY, L = 0.0f, acc = 0.0f;
+        for (int s0 = 0; s0 < np; s0 += BATCH) {
+            float m[BATCH], l[BATCH], v[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int s = s0 + u;
+                const bool ok = s < np;
+                m[u] = ok ? ld_dev(&g_ml[(s * GP + h) * 2]) : -INFINITY;
+                l[u] = ok ? ld_dev(&g_ml[(s * GP + h) * 2 + 1]) : 0.0f;
+                v[u] = ok ? ld_dev(&g_acc[(int64_t(s) * GP + h) * D + dd]) : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                if (s0 + u < np) {
+                    const float Mn = fmaxf(M, m[u]);
+                    const float c_old = exp2f(M - Mn);
+                    const float c_new = exp2f(m[u] - Mn);
+                    L = L * c_old + l[u] * c_new;
+                    acc = acc * c_old + v[u] * c_new;
+                    M = Mn;
+                }
+            }
         }
         const bool empty = np == 0;
         store_elem<T>(&out[int64_t(h) * D + dd], empty ? 0.0f : acc / L);

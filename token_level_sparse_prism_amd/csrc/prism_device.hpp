@@ -127,22 +127,18 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* s_tmp) {
     return tot;
 }
 
-// Radix-digit crossing search.  s_hist (LDS) holds NB bin counts.  Finds the bin b such that
-// above(b) < target <= above(b) + hist[b], where above(b) counts the bins above b; requires
-// 1 <= target <= sum(hist).  Result in s_res[0..2] = (b, above(b), hist[b]).
-template <int NB>
-__device__ __forceinline__ void find_crossing(const uint32_t* s_hist, uint32_t target, uint32_t* s_tmp,
-                                              uint32_t* s_res) {
-    constexpr int BPT = NB >= kThreads ? NB / kThreads : 1;
+// Radix-digit crossing search over NB bins spread BPT per thread in DESCENDING bin order:
+// thread i holds c[k] = count of bin (NB - 1 - (i*BPT + k)).  Finds the bin b with
+// above(b) < target <= above(b) + count(b), above(b) = count of the bins above b; requires
+// 1 <= target <= total.  Result in s_res[0..2] = (b, above(b), count(b)), visible to all threads
+// on return.
+template <int BPT>
+__device__ __forceinline__ void find_crossing_regs(const uint32_t* c, int NB, uint32_t target, uint32_t* s_tmp,
+                                                   uint32_t* s_res) {
     const int tid = threadIdx.x;
-    uint32_t c[BPT];
     uint32_t sum = 0;
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-        const int bin = NB - 1 - (tid * BPT + k);  // thread order = descending bins
-        c[k] = (bin >= 0) ? s_hist[bin] : 0u;
-        sum += c[k];
-    }
+    for (int k = 0; k < BPT; ++k) sum += c[k];
     uint32_t tot;
     uint32_t acc = block_excl_scan(sum, s_tmp, &tot);
 #pragma unroll
@@ -158,22 +154,62 @@ __device__ __forceinline__ void find_crossing(const uint32_t* s_hist, uint32_t t
     __syncthreads();
 }
 
-// Last-workgroup handshake.  Every workgroup of a unit calls this once after its global writes;
-// exactly one (the last to arrive) gets true, after an agent-scope acquire, and then sees every
-// write the others made before arriving.  Each thread releases its own writes first (the
-// workgroup barrier alone does not wait for other waves' stores).
+// Same search over a histogram in LDS.
+template <int NB>
+__device__ __forceinline__ void find_crossing(const uint32_t* s_hist, uint32_t target, uint32_t* s_tmp,
+                                              uint32_t* s_res) {
+    constexpr int BPT = NB >= kThreads ? NB / kThreads : 1;
+    uint32_t c[BPT];
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+        const int bin = NB - 1 - (int(threadIdx.x) * BPT + k);
+        c[k] = bin >= 0 ? s_hist[bin] : 0u;
+    }
+    find_crossing_regs<BPT>(c, NB, target, s_tmp, s_res);
+}
+
+// Loads a 4096-bin global histogram 16 bins per thread in the descending layout above.
+__device__ __forceinline__ void load_hist_desc(const uint32_t* __restrict__ h, uint32_t* c) {
+    const int base = kHistBins - 16 * (int(threadIdx.x) + 1);  // ascending bins base .. base+15
+    const uint4* p = reinterpret_cast<const uint4*>(h + base);
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = p[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        c[15 - 4 * i] = v[i].x;
+        c[14 - 4 * i] = v[i].y;
+        c[13 - 4 * i] = v[i].z;
+        c[12 - 4 * i] = v[i].w;
+    }
+}
+
+// ---- device-scope data hand-off inside one kernel ----------------------------------------
+// Values another workgroup reads in the same kernel are written through to device scope and read
+// at device scope; the handshake waits for this workgroup's stores to complete and counts
+// arrivals with one relaxed atomic on a per-unit counter (no cache write-back fence).
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, uint32_t* s_flag) {
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's device-scope stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = (prev == total - 1) ? 1u : 0u;
     }
     __syncthreads();
-    const bool last = *s_flag != 0u;
-    if (last) __threadfence();
-    return last;
+    return *s_flag != 0u;
+}
+
+// ---- wave ballots --------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
 }
 
 __device__ __forceinline__ int64_t seq_len_of(const Dims& d, int b) {

@@ -9,11 +9,21 @@
 namespace prism {
 
 // ---- tiling constants --------------------------------------------------------------------
+#ifndef PRISM_SCAN_WGS
+#define PRISM_SCAN_WGS 1024            // target scan workgroups over all units
+#endif
+#ifndef PRISM_SCORE_SLICE
+#define PRISM_SCORE_SLICE 256
+#endif
 constexpr int kThreads = 256;          // every kernel runs 4 waves of 64 lanes
-constexpr int kChunk = 1024;           // tokens per workgroup in the proposal kernels
-constexpr int kScoreSlice = 256;       // pool slots per workgroup in pool scoring
+constexpr int kChunk = 1024;           // tokens per chunk in the proposal kernels
+constexpr int kScanWgs = PRISM_SCAN_WGS;
+constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in pool scoring
 constexpr int kAttendSlice = 64;       // selected rows per workgroup in sparse attention
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
+constexpr int kLdsKeys = 16384;        // pool keys a sparse-attention workgroup keeps in LDS
+constexpr int kLdsCand = 4096;         // threshold candidates a compaction workgroup keeps in LDS
+constexpr int kCtrStride = 16;         // counters sit 64 bytes apart (no shared cache line)
 constexpr int kHistBits = 12;          // first radix digit: top 12 bits of the order key
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kKeyShift = 32 - kHistBits;
@@ -25,33 +35,35 @@ constexpr int kMaxG = 16;
 // The first `ctrl_bytes` of a workspace hold counters and histograms that must be zero when a
 // call starts; the call's last workgroups put them back to zero.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// per-unit rows of 32-bit keys are padded to whole 16-byte vectors
+inline int64_t key_stride(int64_t n) { return (n + 3) & ~int64_t(3); }
 
 struct ProposeWs {
-    size_t ghist, done_scan, done_cand, cand_cnt, ctrl_bytes;
-    size_t state, cnt_gt, offs, keys, cand, total;
+    size_t hist1, ctrl_bytes;
+    size_t hist2, cand_cnt, state, cnt_gt, keys, cand, total;
 };
 
+// hist1 must be zero when a call starts (the call's compaction kernel zeroes it again);
+// hist2 and cand_cnt are zeroed by the call's own scan kernel.
 inline ProposeWs propose_ws(int64_t units, int64_t T_max) {
     ProposeWs w{};
     const int64_t nch = (T_max + kChunk - 1) / kChunk;
     size_t o = 0;
-    w.ghist = o;     o = align256(o + size_t(units) * kHistBins * 4);
-    w.done_scan = o; o = align256(o + size_t(units) * 4);
-    w.done_cand = o; o = align256(o + size_t(units) * 4);
-    w.cand_cnt = o;  o = align256(o + size_t(units) * 4);
+    w.hist1 = o;     o = align256(o + size_t(units) * kHistBins * 4);
     w.ctrl_bytes = o;
+    w.hist2 = o;     o = align256(o + size_t(units) * kHistBins * 4);
+    w.cand_cnt = o;  o = align256(o + size_t(units) * kCtrStride * 4);
     w.state = o;     o = align256(o + size_t(units) * 8 * 4);
     w.cnt_gt = o;    o = align256(o + size_t(units) * nch * 4);
-    w.offs = o;      o = align256(o + size_t(units) * nch * 8);
-    w.keys = o;      o = align256(o + size_t(units) * T_max * 4);
+    w.keys = o;      o = align256(o + size_t(units) * key_stride(T_max) * 4);
     w.cand = o;      o = align256(o + size_t(units) * T_max * 8);
     w.total = o;
     return w;
 }
 
 struct RefineWs {
-    size_t ghist, done_s, done_a, ctrl_bytes;
-    size_t state, skey, logits, sel, part_ml, part_acc, total;
+    size_t ghist, done_a, ctrl_bytes;
+    size_t skey, logits, part_ml, part_acc, total;
 };
 
 inline int padded_g(int G) {
@@ -66,13 +78,10 @@ inline RefineWs refine_ws(int64_t units, int64_t kp, int64_t kappa, int GP, int 
     const int64_t nsa = (kappa + kAttendSlice - 1) / kAttendSlice;
     size_t o = 0;
     w.ghist = o;    o = align256(o + size_t(units) * kHistBins * 4);
-    w.done_s = o;   o = align256(o + size_t(units) * 4);
-    w.done_a = o;   o = align256(o + size_t(units) * 4);
+    w.done_a = o;   o = align256(o + size_t(units) * kCtrStride * 4);
     w.ctrl_bytes = o;
-    w.state = o;    o = align256(o + size_t(units) * 8 * 4);
-    w.skey = o;     o = align256(o + size_t(units) * kp * 4);
+    w.skey = o;     o = align256(o + size_t(units) * key_stride(kp) * 4);
     w.logits = o;   o = align256(o + size_t(units) * kp * logit_stride(GP) * 4);
-    w.sel = o;      o = align256(o + size_t(units) * kappa * 4);
     w.part_ml = o;  o = align256(o + size_t(units) * nsa * GP * 2 * 4);
     w.part_acc = o; o = align256(o + size_t(units) * nsa * GP * D * 4);
     w.total = o;
@@ -87,7 +96,7 @@ inline DenseWs dense_ws(int64_t units, int64_t T_max, int GP, int D) {
     DenseWs w{};
     const int64_t nc = (T_max + kDenseChunk - 1) / kDenseChunk;
     size_t o = 0;
-    w.done = o;     o = align256(o + size_t(units) * 4);
+    w.done = o;     o = align256(o + size_t(units) * kCtrStride * 4);
     w.ctrl_bytes = o;
     w.part_ml = o;  o = align256(o + size_t(units) * nc * GP * 2 * 4);
     w.part_acc = o; o = align256(o + size_t(units) * nc * GP * D * 4);
@@ -110,17 +119,16 @@ struct ProposeArgs {
     const float* scales;
     int32_t kp;
     int nchunks;
+    int64_t kstride;        // key_stride(T_max)
     int32_t* pool;
     float* scores;          // optional
-    uint32_t* ghist;        // [U][kHistBins]
-    uint32_t* done_scan;    // [U]
-    uint32_t* done_cand;    // [U]
-    uint32_t* cand_cnt;     // [U]
-    uint32_t* state;        // [U][8]: mode, bin, above, hbin, tau, need, kp_eff
-    uint32_t* cnt_gt;       // [U][nchunks]
-    uint2* offs;            // [U][nchunks]: (output offset, equal-key rank base)
-    uint32_t* keys;         // [U][T_max]
-    uint2* cand;            // [U][T_max]: (key, token)
+    uint32_t* hist1;        // [U][kHistBins]  top 12 bits of every key
+    uint32_t* hist2;        // [U][kHistBins]  bits 19..8 of the keys in the threshold bin
+    uint32_t* cand_cnt;     // [U][kCtrStride]
+    uint32_t* state;        // [U][8]: bin, above, kp_eff
+    uint32_t* cnt_gt;       // [U][nchunks] keys above the threshold bin per chunk
+    uint32_t* keys;         // [U][kstride]
+    uint2* cand;            // [U][T_max]: (key, token) of the threshold bin
 };
 
 struct RefineArgs {
@@ -130,17 +138,15 @@ struct RefineArgs {
     const void* V;
     const int32_t* pool;
     int32_t kp, kappa;
+    int64_t kstride;        // key_stride(kp)
     float y_scale;          // sm_scale * log2(e): logits -> base-2 exponent domain
     void* out;
     int32_t* idx;
     float* lse;
-    uint32_t* ghist;        // [U][kHistBins]
-    uint32_t* done_s;       // [U]
-    uint32_t* done_a;       // [U]
-    uint32_t* state;        // [U][8]: mode, kappa_eff
-    uint32_t* skey;         // [U][kp]
+    uint32_t* ghist;        // [U][kHistBins] top 12 bits of the pool keys
+    uint32_t* done_a;       // [U][kCtrStride]
+    uint32_t* skey;         // [U][kstride] order key of S per pool slot (0 = empty slot)
     float* logits;          // [U][kp][LS]
-    int32_t* sel;           // [U][kappa] selected pool slots
     float* part_ml;         // [U][nsa][GP][2]
     float* part_acc;        // [U][nsa][GP][D]
 };
@@ -153,7 +159,7 @@ struct DenseArgs {
     float y_scale;
     void* out;
     float* lse;
-    uint32_t* done;         // [U]
+    uint32_t* done;         // [U][kCtrStride]
     float* part_ml;         // [U][nc][GP][2]
     float* part_acc;        // [U][nc][GP][D]
 };

@@ -63,3 +63,14 @@ class PrismStep:
         for i in range(len(self.refined)):
             self.refine(i)
         return self.pool, self.idx, self.out, self.lse
+
+    def capture(self):
+        """Record one whole step (proposal + every refined layer) into a HIP graph and return it.
+
+        Nothing is allocated and no memset is issued while capturing, so replays are valid;
+        each replay recomputes the step from the current contents of the input buffers."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self()
+        self.graph = graph
+        return graph
