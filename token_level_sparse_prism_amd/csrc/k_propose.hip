@@ -56,21 +56,65 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     const int G = d.G;
     const int64_t Tb = seq_len_of(d, b);
 
-    for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;
     if (blockIdx.x == 0) {  // per-call state of the later kernels
         uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
         for (int i = tid; i < kHistBins; i += kThreads) h2[i] = 0u;
         if (tid == 0) a.cand_cnt[int64_t(unit) * kCtrStride] = 0u;
     }
+    const int sub = lane % LPT;
+    const int tok_lane = wave * TPW + lane / LPT;
 
-    // ---- query quantization: one absmax over the group's G*D values ----
+    // ---- query quantization: one absmax over the group's G*D values (s_hist holds q meanwhile).
+    // Loads complete in issue order, so the small query and scale loads go out before the first
+    // chunk's key rows, which then stream in while the codes are computed.
+    float* s_qf = reinterpret_cast<float*>(s_hist);
     const int64_t qoff = (int64_t(b) * d.Hq + int64_t(g) * G) * D;
-    auto qval = [&](int i) -> float {
-        return a.q_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[qoff + i])
-                        : static_cast<const float*>(a.q)[qoff + i];
+    const int qe = a.q_bf16 ? 8 : 4;  // values per 16-byte piece
+    constexpr int QP = (kMaxG * 256 / 4 + kThreads - 1) / kThreads;  // 16-byte query pieces per thread, max
+    uint4 qraw[QP];
+    const int npieces = G * D / qe;
+#pragma unroll
+    for (int i = 0; i < QP; ++i) {
+        const int p = tid + i * kThreads;
+        qraw[i] = p < npieces ? load16(static_cast<const uint8_t*>(a.q) + (qoff * (a.q_bf16 ? 2 : 4)) + p * 16)
+                              : make_uint4(0, 0, 0, 0);
+    }
+    int chunk = blockIdx.x;
+    int64_t c0 = int64_t(chunk) * kChunk;
+    int nvalid = chunk < a.nchunks ? chunk_tokens(Tb, c0) : 0;
+    float scl_pre[kChunk / kThreads];
+    {
+        const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
+#pragma unroll
+        for (int i = 0; i < kChunk / kThreads; ++i) {
+            const int t = tid + i * kThreads;
+            scl_pre[i] = t < nvalid ? scl[t] : 0.0f;
+        }
+    }
+    uint4 kv[U];
+    auto issue = [&](int r0) {
+        const int8_t* base = a.Kq + (int64_t(unit) * d.T_max + c0) * D + sub * 16;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tok = (r0 + u) * TPR + tok_lane;
+            kv[u] = tok < nvalid ? load16_stream(base + int64_t(tok) * D) : make_uint4(0, 0, 0, 0);
+        }
     };
+    issue(0);
     float amax = 0.0f;
-    for (int i = tid; i < G * D; i += kThreads) amax = fmaxf(amax, fabsf(qval(i)));
+#pragma unroll
+    for (int i = 0; i < QP; ++i) {
+        const int p = tid + i * kThreads;
+        if (p < npieces) {
+            float x[8];
+            if (a.q_bf16) unpack16<uint16_t>(qraw[i], x);
+            else unpack16<float>(qraw[i], x);
+            for (int e = 0; e < qe; ++e) {
+                s_qf[p * qe + e] = x[e];
+                amax = fmaxf(amax, fabsf(x[e]));
+            }
+        }
+    }
     amax = wave_max(amax);
     if (lane == 0) s_red[wave] = amax;
     __syncthreads();
@@ -83,12 +127,12 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     for (int dd = tid; dd < D; dd += kThreads) {
         if constexpr (kMax) {
 #pragma unroll
-            for (int h = 0; h < NQ; ++h) s_q[h][dd] = int8_t(h < G ? code(qval(h * D + dd)) : 0);
+            for (int h = 0; h < NQ; ++h) s_q[h][dd] = int8_t(h < G ? code(s_qf[h * D + dd]) : 0);
         } else if constexpr (NQ == 1) {
-            s_q[0][dd] = int8_t(code(qval(dd)));
+            s_q[0][dd] = int8_t(code(s_qf[dd]));
         } else {
             int qs = 0;
-            for (int h = 0; h < G; ++h) qs += code(qval(h * D + dd));
+            for (int h = 0; h < G; ++h) qs += code(s_qf[h * D + dd]);
             const int lo = ((qs + 8) & 15) - 8;
             const int hi = (qs - lo) >> 4;
             s_q[0][dd] = int8_t(hi);
@@ -96,34 +140,35 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         }
     }
     __syncthreads();
-    const int sub = lane % LPT;
     int qv[NQ][4];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
         const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * 16]);
         qv[n][0] = int(w.x); qv[n][1] = int(w.y); qv[n][2] = int(w.z); qv[n][3] = int(w.w);
     }
-    const int tok_lane = wave * TPW + lane / LPT;
+    for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;  // q is in registers now
+#pragma unroll
+    for (int i = 0; i < kChunk / kThreads; ++i) s_scale[tid + i * kThreads] = scl_pre[i];
+    __syncthreads();
 
-    for (int chunk = blockIdx.x; chunk < a.nchunks; chunk += gridDim.x) {
-        const int64_t c0 = int64_t(chunk) * kChunk;
-        const int nvalid = chunk_tokens(Tb, c0);
+    bool first = true;
+    for (; chunk < a.nchunks; chunk += gridDim.x) {
+        if (!first) {
+            c0 = int64_t(chunk) * kChunk;
+            nvalid = chunk_tokens(Tb, c0);
+        }
         if (nvalid == 0) break;  // later chunks of this workgroup are past T_b too
-        const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
+        if (!first) {
+            const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
 #pragma unroll 4
-        for (int i = tid; i < nvalid; i += kThreads) s_scale[i] = scl[i];
-        __syncthreads();
+            for (int i = tid; i < nvalid; i += kThreads) s_scale[i] = scl[i];
+            __syncthreads();
+        }
 
         // ---- streaming int8 scan ----
-        const int8_t* base = a.Kq + (int64_t(unit) * d.T_max + c0) * D + sub * 16;
 #pragma unroll 1
         for (int r0 = 0; r0 < ROUNDS; r0 += U) {
-            uint4 kv[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int tok = (r0 + u) * TPR + tok_lane;
-                kv[u] = tok < nvalid ? load16_stream(base + int64_t(tok) * D) : make_uint4(0, 0, 0, 0);
-            }
+            if (!(first && r0 == 0)) issue(r0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int tok = (r0 + u) * TPR + tok_lane;
@@ -136,8 +181,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
                         int acc = 0;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_sdot4(qv[h][i], k4[i], acc, false);
-#pragma unroll
-                        for (int o = LPT / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+                        acc = group_sum_i<LPT>(acc);
                         if (h < G) best = (h == 0 || acc > best) ? acc : best;
                     }
                     A = best;
@@ -151,8 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
                         for (int i = 0; i < 4; ++i) acc1 = __builtin_amdgcn_sdot4(qv[1][i], k4[i], acc1, false);
                         acc0 = acc0 * 16 + acc1;
                     }
-#pragma unroll
-                    for (int o = LPT / 2; o >= 1; o >>= 1) acc0 += __shfl_xor(acc0, o);
+                    acc0 = group_sum_i<LPT>(acc0);
                     A = acc0;
                 }
                 if (sub == 0 && tok < nvalid) {
@@ -161,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
                 }
             }
         }
+        first = false;
         __syncthreads();
 
         // ---- keys out (coalesced), top-digit histogram ----

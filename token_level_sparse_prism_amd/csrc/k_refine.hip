@@ -3,18 +3,17 @@
 // touches only the pool, so its cost does not grow with the context).
 //
 // Two launches per call:
-//   k_rscore  grid (pool slices) x units.  Gathers the pool's K rows, computes the G heads'
-//             logits (fp32) and the group score S, stores the logits and an order key of S per
-//             slot (0 for an empty slot), and adds the slice's histogram of the keys' top 12 bits
-//             into the unit's histogram.
-//   k_attend  grid (64 selected rows) x units.  Every workgroup loads the unit's keys into LDS and
-//             derives the exact top-kappa itself (radix digits 12/12/8, ties to the lower slot),
-//             ranks the selected slots in slot order with wave ballots, writes idx for its 64
+//   k_rscore  grid (pool slices of 64 slots) x units.  Gathers the pool's K rows, computes the G
+//             heads' logits (fp32) and the group score S, and stores the logits and an order key
+//             of S per slot (0 for an empty slot).
+//   k_attend  grid (64 selected ranks) x units.  Every workgroup reads the unit's keys into
+//             registers and derives the exact top-kappa itself (radix digits 12/12/8 in LDS, ties
+//             to the lower slot), ranks the selected slots in slot order, writes idx for its 64
 //             ranks, gathers their V rows and forms a softmax(.)V partial from the stored logits.
-//             The unit's last workgroup merges the partials (log-sum-exp) into out and lse and
-//             clears the histogram for the next call.
+//             The unit's last workgroup merges the partials (log-sum-exp) into out and lse.
 #include "prism_attend.hpp"
 #include "prism_prof.hpp"
+#include "prism_select.hpp"
 
 namespace prism {
 
@@ -29,10 +28,8 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
     constexpr int LS = GP < 4 ? 4 : GP;
     static_assert(ROUNDS % U == 0, "slice must hold whole unrolled rounds");
 
-    __shared__ uint32_t s_hist[kHistBins];
-
     const Dims& d = a.d;
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int lane = lane_id(), wave = wave_id();
     const int unit = blockIdx.y;
     const int slice = blockIdx.x;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
@@ -40,8 +37,6 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
     const int64_t Tb = seq_len_of(d, b);
     const int64_t kp = a.kp;
     const int sub = lane % LPR;
-
-    for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;
 
     QRegs<T, D, GP> q;
     q.load(static_cast<const T*>(a.q) + (int64_t(b) * d.Hq + int64_t(g) * G) * D, G, sub);
@@ -51,7 +46,6 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
     float* logits = a.logits + int64_t(unit) * kp * LS;
     const int64_t j0 = int64_t(slice) * kScoreSlice;
     const int rl = wave * RPW + lane / LPR;
-    __syncthreads();
 
     for (int r0 = 0; r0 < ROUNDS; r0 += U) {
         int32_t t[U];
@@ -89,43 +83,32 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
                     v.w = h4 + 3 < GP ? l[h4 + 3] : 0.0f;
                     *reinterpret_cast<float4*>(&logits[j * LS + h4]) = v;
                 }
-                if (valid) atomicAdd(&s_hist[key >> kKeyShift], 1u);
             }
         }
     }
-    __syncthreads();
-    uint32_t* gh = a.ghist + int64_t(unit) * kHistBins;
-    for (int i = tid; i < kHistBins; i += kThreads) {
-        const uint32_t c = s_hist[i];
-        if (c) atomicAdd(&gh[i], c);
-    }
 }
 
-// Keys of the unit's pool slots, from LDS (kp <= kLdsKeys) or straight from global memory.
-struct KeySrc {
-    const uint32_t* lds;
-    const uint32_t* glob;
-    __device__ __forceinline__ uint32_t operator()(int64_t j) const { return lds ? lds[j] : glob[j]; }
-};
+constexpr int kAttendThreads = 1024;  // 16 waves: latency of the selection is hidden 4 waves per SIMD
 
 template <typename T, int D, int GP>
-__global__ __launch_bounds__(kThreads) void k_attend(RefineArgs a) {
+__global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
+    constexpr int NT = kAttendThreads;
     constexpr int LS = GP < 4 ? 4 : GP;
-    extern __shared__ uint32_t s_keys[];  // kp words when the keys fit in LDS
-    __shared__ uint32_t s_hist[kHistBins];
-    __shared__ uint32_t s_tmp[kThreads / 64];
+    __shared__ uint32_t s_hist[kHistPadded];  // selection histograms, then the merge's table
+    __shared__ uint32_t s_tmp[NT / 64 * 4];
     __shared__ uint32_t s_res[4];
-    __shared__ uint32_t s_w[2][kThreads / 64];
+    __shared__ uint32_t s_cand[kSelCandTotal];
+    __shared__ uint32_t s_ccount[NT / 64];
     __shared__ int32_t s_slot[kAttendSlice];
     __shared__ int32_t s_t[kAttendSlice];
     __shared__ float s_y[kAttendSlice][GP];
     __shared__ float s_stat[2 * GP];
-    __shared__ float s_red[(kThreads / 64) * GP];
+    __shared__ float s_red[(NT / 64) * GP];
     __shared__ float s_acc[GP * D];
     __shared__ uint32_t s_flag;
 
     const Dims& d = a.d;
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int tid = threadIdx.x;
     const int unit = blockIdx.y;
     const int slice = blockIdx.x;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
@@ -133,98 +116,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(RefineArgs a) {
     const int64_t kp = a.kp;
     const int64_t Tb = seq_len_of(d, b);
     const int r0 = slice * kAttendSlice;
-    const uint32_t* gkeys = a.skey + int64_t(unit) * a.kstride;
-    uint32_t* gh = a.ghist + int64_t(unit) * kHistBins;
 
-    // ---- loads: the unit's histogram (16 bins per thread) and its keys into LDS ----
-    uint32_t h[16];
-    load_hist_desc(gh, h);
-    const bool lds_keys = kp <= kLdsKeys;
-    if (lds_keys) {
-        const int64_t kp4 = kp & ~int64_t(3);
-#pragma unroll 4
-        for (int64_t j = int64_t(tid) * 4; j < kp4; j += int64_t(kThreads) * 4)
-            *reinterpret_cast<uint4*>(&s_keys[j]) = *reinterpret_cast<const uint4*>(&gkeys[j]);
-        for (int64_t j = kp4 + tid; j < kp; j += kThreads) s_keys[j] = gkeys[j];
-    }
-    const KeySrc key{lds_keys ? s_keys : nullptr, gkeys};
-
-    // ---- exact top-kappa threshold: tau and the number of keys equal to tau to take ----
-    uint32_t nv = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) nv += (kHistBins - 1 - (tid * 16 + k)) > 0 ? h[k] : 0u;  // bin 0 = empty slots
-    const uint32_t n_valid = block_sum_u32(nv, s_tmp);  // its barriers also publish s_keys
-    const uint32_t kappa_eff = n_valid < uint32_t(a.kappa) ? n_valid : uint32_t(a.kappa);
-    uint32_t tau = 1u, need = 0xFFFFFFFFu;  // kappa_eff == n_valid: every valid key (>= 1) is taken
-    if (kappa_eff > 0 && kappa_eff < n_valid) {
-        find_crossing_regs<16>(h, kHistBins, kappa_eff, s_tmp, s_res);
-        const uint32_t bin = s_res[0], above = s_res[1];
-        for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;
-        __syncthreads();
-        for (int64_t j = tid; j < kp; j += kThreads) {
-            const uint32_t k = key(j);
-            if ((k >> kKeyShift) == bin) atomicAdd(&s_hist[(k >> 8) & 0xFFFu], 1u);
-        }
-        __syncthreads();
-        find_crossing<kHistBins>(s_hist, kappa_eff - above, s_tmp, s_res);
-        const uint32_t da = s_res[0], above_a = s_res[1];
-        const uint32_t pre = (bin << 12) | da;
-        s_hist[tid] = 0u;
-        __syncthreads();
-        for (int64_t j = tid; j < kp; j += kThreads) {
-            const uint32_t k = key(j);
-            if ((k >> 8) == pre) atomicAdd(&s_hist[k & 0xFFu], 1u);
-        }
-        __syncthreads();
-        find_crossing<256>(s_hist, kappa_eff - above - above_a, s_tmp, s_res);
-        tau = (pre << 8) | s_res[0];
-        need = kappa_eff - above - above_a - s_res[1];
-    }
-
-    // ---- ranks of the selected slots in slot order (wave w scans a contiguous quarter) ----
-    const int n = int(kappa_eff) - r0 < 0 ? 0 : (int(kappa_eff) - r0 > kAttendSlice ? kAttendSlice : int(kappa_eff) - r0);
-    if (n > 0) {
-        const int64_t Q = ((kp + 4 * 64 - 1) / (4 * 64)) * 64;
-        const int64_t w0 = int64_t(wave) * Q, w1 = (w0 + Q < kp) ? w0 + Q : kp;
-        uint32_t eq_w = 0;
-        for (int64_t j = w0 + lane; j - lane < w1; j += 64) {
-            const uint32_t k = j < w1 ? key(j) : 0u;
-            eq_w += __popcll(ballot64(k == tau && k != 0u));
-        }
-        if (lane == 0) s_w[0][wave] = eq_w;
-        __syncthreads();
-        uint32_t eq_run = 0;
-        for (int w = 0; w < wave; ++w) eq_run += s_w[0][w];
-        uint32_t sel_w = 0;
-        for (int64_t j = w0 + lane; j - lane < w1; j += 64) {
-            const uint32_t k = j < w1 ? key(j) : 0u;
-            const bool eq = k == tau && k != 0u;
-            const uint64_t me = ballot64(eq);
-            const bool take = k > tau || (eq && eq_run + lanes_below(me) < need);
-            eq_run += __popcll(me);
-            sel_w += __popcll(ballot64(take));
-        }
-        if (lane == 0) s_w[1][wave] = sel_w;
-        __syncthreads();
-        uint32_t rank = 0;
-        eq_run = 0;
-        for (int w = 0; w < wave; ++w) {
-            rank += s_w[1][w];
-            eq_run += s_w[0][w];
-        }
-        for (int64_t j = w0 + lane; j - lane < w1 && rank < uint32_t(r0 + n); j += 64) {
-            const uint32_t k = j < w1 ? key(j) : 0u;
-            const bool eq = k == tau && k != 0u;
-            const uint64_t me = ballot64(eq);
-            const bool take = k > tau || (eq && eq_run + lanes_below(me) < need);
-            eq_run += __popcll(me);
-            const uint64_t mt = ballot64(take);
-            const uint32_t r = rank + lanes_below(mt);
-            if (take && r >= uint32_t(r0) && r < uint32_t(r0 + n)) s_slot[r - r0] = int32_t(j);
-            rank += __popcll(mt);
-        }
-    }
-    __syncthreads();
+    const SelResult sr = select_slice<NT>(a.skey + int64_t(unit) * a.kstride, kp, uint32_t(a.kappa), r0, kAttendSlice,
+                                      s_hist, s_tmp, s_res, s_cand, s_ccount, s_slot);
+    const int n = sr.n;
 
     // ---- idx and the slice's rows ----
     const int32_t* pool = a.pool + int64_t(unit) * kp;
@@ -255,18 +150,21 @@ __global__ __launch_bounds__(kThreads) void k_attend(RefineArgs a) {
     float* part_acc = a.part_acc + int64_t(unit) * nsa * GP * D;
     if (n > 0) {
         const T* Vu = static_cast<const T*>(a.V) + int64_t(unit) * d.T_max * D;
-        softmax_v_partial<T, D, GP, kAttendSlice>(Vu, s_t, s_y, n, G, s_stat, s_red, s_acc,
+        softmax_v_partial<T, D, GP, kAttendSlice, NT>(Vu, s_t, s_y, n, G, s_stat, s_red, s_acc,
                                                    part_acc + int64_t(slice) * GP * D,
                                                    part_ml + int64_t(slice) * GP * 2);
     }
 
     if (!arrive_last(&a.done_a[int64_t(unit) * kCtrStride], gridDim.x, &s_flag)) return;
 
-    const int np = int((kappa_eff + kAttendSlice - 1) / kAttendSlice);
+    const int np = int((sr.kappa_eff + kAttendSlice - 1) / kAttendSlice);
     const int64_t hq0 = int64_t(b) * d.Hq + int64_t(g) * G;
-    merge_partials<T, D, GP>(part_ml, part_acc, np, G, static_cast<T*>(a.out) + hq0 * D,
-                             a.lse ? a.lse + hq0 : nullptr);
-    for (int i = tid; i < kHistBins; i += kThreads) gh[i] = 0u;  // every workgroup has read it
+    T* out = static_cast<T*>(a.out) + hq0 * D;
+    float* lse = a.lse ? a.lse + hq0 : nullptr;
+    if (merge_lds_floats(np, GP) <= kHistBins)
+        merge_partials_lds<T, D, GP, NT>(part_ml, part_acc, np, G, out, lse, reinterpret_cast<float*>(s_hist));
+    else
+        merge_partials<T, D, GP, NT>(part_ml, part_acc, np, G, out, lse);
     if (tid == 0) a.done_a[int64_t(unit) * kCtrStride] = 0u;
 }
 
@@ -283,9 +181,8 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
-        const size_t dyn = a.kp <= kLdsKeys ? size_t(a.kp) * 4 : 0;
         ProfScope prof("k_attend", st);
-        hipLaunchKernelGGL((k_attend<T, D, GP>), ga, dim3(kThreads), dyn, st, a);
+        hipLaunchKernelGGL((k_attend<T, D, GP>), ga, dim3(kAttendThreads), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -154,7 +154,6 @@ prism_status prism_refine_attend(const void* q, const void* K, const void* V, pr
     a.out = out;
     a.idx = idx;
     a.lse = lse;
-    a.ghist = reinterpret_cast<uint32_t*>(carve(ws, L.ghist));
     a.done_a = reinterpret_cast<uint32_t*>(carve(ws, L.done_a));
     a.skey = reinterpret_cast<uint32_t*>(carve(ws, L.skey));
     a.logits = reinterpret_cast<float*>(carve(ws, L.logits));

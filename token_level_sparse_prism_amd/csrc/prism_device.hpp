@@ -86,32 +86,82 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Data-parallel-primitive (DPP) lane moves: VALU operand swizzles, no LDS round trip.
+// Controls used: quad_perm [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
+// row_mirror = 0x140, row_shr:n = 0x110 + n.  Lanes whose source lies outside their row of 16
+// read 0 (bound_ctrl).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
+    return uint32_t(__builtin_amdgcn_readlane(int(v), l));
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// All-reduce over aligned groups of N lanes (N in {1, 2, 4, 8, 16, 32, 64}); every lane of a
+// group ends with the group's result.  Groups of up to 16 lanes stay inside a DPP row.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp_f32<0xB1>(v);
+    if constexpr (N >= 4) v += dpp_f32<0x4E>(v);
+    if constexpr (N >= 8) v += dpp_f32<0x141>(v);
+    if constexpr (N >= 16) v += dpp_f32<0x140>(v);
+    if constexpr (N >= 32) v += __shfl_xor(v, 16);
+    if constexpr (N >= 64) v += __shfl_xor(v, 32);
     return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+template <int N>
+__device__ __forceinline__ int group_sum_i(int v) {
+    if constexpr (N >= 2) v += int(dpp_u32<0xB1>(uint32_t(v)));
+    if constexpr (N >= 4) v += int(dpp_u32<0x4E>(uint32_t(v)));
+    if constexpr (N >= 8) v += int(dpp_u32<0x141>(uint32_t(v)));
+    if constexpr (N >= 16) v += int(dpp_u32<0x140>(uint32_t(v)));
+    if constexpr (N >= 32) v += __shfl_xor(v, 16);
+    if constexpr (N >= 64) v += __shfl_xor(v, 32);
     return v;
 }
 
-// Exclusive prefix sum over the workgroup (kThreads lanes, thread order).  s_tmp holds
-// kThreads/64 words.  Returns the thread's exclusive prefix; *total gets the workgroup sum.
+// Whole-wave reductions, result uniform across the wave.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = group_sum<16>(v);
+    return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+// Inclusive prefix sum over the wave: row_shr steps inside rows of 16, then the row totals.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += dpp_u32<0x111>(x);
+    x += dpp_u32<0x112>(x);
+    x += dpp_u32<0x114>(x);
+    x += dpp_u32<0x118>(x);
+    const uint32_t r0 = readlane_u32(x, 15), r1 = readlane_u32(x, 31), r2 = readlane_u32(x, 47);
+    const int row = lane_id() >> 4;
+    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Exclusive prefix sum over the workgroup (NT lanes, thread order).  s_tmp holds NT/64 words.  Returns the thread's exclusive prefix; *total gets the workgroup sum.
+template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
     const int lane = lane_id(), w = wave_id();
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) s_tmp[w] = x;
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kThreads / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         const uint32_t c = s_tmp[i];
         before += (i < w) ? c : 0u;
         tot += c;
@@ -121,9 +171,38 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp,
     return before + x - v;
 }
 
+// N independent exclusive prefix sums over the workgroup at once (thread order), one barrier pair.
+// s_tmp holds (NT/64) * N words.  pre[i] = sum of v[i] over lower threads; tot[i] = total.
+template <int N, int NT = kThreads>
+__device__ __forceinline__ void block_excl_scan_n(const uint32_t* v, uint32_t* pre, uint32_t* tot, uint32_t* s_tmp) {
+    const int lane = lane_id(), w = wave_id();
+    uint32_t x[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = wave_incl_scan(v[i]);
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) s_tmp[w * N + i] = x[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        uint32_t before = 0, t = 0;
+#pragma unroll
+        for (int ww = 0; ww < NT / 64; ++ww) {
+            const uint32_t c = s_tmp[ww * N + i];
+            before += (ww < w) ? c : 0u;
+            t += c;
+        }
+        pre[i] = before + x[i] - v[i];
+        tot[i] = t;
+    }
+    __syncthreads();
+}
+
+template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* s_tmp) {
     uint32_t tot;
-    block_excl_scan(v, s_tmp, &tot);
+    block_excl_scan<NT>(v, s_tmp, &tot);
     return tot;
 }
 
@@ -132,7 +211,7 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* s_tmp) {
 // above(b) < target <= above(b) + count(b), above(b) = count of the bins above b; requires
 // 1 <= target <= total.  Result in s_res[0..2] = (b, above(b), count(b)), visible to all threads
 // on return.
-template <int BPT>
+template <int BPT, int NT = kThreads>
 __device__ __forceinline__ void find_crossing_regs(const uint32_t* c, int NB, uint32_t target, uint32_t* s_tmp,
                                                    uint32_t* s_res) {
     const int tid = threadIdx.x;
@@ -140,7 +219,7 @@ __device__ __forceinline__ void find_crossing_regs(const uint32_t* c, int NB, ui
 #pragma unroll
     for (int k = 0; k < BPT; ++k) sum += c[k];
     uint32_t tot;
-    uint32_t acc = block_excl_scan(sum, s_tmp, &tot);
+    uint32_t acc = block_excl_scan<NT>(sum, s_tmp, &tot);
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
         const int bin = NB - 1 - (tid * BPT + k);
@@ -154,18 +233,23 @@ __device__ __forceinline__ void find_crossing_regs(const uint32_t* c, int NB, ui
     __syncthreads();
 }
 
-// Same search over a histogram in LDS.
-template <int NB>
+// LDS histograms of kHistBins bins keep one pad word per 16 bins, so that the 16 consecutive bins
+// a thread reads in find_crossing start on different banks across the wave.
+constexpr int kHistPadded = kHistBins + kHistBins / 16;
+__device__ __forceinline__ int hpad(int bin) { return bin + (bin >> 4); }
+
+// Same search over a histogram in LDS (padded layout when NB == kHistBins).
+template <int NB, int NT = kThreads>
 __device__ __forceinline__ void find_crossing(const uint32_t* s_hist, uint32_t target, uint32_t* s_tmp,
                                               uint32_t* s_res) {
-    constexpr int BPT = NB >= kThreads ? NB / kThreads : 1;
+    constexpr int BPT = NB >= NT ? NB / NT : 1;  // with fewer bins than threads the top threads hold none
     uint32_t c[BPT];
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
         const int bin = NB - 1 - (int(threadIdx.x) * BPT + k);
-        c[k] = bin >= 0 ? s_hist[bin] : 0u;
+        c[k] = bin >= 0 ? s_hist[NB == kHistBins ? hpad(bin) : bin] : 0u;
     }
-    find_crossing_regs<BPT>(c, NB, target, s_tmp, s_res);
+    find_crossing_regs<BPT, NT>(c, NB, target, s_tmp, s_res);
 }
 
 // Loads a 4096-bin global histogram 16 bins per thread in the descending layout above.

@@ -13,7 +13,7 @@ namespace prism {
 #define PRISM_SCAN_WGS 1024            // target scan workgroups over all units
 #endif
 #ifndef PRISM_SCORE_SLICE
-#define PRISM_SCORE_SLICE 256
+#define PRISM_SCORE_SLICE 64
 #endif
 constexpr int kThreads = 256;          // every kernel runs 4 waves of 64 lanes
 constexpr int kChunk = 1024;           // tokens per chunk in the proposal kernels
@@ -21,7 +21,6 @@ constexpr int kScanWgs = PRISM_SCAN_WGS;
 constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in pool scoring
 constexpr int kAttendSlice = 64;       // selected rows per workgroup in sparse attention
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
-constexpr int kLdsKeys = 16384;        // pool keys a sparse-attention workgroup keeps in LDS
 constexpr int kLdsCand = 4096;         // threshold candidates a compaction workgroup keeps in LDS
 constexpr int kCtrStride = 16;         // counters sit 64 bytes apart (no shared cache line)
 constexpr int kHistBits = 12;          // first radix digit: top 12 bits of the order key
@@ -62,7 +61,7 @@ inline ProposeWs propose_ws(int64_t units, int64_t T_max) {
 }
 
 struct RefineWs {
-    size_t ghist, done_a, ctrl_bytes;
+    size_t done_a, ctrl_bytes;
     size_t skey, logits, part_ml, part_acc, total;
 };
 
@@ -77,7 +76,6 @@ inline RefineWs refine_ws(int64_t units, int64_t kp, int64_t kappa, int GP, int 
     RefineWs w{};
     const int64_t nsa = (kappa + kAttendSlice - 1) / kAttendSlice;
     size_t o = 0;
-    w.ghist = o;    o = align256(o + size_t(units) * kHistBins * 4);
     w.done_a = o;   o = align256(o + size_t(units) * kCtrStride * 4);
     w.ctrl_bytes = o;
     w.skey = o;     o = align256(o + size_t(units) * key_stride(kp) * 4);
@@ -143,7 +141,6 @@ struct RefineArgs {
     void* out;
     int32_t* idx;
     float* lse;
-    uint32_t* ghist;        // [U][kHistBins] top 12 bits of the pool keys
     uint32_t* done_a;       // [U][kCtrStride]
     uint32_t* skey;         // [U][kstride] order key of S per pool slot (0 = empty slot)
     float* logits;          // [U][kp][LS]
