@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode attn steps/s + achieved HBM GB/s at 128K ctx, proposal+3 refined layers"
 PEAK_HBM_GBPS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "k_scan_128k_pmc.json")
+CALIB_BYTES = 1 << 30  # the copy read and written by the counter pass's calibration kernel
 
 
 def parse():
@@ -35,6 +36,14 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="time stream launches instead of HIP graphs")
+    p.add_argument("--pmc-pass", action="store_true",
+                   help="counter pass for rocprofv3 --pmc: --steps stream-launched steps, then one plain "
+                        "copy of CALIB_BYTES as the counters' scale; no timing, no JSON line")
+    p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="read two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of --pmc-pass and write "
+                        "the scan kernel's HBM traffic per launch to " + os.path.relpath(PMC_FILE, ROOT))
+    p.add_argument("--pmc-command", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("", ""),
+                   help="the two rocprofv3 command lines, recorded beside the ingested figures")
     return p.parse_args()
 
 
@@ -46,8 +55,63 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def _counter_rows(d):
+    """Rows of every *counter_collection.csv under a rocprofv3 output directory."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(root, f)) as fh:
+                    rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (kernel name, counter value summed over its dimensions)}."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        k = int(r["Dispatch_Id"])
+        name, v = out.get(k, (r["Kernel_Name"], 0.0))
+        out[k] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def ingest_pmc(args):
+    """HBM traffic of the scan kernel per launch, from FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    scaled by what the same counters read for the calibration copy of CALIB_BYTES."""
+    res = {"workload": args.config, "source_hash": kernel_source_hash(), "calib_bytes": CALIB_BYTES,
+           "commands": {"FETCH_SIZE": args.pmc_command[0], "WRITE_SIZE": args.pmc_command[1]}}
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", args.ingest_pmc[0]), ("WRITE_SIZE", args.ingest_pmc[1])):
+        disp = _per_dispatch(_counter_rows(d), counter)
+        scan = [v for n, v in disp.values() if "k_scan" in n]
+        calib = [v for n, v in disp.values() if "neg_kernel" in n]
+        if not scan or len(calib) != 1:
+            raise SystemExit(f"{counter}: {len(scan)} scan dispatches, {len(calib)} calibration dispatches")
+        kib = sum(scan) / len(scan)
+        factor = CALIB_BYTES / (calib[0] * 1024.0)
+        bytes_ = kib * 1024.0 * factor
+        res[counter] = {"kib_per_launch": round(kib, 1), "launches": len(scan),
+                        "calib_kib": round(calib[0], 1), "scale": round(factor, 5),
+                        "bytes_per_launch": int(bytes_)}
+        total += bytes_
+    res["traffic_bytes_per_launch"] = int(total)
+    with open(PMC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res))
+    return 0
+
+
 def main():
     args = parse()
+    if args.ingest_pmc:
+        return ingest_pmc(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the hot path needs no exchange between GPUs "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
@@ -102,6 +166,18 @@ def main():
         for b in range(cfg.B):
             for g in range(cfg.Hkv):
                 assert set(ii[b, g][ii[b, g] >= 0].tolist()) <= set(pool[b, g].tolist())
+
+    if args.pmc_pass:
+        for i in range(args.steps):
+            steps[i % R]()
+        torch.cuda.synchronize()
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # the calibration kernel: reads and writes CALIB_BYTES once
+        torch.cuda.synchronize()
+        print(f"pmc pass: {args.steps} steps, calibration copy of {CALIB_BYTES} bytes", flush=True)
+        return 0
 
     for i in range(args.warmup):
         steps[i % R]()

@@ -84,13 +84,12 @@ template <typename T, int D>
 static hipError_t dense_g(const DenseArgs& a, hipStream_t st) {
     const int units = a.d.B * a.d.Hkv;
     const dim3 grid(int((a.d.T_max + kDenseChunk - 1) / kDenseChunk), units);
-    ProfScope prof("k_dense", st);
     switch (padded_g(a.d.G)) {
-        case 1: hipLaunchKernelGGL((k_dense<T, D, 1>), grid, dim3(kThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((k_dense<T, D, 2>), grid, dim3(kThreads), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((k_dense<T, D, 4>), grid, dim3(kThreads), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((k_dense<T, D, 8>), grid, dim3(kThreads), 0, st, a); break;
-        case 16: hipLaunchKernelGGL((k_dense<T, D, 16>), grid, dim3(kThreads), 0, st, a); break;
+        case 1: launch_k("k_dense", (k_dense<T, D, 1>), grid, dim3(kThreads), st, a); break;
+        case 2: launch_k("k_dense", (k_dense<T, D, 2>), grid, dim3(kThreads), st, a); break;
+        case 4: launch_k("k_dense", (k_dense<T, D, 4>), grid, dim3(kThreads), st, a); break;
+        case 8: launch_k("k_dense", (k_dense<T, D, 8>), grid, dim3(kThreads), st, a); break;
+        case 16: launch_k("k_dense", (k_dense<T, D, 16>), grid, dim3(kThreads), st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -414,17 +414,16 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 template <int D>
 static hipError_t launch_scan(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
     const int G = a.d.G;
-    ProfScope prof("k_scan", st);
     if (!agg_max) {
-        if (G == 1) hipLaunchKernelGGL((k_scan<D, 1, false>), grid, dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_scan<D, 2, false>), grid, dim3(kThreads), 0, st, a);
+        if (G == 1) launch_k("k_scan", (k_scan<D, 1, false>), grid, dim3(kThreads), st, a);
+        else launch_k("k_scan", (k_scan<D, 2, false>), grid, dim3(kThreads), st, a);
     } else {
         switch (padded_g(G)) {
-            case 1: hipLaunchKernelGGL((k_scan<D, 1, true>), grid, dim3(kThreads), 0, st, a); break;
-            case 2: hipLaunchKernelGGL((k_scan<D, 2, true>), grid, dim3(kThreads), 0, st, a); break;
-            case 4: hipLaunchKernelGGL((k_scan<D, 4, true>), grid, dim3(kThreads), 0, st, a); break;
-            case 8: hipLaunchKernelGGL((k_scan<D, 8, true>), grid, dim3(kThreads), 0, st, a); break;
-            case 16: hipLaunchKernelGGL((k_scan<D, 16, true>), grid, dim3(kThreads), 0, st, a); break;
+            case 1: launch_k("k_scan", (k_scan<D, 1, true>), grid, dim3(kThreads), st, a); break;
+            case 2: launch_k("k_scan", (k_scan<D, 2, true>), grid, dim3(kThreads), st, a); break;
+            case 4: launch_k("k_scan", (k_scan<D, 4, true>), grid, dim3(kThreads), st, a); break;
+            case 8: launch_k("k_scan", (k_scan<D, 8, true>), grid, dim3(kThreads), st, a); break;
+            case 16: launch_k("k_scan", (k_scan<D, 16, true>), grid, dim3(kThreads), st, a); break;
             default: return hipErrorInvalidValue;
         }
     }
@@ -446,13 +445,11 @@ hipError_t launch_propose(const ProposeArgs& a, int agg_max, hipStream_t st) {
     }
     if (e != hipSuccess) return e;
     {
-        ProfScope prof("k_cand", st);
-        hipLaunchKernelGGL(k_cand, grid, dim3(kThreads), 0, st, a);
+        launch_k("k_cand", k_cand, grid, dim3(kThreads), st, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
-        ProfScope prof("k_compact", st);
-        hipLaunchKernelGGL(k_compact, grid, dim3(kThreads), 0, st, a);
+        launch_k("k_compact", k_compact, grid, dim3(kThreads), st, a);
     }
     return hipGetLastError();
 }

@@ -64,11 +64,10 @@ static hipError_t quantize_dispatch(const void* K, const Dims& d, int8_t* Kq, fl
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
     const T* k = static_cast<const T*>(K);
-    ProfScope prof("k_quantize_keys", st);
     switch (d.D) {
-        case 64: hipLaunchKernelGGL((k_quantize_keys<T, 64>), dim3(blocks), dim3(kThreads), 0, st, k, Kq, scales, d); break;
-        case 128: hipLaunchKernelGGL((k_quantize_keys<T, 128>), dim3(blocks), dim3(kThreads), 0, st, k, Kq, scales, d); break;
-        case 256: hipLaunchKernelGGL((k_quantize_keys<T, 256>), dim3(blocks), dim3(kThreads), 0, st, k, Kq, scales, d); break;
+        case 64: launch_k("k_quantize_keys", (k_quantize_keys<T, 64>), dim3(blocks), dim3(kThreads), st, k, Kq, scales, d); break;
+        case 128: launch_k("k_quantize_keys", (k_quantize_keys<T, 128>), dim3(blocks), dim3(kThreads), st, k, Kq, scales, d); break;
+        case 256: launch_k("k_quantize_keys", (k_quantize_keys<T, 256>), dim3(blocks), dim3(kThreads), st, k, Kq, scales, d); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -174,15 +174,13 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     const dim3 gs((a.kp + kScoreSlice - 1) / kScoreSlice, units);
     const dim3 ga((a.kappa + kAttendSlice - 1) / kAttendSlice, units);
     {
-        ProfScope prof("k_rscore", st);
-        if (agg_max) hipLaunchKernelGGL((k_rscore<T, D, GP, true>), gs, dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_rscore<T, D, GP, false>), gs, dim3(kThreads), 0, st, a);
+        if (agg_max) launch_k("k_rscore", (k_rscore<T, D, GP, true>), gs, dim3(kThreads), st, a);
+        else launch_k("k_rscore", (k_rscore<T, D, GP, false>), gs, dim3(kThreads), st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
-        ProfScope prof("k_attend", st);
-        hipLaunchKernelGGL((k_attend<T, D, GP>), ga, dim3(kAttendThreads), 0, st, a);
+        launch_k("k_attend", (k_attend<T, D, GP>), ga, dim3(kAttendThreads), st, a);
     }
     return hipGetLastError();
 }

@@ -36,22 +36,19 @@ hipEvent_t take_event() {
 
 bool prof_enabled() { return g_on.load(std::memory_order_relaxed); }
 
-void prof_mark(const char* name, hipStream_t st, bool begin) {
+bool prof_pair(const char* name, hipEvent_t* begin, hipEvent_t* end) {
     std::lock_guard<std::mutex> lk(g_mu);
-    hipEvent_t ev = take_event();
-    if (!ev) return;
-    hipEventRecord(ev, st);
-    if (begin) {
-        g_recs.push_back({name, ev, nullptr});
-        return;
+    hipEvent_t b = take_event();
+    if (!b) return false;
+    hipEvent_t e = take_event();
+    if (!e) {
+        g_free.push_back(b);
+        return false;
     }
-    for (size_t i = g_recs.size(); i-- > 0;) {
-        if (g_recs[i].e == nullptr && strcmp(g_recs[i].name, name) == 0) {
-            g_recs[i].e = ev;
-            return;
-        }
-    }
-    g_free.push_back(ev);
+    g_recs.push_back({name, b, e});
+    *begin = b;
+    *end = e;
+    return true;
 }
 
 }  // namespace prism
