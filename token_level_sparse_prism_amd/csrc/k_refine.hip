@@ -4,13 +4,13 @@
 //
 // Two launches per call:
 //   k_rscore  grid (pool slices of 64 slots) x units.  Gathers the pool's K rows, computes the G
-//             heads' logits (fp32) and the group score S, and stores the logits and an order key
-//             of S per slot (0 for an empty slot).
-//   k_attend  grid (64 selected ranks) x units.  Every workgroup reads the unit's keys into
-//             registers and derives the exact top-kappa itself (radix digits 12/12/8 in LDS, ties
-//             to the lower slot), ranks the selected slots in slot order, writes idx for its 64
-//             ranks, gathers their V rows and forms a softmax(.)V partial from the stored logits.
-//             The unit's last workgroup merges the partials (log-sum-exp) into out and lse.
+//             heads' logits (fp32) and the group score S, and stores the logits and {order key
+//             of S, token} per slot (key 0 for an empty slot).
+//   k_attend  grid (256 selected ranks) x units, 1024 threads.  Every workgroup derives the
+//             exact top-kappa of its unit from the keys, ranks the selected
+//             slots in slot order (ties to the lower slot), writes idx for its ranks, gathers
+//             their V rows and forms a softmax(.)V partial from the stored logits.  The unit's
+//             last workgroup merges the partials (log-sum-exp) into out and lse.
 #include "prism_attend.hpp"
 #include "prism_prof.hpp"
 #include "prism_select.hpp"
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
     q.load(static_cast<const T*>(a.q) + (int64_t(b) * d.Hq + int64_t(g) * G) * D, G, sub);
     const T* Ku = static_cast<const T*>(a.K) + int64_t(unit) * d.T_max * D;
     const int32_t* pool = a.pool + int64_t(unit) * kp;
-    uint32_t* skey = a.skey + int64_t(unit) * a.kstride;
+    uint2* skey = a.skey + int64_t(unit) * a.kstride;
     float* logits = a.logits + int64_t(unit) * kp * LS;
     const int64_t j0 = int64_t(slice) * kScoreSlice;
     const int rl = wave * RPW + lane / LPR;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
             }
             if (sub == 0 && j < kp && (r0 + u) * RPR + rl < kScoreSlice) {
                 const uint32_t key = valid ? order_key(S) : 0u;
-                skey[j] = key;
+                st_stream(&skey[j], make_uint2(key, valid ? uint32_t(t[u]) : 0xFFFFFFFFu));
 #pragma unroll
                 for (int h4 = 0; h4 < LS; h4 += 4) {
                     float4 v;
@@ -81,30 +81,29 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
                     v.y = h4 + 1 < GP ? l[h4 + 1] : 0.0f;
                     v.z = h4 + 2 < GP ? l[h4 + 2] : 0.0f;
                     v.w = h4 + 3 < GP ? l[h4 + 3] : 0.0f;
-                    *reinterpret_cast<float4*>(&logits[j * LS + h4]) = v;
+                    st_stream(reinterpret_cast<float4*>(&logits[j * LS + h4]), v);
                 }
             }
         }
     }
 }
 
-constexpr int kAttendThreads = 1024;  // 16 waves: latency of the selection is hidden 4 waves per SIMD
-
 template <typename T, int D, int GP>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     constexpr int NT = kAttendThreads;
+    constexpr int NW = NT / 64;
+    constexpr int NR = kAttendRanks;
     constexpr int LS = GP < 4 ? 4 : GP;
-    __shared__ uint32_t s_hist[kHistPadded];  // selection histograms, then the merge's table
-    __shared__ uint32_t s_tmp[NT / 64 * 4];
-    __shared__ uint32_t s_res[4];
-    __shared__ uint32_t s_cand[kSelCandTotal];
-    __shared__ uint32_t s_ccount[NT / 64];
-    __shared__ int32_t s_slot[kAttendSlice];
-    __shared__ int32_t s_t[kAttendSlice];
-    __shared__ float s_y[kAttendSlice][GP];
-    __shared__ float s_stat[2 * GP];
-    __shared__ float s_red[(NT / 64) * GP];
-    __shared__ float s_acc[GP * D];
+    static_assert(kHistPadded <= kRowsAccFloats && kSelHistWords <= kRowsAccFloats, "LDS buffer too small");
+    __shared__ __align__(16) uint32_t s_big[kRowsAccFloats];  // selection histograms, then the waves' V partials
+    __shared__ __align__(16) uint32_t s_cand[kSelCandTotal];
+    __shared__ uint32_t s_ccount[NW];
+    __shared__ uint32_t s_tmp[NW * 2];
+    __shared__ uint32_t s_res[16];
+    __shared__ int32_t s_slot[NR];
+    __shared__ int32_t s_tok[NR];
+    __shared__ __align__(16) float s_p[NR * GP];
+    __shared__ float s_red[2 * NW * GP];
     __shared__ uint32_t s_flag;
 
     const Dims& d = a.d;
@@ -114,57 +113,30 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
     const int64_t kp = a.kp;
-    const int64_t Tb = seq_len_of(d, b);
-    const int r0 = slice * kAttendSlice;
+    const int r0 = slice * NR;
 
-    const SelResult sr = select_slice<NT>(a.skey + int64_t(unit) * a.kstride, kp, uint32_t(a.kappa), r0, kAttendSlice,
-                                      s_hist, s_tmp, s_res, s_cand, s_ccount, s_slot);
+    const SelResult sr = select_ranks<NT>(a.skey + int64_t(unit) * a.kstride, kp, uint32_t(a.kappa), r0, NR, s_big,
+                                          s_tmp, s_res, s_cand, s_ccount, s_slot, s_tok);
     const int n = sr.n;
 
-    // ---- idx and the slice's rows ----
-    const int32_t* pool = a.pool + int64_t(unit) * kp;
-    if (tid < kAttendSlice && r0 + tid < a.kappa) {
-        int32_t t = -1;
-        if (tid < n) {
-            int32_t j = s_slot[tid];
-            j = (j >= 0 && j < kp) ? j : 0;  // every rank of the slice was filled; keep reads in bounds
-            t = pool[j];
-            t = (t >= 0 && t < Tb) ? t : 0;
-            s_t[tid] = t;
-            const float4* lg = reinterpret_cast<const float4*>(a.logits + (int64_t(unit) * kp + j) * LS);
-#pragma unroll
-            for (int h4 = 0; h4 < LS; h4 += 4) {
-                const float4 v = lg[h4 / 4];
-                const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (h4 + e < GP) s_y[tid][h4 + e] = h4 + e < G ? vv[e] * a.y_scale : 0.0f;
-            }
-        }
-        a.idx[int64_t(unit) * a.kappa + r0 + tid] = t;
-    }
-    __syncthreads();
-
+    // ---- idx, then the slice's softmax(.)V partial ----
+    if (tid < NR && r0 + tid < a.kappa) a.idx[int64_t(unit) * a.kappa + r0 + tid] = tid < n ? s_tok[tid] : -1;
     const int nsa = int(gridDim.x);
     float* part_ml = a.part_ml + int64_t(unit) * nsa * GP * 2;
     float* part_acc = a.part_acc + int64_t(unit) * nsa * GP * D;
     if (n > 0) {
         const T* Vu = static_cast<const T*>(a.V) + int64_t(unit) * d.T_max * D;
-        softmax_v_partial<T, D, GP, kAttendSlice, NT>(Vu, s_t, s_y, n, G, s_stat, s_red, s_acc,
-                                                   part_acc + int64_t(slice) * GP * D,
-                                                   part_ml + int64_t(slice) * GP * 2);
+        softmax_v_rows<T, D, GP, NR, NT>(Vu, a.logits + int64_t(unit) * kp * LS, LS, a.y_scale, s_slot, s_tok, n, G,
+                                         s_p, s_red, reinterpret_cast<float*>(s_big), part_acc + int64_t(slice) * GP * D,
+                                         part_ml + int64_t(slice) * GP * 2);
     }
 
     if (!arrive_last(&a.done_a[int64_t(unit) * kCtrStride], gridDim.x, &s_flag)) return;
 
-    const int np = int((sr.kappa_eff + kAttendSlice - 1) / kAttendSlice);
+    const int np = int((sr.kappa_eff + NR - 1) / NR);
     const int64_t hq0 = int64_t(b) * d.Hq + int64_t(g) * G;
-    T* out = static_cast<T*>(a.out) + hq0 * D;
-    float* lse = a.lse ? a.lse + hq0 : nullptr;
-    if (merge_lds_floats(np, GP) <= kHistBins)
-        merge_partials_lds<T, D, GP, NT>(part_ml, part_acc, np, G, out, lse, reinterpret_cast<float*>(s_hist));
-    else
-        merge_partials<T, D, GP, NT>(part_ml, part_acc, np, G, out, lse);
+    merge_partials<T, D, GP, NT>(part_ml, part_acc, np, G, static_cast<T*>(a.out) + hq0 * D,
+                                 a.lse ? a.lse + hq0 : nullptr);
     if (tid == 0) a.done_a[int64_t(unit) * kCtrStride] = 0u;
 }
 
@@ -172,7 +144,7 @@ template <typename T, int D, int GP>
 static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t st) {
     const int units = a.d.B * a.d.Hkv;
     const dim3 gs((a.kp + kScoreSlice - 1) / kScoreSlice, units);
-    const dim3 ga((a.kappa + kAttendSlice - 1) / kAttendSlice, units);
+    const dim3 ga((a.kappa + kAttendRanks - 1) / kAttendRanks, units);
     {
         if (agg_max) launch_k("k_rscore", (k_rscore<T, D, GP, true>), gs, dim3(kThreads), st, a);
         else launch_k("k_rscore", (k_rscore<T, D, GP, false>), gs, dim3(kThreads), st, a);

@@ -155,7 +155,7 @@ prism_status prism_refine_attend(const void* q, const void* K, const void* V, pr
     a.idx = idx;
     a.lse = lse;
     a.done_a = reinterpret_cast<uint32_t*>(carve(ws, L.done_a));
-    a.skey = reinterpret_cast<uint32_t*>(carve(ws, L.skey));
+    a.skey = reinterpret_cast<uint2*>(carve(ws, L.skey));
     a.logits = reinterpret_cast<float*>(carve(ws, L.logits));
     a.part_ml = reinterpret_cast<float*>(carve(ws, L.part_ml));
     a.part_acc = reinterpret_cast<float*>(carve(ws, L.part_acc));

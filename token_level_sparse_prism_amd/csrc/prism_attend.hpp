@@ -164,6 +164,218 @@ __device__ __forceinline__ void softmax_v_partial(const T* __restrict__ Vu, cons
     }
 }
 
+// ---- sparse partial with one V row per wave instruction ----------------------------------
+// Lane l of a wave holds dims [l*NE, l*NE + NE) of a row, NE = D/64, so a row is one coalesced
+// 64-lane load of D*e bytes and no lane ever holds a partial of another lane's dims.
+template <typename T, int NE> struct LaneRow;
+template <> struct LaneRow<uint16_t, 1> {
+    using R = uint32_t;
+    static __device__ __forceinline__ R load(const uint16_t* p) { return uint32_t(*p); }
+    static __device__ __forceinline__ void unpack(R r, float* x) { x[0] = bf16_bits_to_f32(r); }
+};
+template <> struct LaneRow<uint16_t, 2> {
+    using R = uint32_t;
+    static __device__ __forceinline__ R load(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    static __device__ __forceinline__ void unpack(R r, float* x) {
+        x[0] = bf16_bits_to_f32(r & 0xFFFFu);
+        x[1] = bf16_bits_to_f32(r >> 16);
+    }
+};
+template <> struct LaneRow<uint16_t, 4> {
+    using R = uint2;
+    static __device__ __forceinline__ R load(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ void unpack(R r, float* x) {
+        x[0] = bf16_bits_to_f32(r.x & 0xFFFFu);
+        x[1] = bf16_bits_to_f32(r.x >> 16);
+        x[2] = bf16_bits_to_f32(r.y & 0xFFFFu);
+        x[3] = bf16_bits_to_f32(r.y >> 16);
+    }
+};
+template <> struct LaneRow<float, 1> {
+    using R = float;
+    static __device__ __forceinline__ R load(const float* p) { return *p; }
+    static __device__ __forceinline__ void unpack(R r, float* x) { x[0] = r; }
+};
+template <> struct LaneRow<float, 2> {
+    using R = float2;
+    static __device__ __forceinline__ R load(const float* p) { return *reinterpret_cast<const float2*>(p); }
+    static __device__ __forceinline__ void unpack(R r, float* x) {
+        x[0] = r.x;
+        x[1] = r.y;
+    }
+};
+template <> struct LaneRow<float, 4> {
+    using R = float4;
+    static __device__ __forceinline__ R load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    static __device__ __forceinline__ void unpack(R r, float* x) {
+        x[0] = r.x;
+        x[1] = r.y;
+        x[2] = r.z;
+        x[3] = r.w;
+    }
+};
+
+constexpr int kRowsAccFloats = 8192;  // LDS floats for the waves' V partials (one round of heads)
+
+// softmax(y) V partial over the n (1 <= n <= NR) selected rows of one workgroup of NT threads.
+//   s_slot[r], s_tok[r]  pool slot and token id of row r
+//   logits               the unit's [kp][LS] fp32 logits per pool slot; y = logit * y_scale is
+//                        the base-2 exponent-domain logit (heads >= G unused)
+// Wave w owns rows [w*RPW, w*RPW + RPW): lane i < RPW loads row i's logits, and the wave issues
+// its rows' V loads (branch-free, rows >= n read row 0 and get weight 0) before the statistics,
+// so both arrive in one round trip.  One barrier exchanges the per-wave maxima; a row's weights
+// go through the wave's own rows of s_p (NR*GP floats, 16-byte aligned).  The waves' partials
+// are summed in LDS in wave order, HB heads per round.  Writes g_ml[h] = (max_r y,
+// sum_r 2^(y - max)) and g_acc[h][d] = sum_r 2^(y - max) V[r][d] for h < G at device scope.
+// LDS: s_red 2*(NT/64)*GP floats, s_wacc kRowsAccFloats floats.
+template <typename T, int D, int GP, int NR, int NT>
+__device__ __forceinline__ void softmax_v_rows(const T* __restrict__ Vu, const float* __restrict__ logits, int LS,
+                                               float y_scale, const int32_t* s_slot, const int32_t* s_tok, int n,
+                                               int G, float* s_p, float* s_red, float* s_wacc,
+                                               float* __restrict__ g_acc, float* __restrict__ g_ml) {
+    constexpr int NW = NT / 64;
+    constexpr int NE = D / 64;
+    using LR = LaneRow<T, NE>;
+    using R = typename LR::R;
+    constexpr int WORDS = int(sizeof(R)) / 4 > 0 ? int(sizeof(R)) / 4 : 1;
+    constexpr int RPW = NR / NW;  // rows per wave
+    constexpr int UB = RPW < 32 / WORDS ? RPW : 32 / WORDS;
+    constexpr int HB = kRowsAccFloats / (NW * D) < GP ? kRowsAccFloats / (NW * D) : GP;  // heads per LDS round
+    static_assert(NR % NW == 0 && RPW <= 64 && RPW % UB == 0, "rows must split evenly over the waves' lanes");
+    static_assert(HB >= 1 && GP % HB == 0, "head rounds");
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int row0 = wave * RPW;
+    float* s_max = s_red;
+    float* s_sum = s_red + NW * GP;
+
+    // this lane's row: its logits (the lane's load is issued first)
+    const bool my_valid = lane < RPW && row0 + lane < n;
+    float4 lraw[GP < 4 ? 1 : GP / 4];
+    {
+        const int64_t j = s_slot[my_valid ? row0 + lane : 0];
+#pragma unroll
+        for (int h4 = 0; h4 < (GP < 4 ? 1 : GP / 4); ++h4)
+            lraw[h4] = reinterpret_cast<const float4*>(logits + j * LS)[h4];
+    }
+    // the wave's V rows, first batch
+    R raw[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+        const int r = row0 + u;
+        raw[u] = LR::load(Vu + int64_t(s_tok[r < n ? r : 0]) * D + lane * NE);
+    }
+
+    // statistics
+    float y[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        const float4 v = lraw[h / 4];
+        const float c = (h % 4 == 0) ? v.x : (h % 4 == 1) ? v.y : (h % 4 == 2) ? v.z : v.w;
+        y[h] = (my_valid && h < G) ? c * y_scale : -INFINITY;
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        if (h >= G) break;
+        const float m = wave_max(y[h]);
+        if (lane == 0) s_max[wave * GP + h] = m;
+    }
+    __syncthreads();
+    // every wave's maximum (waves without rows hold -inf), per head: lane l reads wave l % 16 of
+    // head l / 16 of a group of four heads and a row-wide DPP max reduces them
+    static_assert(NW == 16, "the wave maxima fill one DPP row per head");
+    float p[GP];
+#pragma unroll
+    for (int hb = 0; hb < GP; hb += 4) {
+        const int hq = hb + (lane >> 4);
+        const float m = group_max<16>(hq < G ? s_max[(lane & 15) * GP + hq] : -INFINITY);
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) {
+            const int h = hb + h4;
+            if (h < GP) {
+                const float M = readlane_f32(m, 16 * h4);
+                p[h] = (my_valid && h < G) ? exp2_le0(y[h] - M) : 0.0f;
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        if (h >= G) break;
+        const float l = wave_sum(p[h]);
+        if (lane == 0) s_sum[wave * GP + h] = l;
+    }
+    if (lane < RPW) {  // the wave's rows' weights; read back below by the same wave only
+#pragma unroll
+        for (int h = 0; h < GP; ++h) s_p[(row0 + lane) * GP + h] = p[h];
+    }
+
+    // weighted V accumulation (rows beyond n carry weight 0)
+    float acc[GP][NE];
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[h][e] = 0.0f;
+#pragma unroll
+    for (int i0 = 0; i0 < RPW; i0 += UB) {
+        if (i0 > 0) {
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const int r = row0 + i0 + u;
+                raw[u] = LR::load(Vu + int64_t(s_tok[r < n ? r : 0]) * D + lane * NE);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            float x[NE];
+            LR::unpack(raw[u], x);
+            const float* pw = s_p + (row0 + i0 + u) * GP;
+#pragma unroll
+            for (int h = 0; h < GP; ++h) {
+                if (h < G) {
+                    const float w = pw[h];
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) acc[h][e] = fmaf(w, x[e], acc[h][e]);
+                }
+            }
+        }
+    }
+
+    // sum of the waves' partials in wave order, HB heads per round; partials are read by another
+    // workgroup of the same kernel, so they are written through to device scope
+#pragma unroll
+    for (int hb = 0; hb < GP; hb += HB) {
+        if (hb >= G) break;
+        if (hb > 0) __syncthreads();  // the previous round's sums have read s_wacc
+#pragma unroll
+        for (int h = 0; h < HB; ++h) {
+            if (hb + h < G) {
+#pragma unroll
+                for (int e = 0; e < NE; ++e) s_wacc[(wave * HB + h) * D + lane * NE + e] = acc[hb + h][e];
+            }
+        }
+        __syncthreads();
+        const int nb = (G - hb < HB ? G - hb : HB) * D;
+        for (int i = tid; i < nb; i += NT) {
+            const int h = i / D, dd = i % D;
+            float sacc = s_wacc[h * D + dd];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) sacc += s_wacc[(w * HB + h) * D + dd];
+            st_dev(&g_acc[(hb + h) * D + dd], sacc);
+        }
+    }
+    if (wave == 0) {
+#pragma unroll
+        for (int hb = 0; hb < GP; hb += 4) {
+            const int hq = hb + (lane >> 4);
+            const float m = group_max<16>(hq < G ? s_max[(lane & 15) * GP + hq] : -INFINITY);
+            const float l = group_sum<16>(hq < G ? s_sum[(lane & 15) * GP + hq] : 0.0f);
+            if ((lane & 15) == 0 && hq < G) {
+                st_dev(&g_ml[2 * hq], m);
+                st_dev(&g_ml[2 * hq + 1], l);
+            }
+        }
+    }
+}
+
 // Log-sum-exp merge of `np` partials (partial s at g_ml + s*GP*2, g_acc + s*GP*D), read at
 // device scope, eight partials per batch of independent loads.  Writes out[h][d] (dtype T) and
 // lse[h] (natural log) for h < G; np == 0 gives out = 0, lse = -inf.
@@ -189,8 +401,8 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, c
             for (int u = 0; u < BATCH; ++u) {
                 if (s0 + u < np) {
                     const float Mn = fmaxf(M, m[u]);
-                    const float c_old = exp2f(M - Mn);
-                    const float c_new = exp2f(m[u] - Mn);
+                    const float c_old = exp2_le0(M - Mn);
+                    const float c_new = exp2_le0(m[u] - Mn);
                     L = L * c_old + l[u] * c_new;
                     acc = acc * c_old + v[u] * c_new;
                     M = Mn;
@@ -200,88 +412,6 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, c
         const bool empty = np == 0;
         store_elem<T>(&out[int64_t(h) * D + dd], empty ? 0.0f : acc / L);
         if (dd == 0 && lse) lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
-    }
-}
-
-// Log-sum-exp merge of `np` partials with the per-partial statistics staged in LDS.  The first
-// batch of partial sums is requested before the statistics, so both arrive in one round trip.
-// s_tab must hold 3*np*GP + 2*GP floats (fits_lds_merge).  Deterministic: partials are summed in
-// index order.
-__host__ __device__ constexpr int merge_lds_floats(int np, int GP) { return 3 * np * GP + 2 * GP; }
-
-template <typename T, int D, int GP, int NT = kThreads>
-__device__ __forceinline__ void merge_partials_lds(const float* __restrict__ g_ml, const float* __restrict__ g_acc, int np, int G,
-                                   T* __restrict__ out, float* __restrict__ lse, float* s_tab) {
-    constexpr float kLn2 = 0.6931471805599453f;
-    constexpr int OPT = (GP * D + NT - 1) / NT;  // outputs per thread
-    constexpr int BATCH = (64 / OPT) < 4 ? 4 : ((64 / OPT) > 32 ? 32 : 64 / OPT);
-    const int tid = threadIdx.x;
-    float* sm = s_tab;
-    float* sl = sm + np * GP;
-    float* sw = sl + np * GP;
-    float* sM = sw + np * GP;
-    float* sL = sM + GP;
-
-    float accv[OPT][BATCH];
-    auto load_batch = [&](int s0) {
-#pragma unroll
-        for (int q = 0; q < OPT; ++q) {
-            const int o = tid + q * NT;
-            const int h = o / D, dd = o % D;
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                const int s = s0 + u;
-                accv[q][u] = (o < G * D && s < np) ? ld_dev(&g_acc[(int64_t(s) * GP + h) * D + dd]) : 0.0f;
-            }
-        }
-    };
-    load_batch(0);
-    for (int i = tid; i < np * GP; i += NT) {
-        const int h = i % GP;
-        sm[i] = h < G ? ld_dev(&g_ml[2 * i]) : -INFINITY;
-        sl[i] = h < G ? ld_dev(&g_ml[2 * i + 1]) : 0.0f;
-    }
-    __syncthreads();
-    if (tid < GP) {
-        float M = -INFINITY;
-        for (int s = 0; s < np; ++s) M = fmaxf(M, sm[s * GP + tid]);
-        sM[tid] = M;
-    }
-    __syncthreads();
-    for (int i = tid; i < np * GP; i += NT) {
-        const int h = i % GP;
-        sw[i] = h < G ? exp2f(sm[i] - sM[h]) : 0.0f;
-    }
-    __syncthreads();
-    if (tid < GP) {
-        float L = 0.0f;
-        for (int s = 0; s < np; ++s) L = fmaf(sw[s * GP + tid], sl[s * GP + tid], L);
-        sL[tid] = L;
-    }
-    __syncthreads();
-    float res[OPT];
-#pragma unroll
-    for (int q = 0; q < OPT; ++q) res[q] = 0.0f;
-    for (int s0 = 0; s0 < np; s0 += BATCH) {
-        if (s0 > 0) load_batch(s0);
-#pragma unroll
-        for (int q = 0; q < OPT; ++q) {
-            const int o = tid + q * NT;
-            const int h = (o / D) < GP ? o / D : 0;
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u)
-                if (s0 + u < np) res[q] = fmaf(sw[(s0 + u) * GP + h], accv[q][u], res[q]);
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < OPT; ++q) {
-        const int o = tid + q * NT;
-        if (o < G * D) {
-            const int h = o / D, dd = o % D;
-            const bool empty = np == 0;
-            store_elem<T>(&out[o], empty ? 0.0f : res[q] / sL[h]);
-            if (dd == 0 && lse) lse[h] = empty ? -INFINITY : (sM[h] + log2f(sL[h])) * kLn2;
-        }
     }
 }
 

@@ -128,6 +128,20 @@ __device__ __forceinline__ int group_sum_i(int v) {
     return v;
 }
 
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(N >= 1 && N <= 16, "groups inside a DPP row");
+    if constexpr (N >= 2) v = fmaxf(v, dpp_f32<0xB1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp_f32<0x4E>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp_f32<0x141>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp_f32<0x140>(v));
+    return v;
+}
+
+// 2^x by the hardware instruction (no range reduction): for x <= 0, where the result is in
+// [0, 1] and tiny results may flush to zero.
+__device__ __forceinline__ float exp2_le0(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Whole-wave reductions, result uniform across the wave.
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_f32<0xB1>(v));
@@ -152,6 +166,23 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
+// Prefix over the NW (<= 16) per-wave totals in s_tot[0..NW): lane i of every wave reads total i
+// and a row-0 DPP scan forms the prefix; the wave's exclusive prefix and the grand total are
+// taken with readlane.
+template <int NW>
+__device__ __forceinline__ void wave_totals_prefix(const uint32_t* s_tot, uint32_t* before, uint32_t* total) {
+    static_assert(NW >= 1 && NW <= 16, "one DPP row holds the wave totals");
+    const int lane = lane_id();
+    uint32_t x = lane < NW ? s_tot[lane] : 0u;
+    if constexpr (NW > 1) x += dpp_u32<0x111>(x);
+    if constexpr (NW > 2) x += dpp_u32<0x112>(x);
+    if constexpr (NW > 4) x += dpp_u32<0x114>(x);
+    if constexpr (NW > 8) x += dpp_u32<0x118>(x);
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    *before = w > 0 ? readlane_u32(x, w - 1) : 0u;
+    *total = readlane_u32(x, NW - 1);
+}
+
 // Exclusive prefix sum over the workgroup (NT lanes, thread order).  s_tmp holds NT/64 words.  Returns the thread's exclusive prefix; *total gets the workgroup sum.
 template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
@@ -159,13 +190,8 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp,
     const uint32_t x = wave_incl_scan(v);
     if (lane == 63) s_tmp[w] = x;
     __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NT / 64; ++i) {
-        const uint32_t c = s_tmp[i];
-        before += (i < w) ? c : 0u;
-        tot += c;
-    }
+    uint32_t before, tot;
+    wave_totals_prefix<NT / 64>(s_tmp, &before, &tot);
     __syncthreads();
     *total = tot;
     return before + x - v;
@@ -175,26 +201,21 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp,
 // s_tmp holds (NT/64) * N words.  pre[i] = sum of v[i] over lower threads; tot[i] = total.
 template <int N, int NT = kThreads>
 __device__ __forceinline__ void block_excl_scan_n(const uint32_t* v, uint32_t* pre, uint32_t* tot, uint32_t* s_tmp) {
+    constexpr int NW = NT / 64;
     const int lane = lane_id(), w = wave_id();
     uint32_t x[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) x[i] = wave_incl_scan(v[i]);
     if (lane == 63) {
 #pragma unroll
-        for (int i = 0; i < N; ++i) s_tmp[w * N + i] = x[i];
+        for (int i = 0; i < N; ++i) s_tmp[i * NW + w] = x[i];
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        uint32_t before = 0, t = 0;
-#pragma unroll
-        for (int ww = 0; ww < NT / 64; ++ww) {
-            const uint32_t c = s_tmp[ww * N + i];
-            before += (ww < w) ? c : 0u;
-            t += c;
-        }
+        uint32_t before;
+        wave_totals_prefix<NW>(s_tmp + i * NW, &before, &tot[i]);
         pre[i] = before + x[i] - v[i];
-        tot[i] = t;
     }
     __syncthreads();
 }
@@ -266,6 +287,18 @@ __device__ __forceinline__ void load_hist_desc(const uint32_t* __restrict__ h, u
         c[13 - 4 * i] = v[i].z;
         c[12 - 4 * i] = v[i].w;
     }
+}
+
+// ---- streaming stores of scratch that the next kernel reads once -------------------------
+__device__ __forceinline__ void st_stream(float4* p, float4 v) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f4*>(p));
+}
+__device__ __forceinline__ void st_stream(uint2* p, uint2 v) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 x = {v.x, v.y};
+    __builtin_nontemporal_store(x, reinterpret_cast<u2*>(p));
 }
 
 // ---- device-scope data hand-off inside one kernel ----------------------------------------

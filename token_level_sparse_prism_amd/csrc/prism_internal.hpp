@@ -19,7 +19,8 @@ constexpr int kThreads = 256;          // every kernel runs 4 waves of 64 lanes
 constexpr int kChunk = 1024;           // tokens per chunk in the proposal kernels
 constexpr int kScanWgs = PRISM_SCAN_WGS;
 constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in pool scoring
-constexpr int kAttendSlice = 64;       // selected rows per workgroup in sparse attention
+constexpr int kAttendRanks = 256;      // selected rows per workgroup in sparse attention
+constexpr int kAttendThreads = 1024;   // 16 waves: the selection's latency is shared by 4 waves per SIMD
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
 constexpr int kLdsCand = 4096;         // threshold candidates a compaction workgroup keeps in LDS
 constexpr int kCtrStride = 16;         // counters sit 64 bytes apart (no shared cache line)
@@ -74,11 +75,11 @@ inline int logit_stride(int GP) { return GP < 4 ? 4 : GP; }
 
 inline RefineWs refine_ws(int64_t units, int64_t kp, int64_t kappa, int GP, int D) {
     RefineWs w{};
-    const int64_t nsa = (kappa + kAttendSlice - 1) / kAttendSlice;
+    const int64_t nsa = (kappa + kAttendRanks - 1) / kAttendRanks;
     size_t o = 0;
     w.done_a = o;   o = align256(o + size_t(units) * kCtrStride * 4);
     w.ctrl_bytes = o;
-    w.skey = o;     o = align256(o + size_t(units) * key_stride(kp) * 4);
+    w.skey = o;     o = align256(o + size_t(units) * key_stride(kp) * 8);
     w.logits = o;   o = align256(o + size_t(units) * kp * logit_stride(GP) * 4);
     w.part_ml = o;  o = align256(o + size_t(units) * nsa * GP * 2 * 4);
     w.part_acc = o; o = align256(o + size_t(units) * nsa * GP * D * 4);
@@ -142,7 +143,7 @@ struct RefineArgs {
     int32_t* idx;
     float* lse;
     uint32_t* done_a;       // [U][kCtrStride]
-    uint32_t* skey;         // [U][kstride] order key of S per pool slot (0 = empty slot)
+    uint2* skey;            // [U][kstride] {order key of S (0 = empty slot), token} per pool slot
     float* logits;          // [U][kp][LS]
     float* part_ml;         // [U][nsa][GP][2]
     float* part_acc;        // [U][nsa][GP][D]

@@ -1,59 +1,150 @@
 // prism_select.hpp -- exact top-kappa selection of one unit's pool slots inside one workgroup
 // (the refined layer's re-selection within the inherited pool, Prism Attention page Sec. 4.1).
 //
-// Keys are 32-bit order keys of the group scores, one per pool slot (0 = empty slot).  They are
-// read from global memory in rows of 1024 (four consecutive slots per thread, one 16-byte load),
-// up to eight rows per tile held in registers.  The threshold comes from three radix digits
-// (12/12/8 bits): the first histogram covers every key; the keys of the threshold bin are then
-// compacted into a short LDS list (wave ballots) and the two lower digits are histogrammed over
-// that list.  Selected slots are ranked in slot order (ties at the threshold go to the lower
-// slot) with two multi-row workgroup scans.  The per-key work is branch-free.
+// Input per pool slot: {order key of the group score S (0 = empty slot), token id}.
+//   1. The keys' top 12 bits are counted in an LDS histogram; one wave scans it in descending
+//      bin order and finds the bin that holds the kappa-th largest key.
+//   2. The keys of that bin are compacted into per-wave LDS lists with wave ballots.
+//   3. The candidates' next 8 bits (19..12) are counted in a 256-bin LDS histogram and one wave
+//      finds the sub-bin of the threshold; the few keys of that sub-bin give the exact threshold
+//      key tau, how many keys equal to tau are taken and how many there are, by direct counting.
+//      When a wave's list overflows, two radix digits (12 + 8 bits) over every key are used.
+//   4. Selected slots are ranked in slot order, ties at tau going to the lower slot, with
+//      workgroup scans; ranks [r0, r0 + n) land in LDS with their token ids.
+// Keys are read in tiles of 8192 slots, two slots per thread and row (one 16-byte load).
 #pragma once
 
 #include "prism_device.hpp"
 
 namespace prism {
 
-// A tile is 8192 keys: NT threads x sel_rows<NT>() rows of four keys.
 constexpr int64_t kSelTile = 8192;
-template <int NT> constexpr int sel_rows() { return int(kSelTile / (4 * NT)); }
-// LDS list of the threshold bin's keys: 2048 entries split over the waves
-template <int NT> constexpr int sel_cand_per_wave() { return 2048 / (NT / 64); }
-constexpr int kSelCandTotal = 2048;
+template <int NT> constexpr int sel_rows() { return int(kSelTile / (2 * NT)); }
+constexpr int kSelCandTotal = 2048;  // LDS list of the threshold bin's keys, split over the waves
+template <int NT> constexpr int sel_cand_per_wave() { return kSelCandTotal / (NT / 64); }
 
 struct SelResult {
     uint32_t kappa_eff;  // min(kappa, number of valid slots)
-    int n;               // ranks [r0, r0 + n) written to s_slot
+    int n;               // ranks [r0, r0 + n) written to s_slot / s_tok
+};
+
+// s_res words
+enum : int {
+    kResValid = 0, kResKappa, kResBin, kResAbove, kResCount, kResTau, kResNeed, kResEq,
+    kResOvf, kResBin2, kResAbove2, kResC2, kResScratch
 };
 
 template <int NT>
-__device__ __forceinline__ void sel_load_tile(const uint32_t* __restrict__ gkeys, int64_t kp, int64_t t0,
-                                              uint4* kv) {
+__device__ __forceinline__ void sel_load_tile(const uint2* __restrict__ gk, int64_t kp, int64_t t0, uint4* kv) {
 #pragma unroll
     for (int r = 0; r < sel_rows<NT>(); ++r) {
-        const int64_t j = t0 + int64_t(r) * 4 * NT + int64_t(threadIdx.x) * 4;
-        if (j + 4 <= kp) {
-            kv[r] = *reinterpret_cast<const uint4*>(gkeys + j);
+        const int64_t j = t0 + int64_t(r) * 2 * NT + int64_t(threadIdx.x) * 2;
+        if (j + 2 <= kp) {
+            kv[r] = *reinterpret_cast<const uint4*>(gk + j);
         } else {
-            kv[r].x = j < kp ? gkeys[j] : 0u;
-            kv[r].y = j + 1 < kp ? gkeys[j + 1] : 0u;
-            kv[r].z = j + 2 < kp ? gkeys[j + 2] : 0u;
-            kv[r].w = j + 3 < kp ? gkeys[j + 3] : 0u;
+            const uint2 v = j < kp ? gk[j] : make_uint2(0u, 0xFFFFFFFFu);
+            kv[r] = make_uint4(v.x, v.y, 0u, 0xFFFFFFFFu);
         }
     }
 }
 
-__device__ __forceinline__ void unpack4(const uint4& v, uint32_t* k) {
-    k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
+// Level-1 LDS histogram: every 64 bins are followed by 4 pad words, so that the 64 lanes of the
+// crossing wave, each reading one group of 64 bins with 16-byte loads, spread over the banks.
+constexpr int kHist1Words = kHistBins + kHistBins / 16;
+constexpr int kSelHistWords = kHist1Words + 256;  // level-1 histogram, then the 256-bin level 2
+__device__ __forceinline__ int hpad64(int bin) { return bin + 4 * (bin >> 6); }
+
+// Step 1, run by one wave: lane l holds bins 4095 - 64 l - k (k < 64).  Writes the number of
+// valid keys, kappa_eff and, when 0 < kappa_eff < valid, the crossing bin, the count of keys
+// above it and its own count.
+__device__ __forceinline__ void sel_hist_crossing(const uint32_t* s_hist, uint32_t kappa, uint32_t* s_res) {
+    const int lane = lane_id();
+    const int base = kHistBins - 64 * (lane + 1);  // ascending bins base .. base + 63
+    const uint4* p = reinterpret_cast<const uint4*>(s_hist + hpad64(base));
+    uint32_t gs[16], sum = 0;  // group g: the four bins base + 60 - 4g .. base + 63 - 4g
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+        const uint4 x = p[15 - g];
+        gs[g] = (x.x + x.y) + (x.z + x.w);
+        sum += gs[g];
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t total = readlane_u32(incl, 63);
+    const uint32_t kap = kappa < total ? kappa : total;
+    if (lane == 0) {
+        s_res[kResValid] = total;
+        s_res[kResKappa] = kap;
+        s_res[kResBin] = 0u;
+        s_res[kResAbove] = 0u;
+        s_res[kResCount] = 0u;
+        s_res[kResOvf] = 0u;
+        s_res[kResC2] = 0u;
+    }
+    if (kap == 0u || kap == total) return;
+    uint32_t acc = incl - sum;
+    if (acc < kap && kap <= incl) {  // exactly one lane
+        bool found = false;
+        uint32_t gacc = 0;
+        int gsel = 0;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            const bool hit = !found && acc + gs[g] >= kap;
+            gsel = hit ? g : gsel;
+            gacc = hit ? acc : gacc;
+            found = found || hit;
+            acc += found ? 0u : gs[g];
+        }
+        const uint4 x = p[15 - gsel];  // the group's bins again, from LDS
+        const uint32_t c[4] = {x.w, x.z, x.y, x.x};
+        bool f2 = false;
+        uint32_t bin = 0, above = 0, cnt = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool hit = !f2 && gacc + c[k] >= kap;
+            bin = hit ? uint32_t(base + 4 * (15 - gsel) + 3 - k) : bin;
+            above = hit ? gacc : above;
+            cnt = hit ? c[k] : cnt;
+            f2 = f2 || hit;
+            gacc += f2 ? 0u : c[k];
+        }
+        s_res[kResBin] = bin;
+        s_res[kResAbove] = above;
+        s_res[kResCount] = cnt;
+    }
+}
+
+// Level-2 crossing, run by one wave over the 256-bin histogram of bits 19..12 of the threshold
+// bin's keys: lane l holds bins 255 - 4 l - k (k < 4).  Requires 1 <= R <= the histogram total.
+__device__ __forceinline__ void sel_sub_crossing(const uint32_t* s_h2, uint32_t R, uint32_t* s_res) {
+    const int lane = lane_id();
+    const uint4 x = reinterpret_cast<const uint4*>(s_h2)[63 - lane];  // bins 252 - 4 l .. 255 - 4 l
+    const uint32_t c[4] = {x.w, x.z, x.y, x.x};
+    const uint32_t sum = (c[0] + c[1]) + (c[2] + c[3]);
+    const uint32_t incl = wave_incl_scan(sum);
+    uint32_t acc = incl - sum;
+    if (acc < R && R <= incl) {
+        bool f = false;
+        uint32_t bin = 0, above = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool hit = !f && acc + c[k] >= R;
+            bin = hit ? uint32_t(255 - 4 * lane - k) : bin;
+            above = hit ? acc : above;
+            f = f || hit;
+            acc += f ? 0u : c[k];
+        }
+        s_res[kResBin2] = bin;
+        s_res[kResAbove2] = above;
+    }
 }
 
 // Histogram of the digit (k >> shift) & mask over the keys whose bits from pre_shift up equal
-// `pre`.  Reads the compacted per-wave lists when none overflowed, else every key again.
+// `pre`, from the per-wave lists when none overflowed, else from every key again.
 template <int NT>
-__device__ __forceinline__ void sel_digit_hist(const uint32_t* __restrict__ gkeys, int64_t kp, int ntiles, uint4* kv,
+__device__ __forceinline__ void sel_digit_hist(const uint2* __restrict__ gk, int64_t kp, int ntiles, uint4* kv,
                                                const uint32_t* s_cand, const uint32_t* s_ccount, bool from_list,
-                                               uint32_t pre, int pre_shift, int shift, uint32_t mask,
-                                               bool padded, uint32_t* s_hist) {
+                                               uint32_t pre, int pre_shift, int shift, uint32_t mask, bool padded,
+                                               uint32_t* s_hist) {
     const int tid = threadIdx.x;
     if (from_list) {
         for (int w = 0; w < NT / 64; ++w) {
@@ -68,15 +159,14 @@ __device__ __forceinline__ void sel_digit_hist(const uint32_t* __restrict__ gkey
         }
     } else {
         for (int t = 0; t < ntiles; ++t) {
-            if (ntiles > 1) sel_load_tile<NT>(gkeys, kp, int64_t(t) * kSelTile, kv);
+            if (ntiles > 1) sel_load_tile<NT>(gk, kp, int64_t(t) * kSelTile, kv);
 #pragma unroll
             for (int r = 0; r < sel_rows<NT>(); ++r) {
-                uint32_t k[4];
-                unpack4(kv[r], k);
+                const uint32_t k2[2] = {kv[r].x, kv[r].z};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if ((k[e] >> pre_shift) == pre && k[e]) {
-                        const int bin = int((k[e] >> shift) & mask);
+                for (int e = 0; e < 2; ++e) {
+                    if ((k2[e] >> pre_shift) == pre && k2[e]) {
+                        const int bin = int((k2[e] >> shift) & mask);
                         atomicAdd(&s_hist[padded ? hpad(bin) : bin], 1u);
                     }
                 }
@@ -85,151 +175,205 @@ __device__ __forceinline__ void sel_digit_hist(const uint32_t* __restrict__ gkey
     }
 }
 
-// s_hist: kHistPadded words; s_tmp: (NT/64) * max(1, sel_rows/2) words; s_cand: kSelCandTotal
-// words; s_ccount: NT/64 words; s_slot: nmax slots.
+// gk: the unit's [kp] {key, token} slots (16-byte aligned).
+// LDS: s_hist kSelHistWords words, 16-byte aligned; s_tmp (NT/64)*2 words; s_res 16 words;
+// s_cand kSelCandTotal words (16-byte aligned), s_ccount NT/64 words, s_slot / s_tok nmax each.
 template <int NT>
-__device__ __forceinline__ SelResult select_slice(const uint32_t* __restrict__ gkeys, int64_t kp, uint32_t kappa,
-                                                  int r0, int nmax, uint32_t* s_hist, uint32_t* s_tmp,
-                                                  uint32_t* s_res, uint32_t* s_cand, uint32_t* s_ccount,
-                                                  int32_t* s_slot) {
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+__device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, int64_t kp, uint32_t kappa, int r0, int nmax, uint32_t* s_hist,
+                                                  uint32_t* s_tmp, uint32_t* s_res, uint32_t* s_cand,
+                                                  uint32_t* s_ccount, int32_t* s_slot, int32_t* s_tok) {
+    constexpr int NW = NT / 64;
     constexpr int ROWS = sel_rows<NT>();
     constexpr int CPW = sel_cand_per_wave<NT>();
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int ntiles = int((kp + kSelTile - 1) / kSelTile);
     uint4 kv[ROWS];
 
-    // ---- digit 1: top 12 bits of every key (empty and padding slots land in bin 0) ----
-    for (int i = tid; i < kHistPadded; i += NT) s_hist[i] = 0u;
+    // ---- level-1 histogram (the LDS is cleared while the first keys are in flight) ----
+    sel_load_tile<NT>(gk, kp, 0, kv);
+    for (int i = tid; i < kSelHistWords / 4; i += NT) reinterpret_cast<uint4*>(s_hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-    uint32_t nv = 0;
     for (int t = 0; t < ntiles; ++t) {
-        sel_load_tile<NT>(gkeys, kp, int64_t(t) * kSelTile, kv);
+        if (t > 0) sel_load_tile<NT>(gk, kp, int64_t(t) * kSelTile, kv);
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            uint32_t k[4];
-            unpack4(kv[r], k);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                nv += k[e] != 0u ? 1u : 0u;
-                atomicAdd(&s_hist[hpad(int(k[e] >> kKeyShift))], 1u);
-            }
+            if (kv[r].x) atomicAdd(&s_hist[hpad64(int(kv[r].x >> kKeyShift))], 1u);
+            if (kv[r].z) atomicAdd(&s_hist[hpad64(int(kv[r].z >> kKeyShift))], 1u);
         }
     }
-    const uint32_t n_valid = block_sum_u32<NT>(nv, s_tmp);
-    const uint32_t kappa_eff = n_valid < kappa ? n_valid : kappa;
+    __syncthreads();
+    if (wave == 0) sel_hist_crossing(s_hist, kappa, s_res);
+    if (ntiles > 1) sel_load_tile<NT>(gk, kp, 0, kv);
+    __syncthreads();
+    const uint32_t n_valid = s_res[kResValid];
+    const uint32_t kappa_eff = s_res[kResKappa];
     SelResult res{kappa_eff, 0};
     if (kappa_eff == 0) return res;
-    if (tid == 0) s_hist[hpad(0)] = 0u;  // bin 0 holds no valid key
-    __syncthreads();
 
-    // ---- threshold tau and the number of keys equal to it to take ----
-    uint32_t tau = 1u, need = 0xFFFFFFFFu;  // every valid key is taken
+    // ---- threshold tau, the number of keys equal to tau to take, and how many there are ----
+    uint32_t tau = 1u, need = 0xFFFFFFFFu, eq_total = 0u;  // default: every valid key is taken
     if (kappa_eff < n_valid) {
-        find_crossing<kHistBins, NT>(s_hist, kappa_eff, s_tmp, s_res);
-        const uint32_t bin = s_res[0], above = s_res[1];
-        // compact the threshold bin's keys, per wave, into LDS
+        const uint32_t bin = s_res[kResBin], above = s_res[kResAbove];
         uint32_t cnt = 0;
         for (int t = 0; t < ntiles; ++t) {
-            if (ntiles > 1) sel_load_tile<NT>(gkeys, kp, int64_t(t) * kSelTile, kv);
+            if (t > 0) sel_load_tile<NT>(gk, kp, int64_t(t) * kSelTile, kv);
 #pragma unroll
             for (int r = 0; r < ROWS; ++r) {
-                uint32_t k[4];
-                unpack4(kv[r], k);
+                const uint32_t k2[2] = {kv[r].x, kv[r].z};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool f = (k[e] >> kKeyShift) == bin && k[e] != 0u;
+                for (int e = 0; e < 2; ++e) {
+                    const bool f = (k2[e] >> kKeyShift) == bin && k2[e] != 0u;
                     const uint64_t m = ballot64(f);
                     const uint32_t pos = cnt + lanes_below(m);
-                    if (f && pos < uint32_t(CPW)) s_cand[wave * CPW + pos] = k[e];
+                    if (f && pos < uint32_t(CPW)) s_cand[wave * CPW + pos] = k2[e];
                     cnt += uint32_t(__popcll(m));
                 }
             }
         }
         if (lane == 0) s_ccount[wave] = cnt;
-        for (int i = tid; i < kHistPadded; i += NT) s_hist[i] = 0u;
+        if (lane == 0 && cnt > uint32_t(CPW)) s_res[kResOvf] = 1u;
         __syncthreads();
-        bool from_list = true;
-        for (int w = 0; w < NT / 64; ++w) from_list = from_list && s_ccount[w] <= uint32_t(CPW);
-        sel_digit_hist<NT>(gkeys, kp, ntiles, kv, s_cand, s_ccount, from_list, bin, kKeyShift, 8, 0xFFFu, true, s_hist);
-        __syncthreads();
-        find_crossing<kHistBins, NT>(s_hist, kappa_eff - above, s_tmp, s_res);
-        const uint32_t pre = (bin << 12) | s_res[0];
-        const uint32_t above_a = s_res[1];
-        if (tid < 256) s_hist[tid] = 0u;
-        __syncthreads();
-        sel_digit_hist<NT>(gkeys, kp, ntiles, kv, s_cand, s_ccount, from_list, pre, 8, 0, 0xFFu, false, s_hist);
-        __syncthreads();
-        find_crossing<256, NT>(s_hist, kappa_eff - above - above_a, s_tmp, s_res);
-        tau = (pre << 8) | s_res[0];
-        need = kappa_eff - above - above_a - s_res[1];
+        const bool overflow = s_res[kResOvf] != 0u;
+        const uint32_t R = kappa_eff - above;  // rank of tau inside the bin, 1 <= R <= count of the bin
+        if (!overflow) {
+            // level 2: bits 19..12 of the wave's own list
+            uint32_t* s_h2 = s_hist + kHist1Words;
+            const uint32_t k0 = uint32_t(lane) < cnt ? s_cand[wave * CPW + lane] : 0u;
+            const uint32_t k1 = uint32_t(lane) + 64 < cnt ? s_cand[wave * CPW + 64 + lane] : 0u;
+            if (k0) atomicAdd(&s_h2[(k0 >> 12) & 0xFFu], 1u);
+            if (k1) atomicAdd(&s_h2[(k1 >> 12) & 0xFFu], 1u);
+            __syncthreads();
+            if (wave == 0) sel_sub_crossing(s_h2, R, s_res);
+            __syncthreads();
+            // the sub-bin's keys into one short list (any order), in the dead level-1 buffer
+            const uint32_t pre = (bin << 8) | s_res[kResBin2];
+            const uint32_t R2 = R - s_res[kResAbove2];
+            const bool f0 = k0 != 0u && (k0 >> 12) == pre;
+            const bool f1 = k1 != 0u && (k1 >> 12) == pre;
+            const uint64_t m0 = ballot64(f0), m1 = ballot64(f1);
+            const uint32_t nf = uint32_t(__popcll(m0) + __popcll(m1));
+            if (nf) {
+                uint32_t base = 0;
+                if (lane == 0) base = atomicAdd(&s_res[kResC2], nf);
+                base = readlane_u32(base, 0);
+                if (f0) s_hist[base + lanes_below(m0)] = k0;
+                if (f1) s_hist[base + uint32_t(__popcll(m0)) + lanes_below(m1)] = k1;
+            }
+            __syncthreads();
+            const uint32_t c2 = s_res[kResC2];
+            for (uint32_t i = tid; i < c2; i += NT) {
+                const uint32_t k = s_hist[i];
+                uint32_t gt = 0, ge = 0;
+                for (uint32_t j = 0; j < c2; ++j) {
+                    const uint32_t x = s_hist[j];
+                    gt += x > k ? 1u : 0u;
+                    ge += x >= k ? 1u : 0u;
+                }
+                if (gt < R2 && R2 <= ge) {
+                    s_res[kResTau] = k;
+                    s_res[kResNeed] = R2 - gt;
+                    s_res[kResEq] = ge - gt;
+                }
+            }
+            __syncthreads();
+        } else {
+            // radix digits 2 (bits 19..8) and 3 (bits 7..0) of the keys in the bin
+            uint32_t* s_r2 = s_res + kResScratch;
+            for (int i = tid; i < kHistPadded; i += NT) s_hist[i] = 0u;
+            __syncthreads();
+            sel_digit_hist<NT>(gk, kp, ntiles, kv, s_cand, s_ccount, !overflow, bin, kKeyShift, 8, 0xFFFu, true,
+                               s_hist);
+            __syncthreads();
+            find_crossing<kHistBins, NT>(s_hist, R, s_tmp, s_r2);
+            const uint32_t pre = (bin << 12) | s_r2[0];
+            const uint32_t above_a = s_r2[1];
+            __syncthreads();
+            if (tid < 256) s_hist[tid] = 0u;
+            __syncthreads();
+            sel_digit_hist<NT>(gk, kp, ntiles, kv, s_cand, s_ccount, !overflow, pre, 8, 0, 0xFFu, false, s_hist);
+            __syncthreads();
+            find_crossing<256, NT>(s_hist, R - above_a, s_tmp, s_r2);
+            if (tid == 0) {
+                s_res[kResTau] = (pre << 8) | s_r2[0];
+                s_res[kResNeed] = R - above_a - s_r2[1];
+                s_res[kResEq] = s_r2[2];
+            }
+            __syncthreads();
+        }
+        tau = s_res[kResTau];
+        need = s_res[kResNeed];
+        eq_total = s_res[kResEq];
+        if (ntiles > 1) sel_load_tile<NT>(gk, kp, 0, kv);  // the rank pass starts from the first tile
     }
-    if (ntiles > 1) sel_load_tile<NT>(gkeys, kp, 0, kv);  // the rank pass starts from the first tile
 
     const int n = int(kappa_eff) - r0 <= 0 ? 0 : (int(kappa_eff) - r0 > nmax ? nmax : int(kappa_eff) - r0);
     res.n = n;
     if (n == 0) return res;
 
-    // ---- ranks in slot order; ranks [r0, r0 + n) land in s_slot ----
+    // ---- ranks in slot order; ranks [r0, r0 + n) land in s_slot / s_tok ----
+    // per-row counts of one thread are at most 2, two rows share a 32-bit word (16 bits each)
+    constexpr int NP = ROWS / 2 > 0 ? ROWS / 2 : 1;
+    const bool take_all_eq = need >= eq_total;  // every key equal to tau is taken: select key >= tau
     uint32_t eq_base = 0, rank_base = 0;
     for (int t = 0; t < ntiles && rank_base < uint32_t(r0 + n); ++t) {
-        if (ntiles > 1 && t > 0) sel_load_tile<NT>(gkeys, kp, int64_t(t) * kSelTile, kv);
-        // per-row counts, two rows per 32-bit word (a row holds at most 1024 keys)
-        constexpr int NP = ROWS / 2 > 0 ? ROWS / 2 : 1;
-        uint32_t eqc[NP], gtc[NP];
+        if (t > 0) sel_load_tile<NT>(gk, kp, int64_t(t) * kSelTile, kv);
+        uint32_t eqc[NP], eqp[NP], eqt[NP], selc[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            eqc[p] = gtc[p] = 0;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                uint32_t k[4];
-                if (2 * p + half >= ROWS) continue;
-                unpack4(kv[2 * p + half], k);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    eqc[p] += ((k[e] == tau && k[e] != 0u) ? 1u : 0u) << (16 * half);
-                    gtc[p] += (k[e] > tau ? 1u : 0u) << (16 * half);
-                }
-            }
-        }
-        uint32_t eqp[NP], eqt[NP];
-        block_excl_scan_n<NP, NT>(eqc, eqp, eqt, s_tmp);
-        uint32_t selc[NP];
-        uint32_t run = eq_base;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
+            eqc[p] = 0;
             selc[p] = 0;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const uint32_t ec = (eqc[p] >> (16 * half)) & 0xFFFFu;
-                const uint32_t eqb = run + ((eqp[p] >> (16 * half)) & 0xFFFFu);
-                const uint32_t take = eqb >= need ? 0u : (ec < need - eqb ? ec : need - eqb);
-                selc[p] += (((gtc[p] >> (16 * half)) & 0xFFFFu) + take) << (16 * half);
-                run += (eqt[p] >> (16 * half)) & 0xFFFFu;
+                if (2 * p + half >= ROWS) continue;
+                const uint4 v = kv[2 * p + half];
+                const uint32_t ge = (v.x >= tau ? 1u : 0u) + (v.z >= tau ? 1u : 0u);
+                const uint32_t eq = (v.x == tau ? 1u : 0u) + (v.z == tau ? 1u : 0u);
+                eqc[p] += eq << (16 * half);
+                selc[p] += (take_all_eq ? ge : ge - eq) << (16 * half);  // keys above tau, or >= tau
+            }
+        }
+        if (!take_all_eq) {
+            block_excl_scan_n<NP, NT>(eqc, eqp, eqt, s_tmp);
+            uint32_t run = eq_base;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint32_t ec = (eqc[p] >> (16 * half)) & 0xFFFFu;
+                    const uint32_t eqb = run + ((eqp[p] >> (16 * half)) & 0xFFFFu);
+                    const uint32_t take = eqb >= need ? 0u : (ec < need - eqb ? ec : need - eqb);
+                    selc[p] += take << (16 * half);
+                    run += (eqt[p] >> (16 * half)) & 0xFFFFu;
+                }
             }
         }
         uint32_t selp[NP], selt[NP];
         block_excl_scan_n<NP, NT>(selc, selp, selt, s_tmp);
         uint32_t rrun = rank_base;
-        run = eq_base;
+        uint32_t run = eq_base;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
             const int p = r / 2, sh = 16 * (r % 2);
             uint32_t rank = rrun + ((selp[p] >> sh) & 0xFFFFu);
-            uint32_t eqr = run + ((eqp[p] >> sh) & 0xFFFFu);
-            uint32_t k[4];
-            unpack4(kv[r], k);
-            const int32_t slot0 = int32_t(int64_t(t) * kSelTile + int64_t(r) * 4 * NT + tid * 4);
+            uint32_t eqr = run + (take_all_eq ? 0u : ((eqp[p] >> sh) & 0xFFFFu));
+            const uint4 v = kv[r];
+            const uint32_t k2[2] = {v.x, v.z};
+            const int32_t t2[2] = {int32_t(v.y), int32_t(v.w)};
+            const int32_t slot0 = int32_t(int64_t(t) * kSelTile + int64_t(r) * 2 * NT + tid * 2);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool eq = k[e] == tau && k[e] != 0u;
-                const bool take = k[e] > tau || (eq && eqr < need);
+            for (int e = 0; e < 2; ++e) {
+                const bool eq = k2[e] == tau;
+                const bool take = k2[e] > tau || (eq && (take_all_eq || eqr < need));
                 eqr += eq ? 1u : 0u;
                 const uint32_t off = rank - uint32_t(r0);  // wraps for ranks below r0
-                if (take && off < uint32_t(n)) s_slot[off] = slot0 + e;
+                if (take && off < uint32_t(n)) {
+                    s_slot[off] = slot0 + e;
+                    s_tok[off] = t2[e];
+                }
                 rank += take ? 1u : 0u;
             }
             rrun += (selt[p] >> sh) & 0xFFFFu;
-            run += (eqt[p] >> sh) & 0xFFFFu;
+            if (!take_all_eq) run += (eqt[p] >> sh) & 0xFFFFu;
         }
         eq_base = run;
         rank_base = rrun;
