@@ -88,6 +88,78 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
     }
 }
 
+// Matrix-core variant for bf16 (dense contraction of the G query heads with the gathered K rows).
+// v_mfma_f32_16x16x32_bf16 per 32 dims: A = the unit's queries (16 rows, heads >= G zero), B = 16
+// pool rows; lane l carries row / column l % 16 and dims 8 (l / 16) .. + 7 of the step, so a B
+// operand is one 16-byte piece of a K row.  A wave scores 16 slots; lane group l / 16 ends with
+// heads 4 (l / 16) .. + 3 of slot l % 16.
+template <int D, int GP, bool kMax>
+__global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int STEPS = D / 32;
+    constexpr int LS = GP < 4 ? 4 : GP;
+    constexpr int SLOTS = 16 * (kThreads / 64);
+    static_assert(SLOTS == kScoreSlice, "one slice of slots per workgroup");
+    const Dims& d = a.d;
+    const int lane = lane_id(), wave = wave_id();
+    const int unit = blockIdx.y;
+    const int b = unit / d.Hkv, g = unit % d.Hkv;
+    const int G = d.G;
+    const int64_t Tb = seq_len_of(d, b);
+    const int64_t kp = a.kp;
+    const int n = lane & 15, kg = lane >> 4;
+    const int64_t j = int64_t(blockIdx.x) * SLOTS + wave * 16 + n;
+
+    const int32_t t = j < kp ? a.pool[int64_t(unit) * kp + j] : -1;
+    const bool valid = t >= 0 && t < Tb;
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (int64_t(b) * d.Hq + int64_t(g) * G + n) * D + 8 * kg;
+    bf16x8 qa[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const uint4 v = n < G ? load16(qh + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
+        qa[s] = __builtin_bit_cast(bf16x8, v);
+    }
+    const uint16_t* kr = static_cast<const uint16_t*>(a.K) + (int64_t(unit) * d.T_max + (valid ? t : 0)) * D + 8 * kg;
+    uint4 kb[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) kb[s] = load16(kr + 32 * s);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, kb[s]), acc, 0, 0, 0);
+
+    // group score over the heads this lane holds, then over the lane groups holding heads
+    const float l4[4] = {acc[0], acc[1], acc[2], acc[3]};
+    float S = kMax ? -INFINITY : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (4 * kg + i < G) S = kMax ? fmaxf(S, l4[i]) : S + l4[i];
+    }
+    if constexpr (GP > 4) {
+        const float o = __shfl_xor(S, 16);
+        S = kMax ? fmaxf(S, o) : S + o;
+    }
+    if constexpr (GP > 8) {
+        const float o = __shfl_xor(S, 32);
+        S = kMax ? fmaxf(S, o) : S + o;
+    }
+    if (j < kp) {
+        if (4 * kg < LS) {
+            float4 v;
+            v.x = 4 * kg + 0 < GP ? l4[0] : 0.0f;
+            v.y = 4 * kg + 1 < GP ? l4[1] : 0.0f;
+            v.z = 4 * kg + 2 < GP ? l4[2] : 0.0f;
+            v.w = 4 * kg + 3 < GP ? l4[3] : 0.0f;
+            st_stream(reinterpret_cast<float4*>(a.logits + (int64_t(unit) * kp + j) * LS + 4 * kg), v);
+        }
+        if (kg == 0) {
+            const uint32_t key = valid ? order_key(S) : 0u;
+            st_stream(a.skey + int64_t(unit) * a.kstride + j, make_uint2(key, valid ? uint32_t(t) : 0xFFFFFFFFu));
+        }
+    }
+}
+
 template <typename T, int D, int GP>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     constexpr int NT = kAttendThreads;
@@ -145,7 +217,10 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     const int units = a.d.B * a.d.Hkv;
     const dim3 gs((a.kp + kScoreSlice - 1) / kScoreSlice, units);
     const dim3 ga((a.kappa + kAttendRanks - 1) / kAttendRanks, units);
-    {
+    if constexpr (sizeof(T) == 2) {
+        if (agg_max) launch_k("k_rscore", (k_rscore_mfma<D, GP, true>), gs, dim3(kThreads), st, a);
+        else launch_k("k_rscore", (k_rscore_mfma<D, GP, false>), gs, dim3(kThreads), st, a);
+    } else {
         if (agg_max) launch_k("k_rscore", (k_rscore<T, D, GP, true>), gs, dim3(kThreads), st, a);
         else launch_k("k_rscore", (k_rscore<T, D, GP, false>), gs, dim3(kThreads), st, a);
     }

@@ -2,8 +2,8 @@
 // (the refined layer's re-selection within the inherited pool, Prism Attention page Sec. 4.1).
 //
 // Input per pool slot: {order key of the group score S (0 = empty slot), token id}.
-//   1. The keys' top 12 bits are counted in an LDS histogram; one wave scans it in descending
-//      bin order and finds the bin that holds the kappa-th largest key.
+//   1. The keys' top 12 bits are counted in an LDS histogram; a workgroup scan over it in
+//      descending bin order finds the bin that holds the kappa-th largest key.
 //   2. The keys of that bin are compacted into per-wave LDS lists with wave ballots.
 //   3. The candidates' next 8 bits (19..12) are counted in a 256-bin LDS histogram and one wave
 //      finds the sub-bin of the threshold; the few keys of that sub-bin give the exact threshold
@@ -48,70 +48,9 @@ __device__ __forceinline__ void sel_load_tile(const uint2* __restrict__ gk, int6
     }
 }
 
-// Level-1 LDS histogram: every 64 bins are followed by 4 pad words, so that the 64 lanes of the
-// crossing wave, each reading one group of 64 bins with 16-byte loads, spread over the banks.
-constexpr int kHist1Words = kHistBins + kHistBins / 16;
-constexpr int kSelHistWords = kHist1Words + 256;  // level-1 histogram, then the 256-bin level 2
-__device__ __forceinline__ int hpad64(int bin) { return bin + 4 * (bin >> 6); }
-
-// Step 1, run by one wave: lane l holds bins 4095 - 64 l - k (k < 64).  Writes the number of
-// valid keys, kappa_eff and, when 0 < kappa_eff < valid, the crossing bin, the count of keys
-// above it and its own count.
-__device__ __forceinline__ void sel_hist_crossing(const uint32_t* s_hist, uint32_t kappa, uint32_t* s_res) {
-    const int lane = lane_id();
-    const int base = kHistBins - 64 * (lane + 1);  // ascending bins base .. base + 63
-    const uint4* p = reinterpret_cast<const uint4*>(s_hist + hpad64(base));
-    uint32_t gs[16], sum = 0;  // group g: the four bins base + 60 - 4g .. base + 63 - 4g
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-        const uint4 x = p[15 - g];
-        gs[g] = (x.x + x.y) + (x.z + x.w);
-        sum += gs[g];
-    }
-    const uint32_t incl = wave_incl_scan(sum);
-    const uint32_t total = readlane_u32(incl, 63);
-    const uint32_t kap = kappa < total ? kappa : total;
-    if (lane == 0) {
-        s_res[kResValid] = total;
-        s_res[kResKappa] = kap;
-        s_res[kResBin] = 0u;
-        s_res[kResAbove] = 0u;
-        s_res[kResCount] = 0u;
-        s_res[kResOvf] = 0u;
-        s_res[kResC2] = 0u;
-    }
-    if (kap == 0u || kap == total) return;
-    uint32_t acc = incl - sum;
-    if (acc < kap && kap <= incl) {  // exactly one lane
-        bool found = false;
-        uint32_t gacc = 0;
-        int gsel = 0;
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            const bool hit = !found && acc + gs[g] >= kap;
-            gsel = hit ? g : gsel;
-            gacc = hit ? acc : gacc;
-            found = found || hit;
-            acc += found ? 0u : gs[g];
-        }
-        const uint4 x = p[15 - gsel];  // the group's bins again, from LDS
-        const uint32_t c[4] = {x.w, x.z, x.y, x.x};
-        bool f2 = false;
-        uint32_t bin = 0, above = 0, cnt = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool hit = !f2 && gacc + c[k] >= kap;
-            bin = hit ? uint32_t(base + 4 * (15 - gsel) + 3 - k) : bin;
-            above = hit ? gacc : above;
-            cnt = hit ? c[k] : cnt;
-            f2 = f2 || hit;
-            gacc += f2 ? 0u : c[k];
-        }
-        s_res[kResBin] = bin;
-        s_res[kResAbove] = above;
-        s_res[kResCount] = cnt;
-    }
-}
+// LDS: the 4096-bin level-1 histogram, then the 256-bin level-2 histogram.
+constexpr int kHist1Words = kHistBins;
+constexpr int kSelHistWords = kHist1Words + 256;
 
 // Level-2 crossing, run by one wave over the 256-bin histogram of bits 19..12 of the threshold
 // bin's keys: lane l holds bins 255 - 4 l - k (k < 4).  Requires 1 <= R <= the histogram total.
@@ -197,12 +136,41 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
         if (t > 0) sel_load_tile<NT>(gk, kp, int64_t(t) * kSelTile, kv);
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            if (kv[r].x) atomicAdd(&s_hist[hpad64(int(kv[r].x >> kKeyShift))], 1u);
-            if (kv[r].z) atomicAdd(&s_hist[hpad64(int(kv[r].z >> kKeyShift))], 1u);
+            if (kv[r].x) atomicAdd(&s_hist[kv[r].x >> kKeyShift], 1u);
+            if (kv[r].z) atomicAdd(&s_hist[kv[r].z >> kKeyShift], 1u);
         }
     }
     __syncthreads();
-    if (wave == 0) sel_hist_crossing(s_hist, kappa, s_res);
+    // ---- crossing: thread t holds bins 4095 - 4t - k (k < 4), one 16-byte LDS read ----
+    {
+        static_assert(NT * 4 == kHistBins, "four bins per thread");
+        const uint4 x = *reinterpret_cast<const uint4*>(s_hist + (kHistBins - 4 * (tid + 1)));
+        const uint32_t c[4] = {x.w, x.z, x.y, x.x};
+        const uint32_t sum = (c[0] + c[1]) + (c[2] + c[3]);
+        uint32_t total;
+        uint32_t acc = block_excl_scan<NT>(sum, s_tmp, &total);
+        const uint32_t kap = kappa < total ? kappa : total;
+        if (tid == 0) {
+            s_res[kResValid] = total;
+            s_res[kResKappa] = kap;
+            s_res[kResOvf] = 0u;
+            s_res[kResC2] = 0u;
+        }
+        if (kap > 0u && kap < total && acc < kap && kap <= acc + sum) {  // exactly one thread
+            bool f = false;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool hit = !f && acc + c[k] >= kap;
+                if (hit) {
+                    s_res[kResBin] = uint32_t(kHistBins - 1 - 4 * tid - k);
+                    s_res[kResAbove] = acc;
+                    s_res[kResCount] = c[k];
+                }
+                f = f || hit;
+                acc += f ? 0u : c[k];
+            }
+        }
+    }
     if (ntiles > 1) sel_load_tile<NT>(gk, kp, 0, kv);
     __syncthreads();
     const uint32_t n_valid = s_res[kResValid];
