@@ -91,16 +91,15 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
             scl_pre[i] = t < nvalid ? scl[t] : 0.0f;
         }
     }
+    // rolling buffer of U rows per lane: a register is refilled with the row U rounds ahead as
+    // soon as it has been used, so about U loads stay in flight through the whole chunk
     uint4 kv[U];
-    auto issue = [&](int r0) {
-        const int8_t* base = a.Kq + (int64_t(unit) * d.T_max + c0) * D + sub * 16;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int tok = (r0 + u) * TPR + tok_lane;
-            kv[u] = tok < nvalid ? load16_stream(base + int64_t(tok) * D) : make_uint4(0, 0, 0, 0);
-        }
+    const int8_t* krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * D + sub * 16;  // this lane's first row
+    auto load_row = [&](int r) -> uint4 {
+        return r * TPR + tok_lane < nvalid ? load16_stream(krow + r * (TPR * D)) : make_uint4(0, 0, 0, 0);
     };
-    issue(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) kv[u] = load_row(u);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
@@ -156,6 +155,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         if (!first) {
             c0 = int64_t(chunk) * kChunk;
             nvalid = chunk_tokens(Tb, c0);
+            krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * D + sub * 16;
         }
         if (nvalid == 0) break;  // later chunks of this workgroup are past T_b too
         if (!first) {
@@ -166,9 +166,12 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         }
 
         // ---- streaming int8 scan ----
+        if (!first) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) kv[u] = load_row(u);
+        }
 #pragma unroll 1
         for (int r0 = 0; r0 < ROUNDS; r0 += U) {
-            if (!(first && r0 == 0)) issue(r0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int tok = (r0 + u) * TPR + tok_lane;
@@ -202,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
                     const float score = float(A) * s_scale[tok];  // one fp32 product
                     s_key[tok] = order_key(score);
                 }
+                if (r0 + U < ROUNDS) kv[u] = load_row(r0 + U + u);
             }
         }
         first = false;
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
 // ---------------------------------------------------------------------------------------------
 // k_cand: grid (chunks, units).
 __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
-    __shared__ uint32_t s_tmp[kThreads / 64];
+    __shared__ uint32_t s_tmp[kThreads / 64 * 2];
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_base;
 
@@ -273,12 +277,12 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
             ncand += kb == bin ? 1u : 0u;
         }
     }
-    const uint32_t chunk_gt = block_sum_u32(ngt, s_tmp);
-    uint32_t ctot;
-    uint32_t cpre = block_excl_scan(ncand, s_tmp, &ctot);
+    uint32_t v2[2] = {ngt, ncand}, p2[2], t2[2];
+    block_excl_scan_n<2>(v2, p2, t2, s_tmp);
+    uint32_t cpre = p2[1];
     if (tid == 0) {
-        a.cnt_gt[int64_t(unit) * a.nchunks + chunk] = chunk_gt;
-        s_base = ctot ? atomicAdd(&a.cand_cnt[int64_t(unit) * kCtrStride], ctot) : 0u;
+        a.cnt_gt[int64_t(unit) * a.nchunks + chunk] = t2[0];
+        s_base = t2[1] ? atomicAdd(&a.cand_cnt[int64_t(unit) * kCtrStride], t2[1]) : 0u;
     }
     __syncthreads();
     if (ncand) {
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
 // ---------------------------------------------------------------------------------------------
 // k_compact: grid (chunks, units).  Chunk 0 also writes the -1 padding and clears hist1.
 __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
-    __shared__ uint32_t s_tmp[kThreads / 64];
+    __shared__ uint32_t s_tmp[kThreads / 64 * 3];
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_hist[256];
     __shared__ uint2 s_cand[kLdsCand];
@@ -379,10 +383,10 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
             ceq += e.x == tau ? 1u : 0u;
         }
     }
-    gt_before = block_sum_u32(gt_before, s_tmp);
-    cgt = block_sum_u32(cgt, s_tmp);
-    const uint32_t eq_before = block_sum_u32(ceq, s_tmp);
-    const uint32_t offset = gt_before + cgt + min(eq_before, need);
+    uint32_t v3[3] = {gt_before, cgt, ceq}, p3[3], t3[3];
+    block_excl_scan_n<3>(v3, p3, t3, s_tmp);
+    const uint32_t eq_before = t3[2];
+    const uint32_t offset = t3[0] + t3[1] + min(eq_before, need);
 
     // ordered compaction of the chunk
     uint32_t neq = 0;
