@@ -19,7 +19,7 @@ constexpr int kThreads = 256;          // every kernel runs 4 waves of 64 lanes
 constexpr int kChunk = 1024;           // tokens per chunk in the proposal kernels
 constexpr int kScanWgs = PRISM_SCAN_WGS;
 constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in pool scoring
-constexpr int kAttendRanks = 256;      // selected rows per workgroup in sparse attention
+constexpr int kAttendRanks = 128;      // selected rows per workgroup in sparse attention
 constexpr int kAttendThreads = 1024;   // 16 waves: the selection's latency is shared by 4 waves per SIMD
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
 constexpr int kLdsCand = 4096;         // threshold candidates a compaction workgroup keeps in LDS
