@@ -21,6 +21,7 @@
 namespace prism {
 
 enum { kStBin = 0, kStAbove = 1, kStKpEff = 2 };
+constexpr int kFewCand = 256;  // LDS list of the candidates that share tau's top 24 bits
 
 __device__ __forceinline__ int chunk_tokens(int64_t Tb, int64_t c0) {
     return int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
@@ -306,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
     __shared__ uint32_t s_tmp[kThreads / 64 * 3];
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_hist[256];
-    __shared__ uint2 s_cand[kLdsCand];
+    __shared__ uint2 s_few[kFewCand];  // candidates sharing tau's top 24 bits
+    __shared__ uint32_t s_nfew;
 
     const Dims& d = a.d;
     const int tid = threadIdx.x;
@@ -351,36 +353,63 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
         for (int i = 0; i < 4; ++i) k[i] = tid * 4 + i < nvalid ? keys[tid * 4 + i] : 0u;
     }
     const uint2* cand = a.cand + int64_t(unit) * d.T_max;
-    const bool in_lds = c <= uint32_t(kLdsCand);
-    if (in_lds) {
-#pragma unroll 8
-        for (uint32_t i = tid; i < c; i += kThreads) s_cand[i] = cand[i];
-    }
 
     // digit A (bits 19..8) of the threshold
     const uint32_t need_bin = uint32_t(kp_eff) - above;
     find_crossing_regs<16>(h, kHistBins, need_bin, s_tmp, s_res);
     const uint32_t da = s_res[0], above_a = s_res[1];
     const uint32_t pre = (bin << 12) | da;
-    // digit B (bits 7..0) among the candidates whose top 24 bits match
+    // one pass over the candidates: the earlier chunks' candidates above pre (all of them above
+    // tau), and the last-byte histogram and list of those sharing pre
     s_hist[tid] = 0u;
+    if (tid == 0) s_nfew = 0u;
     __syncthreads();
-    for (uint32_t i = tid; i < c; i += kThreads) {
-        const uint32_t kk = in_lds ? s_cand[i].x : cand[i].x;
-        if ((kk >> 8) == pre) atomicAdd(&s_hist[kk & 0xFFu], 1u);
+    uint32_t cgt = 0;
+    constexpr int CB = 8;  // candidate loads in flight per thread
+    for (uint32_t i0 = 0; i0 < c; i0 += CB * kThreads) {
+        uint2 e[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const uint32_t i = i0 + u * kThreads + tid;
+            e[u] = i < c ? cand[i] : make_uint2(0u, 0xFFFFFFFFu);
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const uint32_t hi = e[u].x >> 8;
+            if (e[u].y != 0xFFFFFFFFu) {
+                if (hi == pre) {
+                    atomicAdd(&s_hist[e[u].x & 0xFFu], 1u);
+                    const uint32_t q = atomicAdd(&s_nfew, 1u);
+                    if (q < uint32_t(kFewCand)) s_few[q] = e[u];
+                } else if (hi > pre && e[u].y < uint32_t(c0)) {
+                    ++cgt;
+                }
+            }
+        }
     }
     __syncthreads();
     find_crossing<256>(s_hist, need_bin - above_a, s_tmp, s_res);
     const uint32_t tau = (pre << 8) | s_res[0];
     const uint32_t need = need_bin - above_a - s_res[1];  // keys equal to tau to take, >= 1
 
-    // candidates of the earlier chunks above / equal to tau
-    uint32_t cgt = 0, ceq = 0;
-    for (uint32_t i = tid; i < c; i += kThreads) {
-        const uint2 e = in_lds ? s_cand[i] : cand[i];
-        if (e.y < uint32_t(c0)) {
-            cgt += e.x > tau ? 1u : 0u;
-            ceq += e.x == tau ? 1u : 0u;
+    // the earlier chunks' candidates sharing pre: above tau, or equal to it
+    uint32_t ceq = 0;
+    const uint32_t nfew = s_nfew;
+    if (nfew <= uint32_t(kFewCand)) {
+        for (uint32_t i = tid; i < nfew; i += kThreads) {
+            const uint2 e = s_few[i];
+            if (e.y < uint32_t(c0)) {
+                cgt += e.x > tau ? 1u : 0u;
+                ceq += e.x == tau ? 1u : 0u;
+            }
+        }
+    } else {  // more than kFewCand keys share tau's top 24 bits: scan the list again
+        for (uint32_t i = tid; i < c; i += kThreads) {
+            const uint2 e = cand[i];
+            if ((e.x >> 8) == pre && e.y < uint32_t(c0)) {
+                cgt += e.x > tau ? 1u : 0u;
+                ceq += e.x == tau ? 1u : 0u;
+            }
         }
     }
     uint32_t v3[3] = {gt_before, cgt, ceq}, p3[3], t3[3];

@@ -22,7 +22,6 @@ constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in p
 constexpr int kAttendRanks = 128;      // selected rows per workgroup in sparse attention
 constexpr int kAttendThreads = 1024;   // 16 waves: the selection's latency is shared by 4 waves per SIMD
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
-constexpr int kLdsCand = 4096;         // threshold candidates a compaction workgroup keeps in LDS
 constexpr int kCtrStride = 16;         // counters sit 64 bytes apart (no shared cache line)
 constexpr int kHistBits = 12;          // first radix digit: top 12 bits of the order key
 constexpr int kHistBins = 1 << kHistBits;
