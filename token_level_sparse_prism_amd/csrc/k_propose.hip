@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     if (blockIdx.x == 0) {  // per-call state of the later kernels
         uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
         for (int i = tid; i < kHistBins; i += kThreads) h2[i] = 0u;
-        if (tid == 0) a.cand_cnt[int64_t(unit) * kCtrStride] = 0u;
+        if (tid < kCandLists) a.cand_cnt[(int64_t(unit) * kCandLists + tid) * kCtrStride] = 0u;
     }
     const int sub = lane % LPT;
     const int tok_lane = wave * TPW + lane / LPT;
@@ -283,18 +283,19 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
     uint32_t cpre = p2[1];
     if (tid == 0) {
         a.cnt_gt[int64_t(unit) * a.nchunks + chunk] = t2[0];
-        s_base = t2[1] ? atomicAdd(&a.cand_cnt[int64_t(unit) * kCtrStride], t2[1]) : 0u;
+        s_base = t2[1] ? atomicAdd(&a.cand_cnt[(int64_t(unit) * kCandLists + chunk % kCandLists) * kCtrStride], t2[1])
+                       : 0u;
     }
     __syncthreads();
     if (ncand) {
-        uint2* cand = a.cand + int64_t(unit) * d.T_max;
+        uint2* cand = a.cand + (int64_t(unit) * kCandLists + chunk % kCandLists) * a.cand_cap;
         uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
         const uint32_t base = s_base;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (tid * 4 + i < nvalid && (k[i] >> kKeyShift) == bin) {
                 const uint32_t pos = base + cpre++;
-                if (pos < uint32_t(d.T_max)) cand[pos] = make_uint2(k[i], uint32_t(c0 + tid * 4 + i));
+                if (pos < uint64_t(a.cand_cap)) cand[pos] = make_uint2(k[i], uint32_t(c0 + tid * 4 + i));
                 atomicAdd(&h2[(k[i] >> 8) & 0xFFFu], 1u);
             }
         }
@@ -336,7 +337,12 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
     const uint32_t* st = a.state + int64_t(unit) * 8;
     const uint32_t bin = st[kStBin];
     const uint32_t above = st[kStAbove];
-    const uint32_t c = min(a.cand_cnt[int64_t(unit) * kCtrStride], uint32_t(d.T_max));
+    // candidate sub-list l is read by threads 32 l .. 32 l + 31
+    static_assert(kCandLists * 32 == kThreads, "32 threads per candidate sub-list");
+    const int cl_id = tid >> 5, cl_lane = tid & 31;
+    const uint2* cand = a.cand + (int64_t(unit) * kCandLists + cl_id) * a.cand_cap;
+    uint32_t cn = a.cand_cnt[(int64_t(unit) * kCandLists + cl_id) * kCtrStride];
+    cn = cn < uint64_t(a.cand_cap) ? cn : uint32_t(a.cand_cap);
     uint32_t h[16];
     load_hist_desc(a.hist2 + int64_t(unit) * kHistBins, h);
     uint32_t gt_before = 0;
@@ -352,7 +358,6 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) k[i] = tid * 4 + i < nvalid ? keys[tid * 4 + i] : 0u;
     }
-    const uint2* cand = a.cand + int64_t(unit) * d.T_max;
 
     // digit A (bits 19..8) of the threshold
     const uint32_t need_bin = uint32_t(kp_eff) - above;
@@ -366,12 +371,12 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
     __syncthreads();
     uint32_t cgt = 0;
     constexpr int CB = 8;  // candidate loads in flight per thread
-    for (uint32_t i0 = 0; i0 < c; i0 += CB * kThreads) {
+    for (uint32_t i0 = 0; i0 < cn; i0 += CB * 32) {
         uint2 e[CB];
 #pragma unroll
         for (int u = 0; u < CB; ++u) {
-            const uint32_t i = i0 + u * kThreads + tid;
-            e[u] = i < c ? cand[i] : make_uint2(0u, 0xFFFFFFFFu);
+            const uint32_t i = i0 + u * 32 + cl_lane;
+            e[u] = i < cn ? cand[i] : make_uint2(0u, 0xFFFFFFFFu);
         }
 #pragma unroll
         for (int u = 0; u < CB; ++u) {
@@ -403,8 +408,8 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
                 ceq += e.x == tau ? 1u : 0u;
             }
         }
-    } else {  // more than kFewCand keys share tau's top 24 bits: scan the list again
-        for (uint32_t i = tid; i < c; i += kThreads) {
+    } else {  // more than kFewCand keys share tau's top 24 bits: scan the lists again
+        for (uint32_t i = cl_lane; i < cn; i += 32) {
             const uint2 e = cand[i];
             if ((e.x >> 8) == pre && e.y < uint32_t(c0)) {
                 cgt += e.x > tau ? 1u : 0u;

@@ -119,6 +119,7 @@ prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, con
     a.cnt_gt = reinterpret_cast<uint32_t*>(carve(ws, L.cnt_gt));
     a.keys = reinterpret_cast<uint32_t*>(carve(ws, L.keys));
     a.cand = reinterpret_cast<uint2*>(carve(ws, L.cand));
+    a.cand_cap = cand_list_cap(s->T_max);
     return hip_status(launch_propose(a, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream)));
 }
 

@@ -23,6 +23,7 @@ constexpr int kAttendRanks = 128;      // selected rows per workgroup in sparse 
 constexpr int kAttendThreads = 1024;   // 16 waves: the selection's latency is shared by 4 waves per SIMD
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
 constexpr int kCtrStride = 16;         // counters sit 64 bytes apart (no shared cache line)
+constexpr int kCandLists = 8;          // candidate sub-lists per unit (chunk % kCandLists), one counter each
 constexpr int kHistBits = 12;          // first radix digit: top 12 bits of the order key
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kKeyShift = 32 - kHistBits;
@@ -36,6 +37,11 @@ constexpr int kMaxG = 16;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // per-unit rows of 32-bit keys are padded to whole 16-byte vectors
 inline int64_t key_stride(int64_t n) { return (n + 3) & ~int64_t(3); }
+// capacity of one candidate sub-list: every token of the chunks that feed it
+inline int64_t cand_list_cap(int64_t T_max) {
+    const int64_t nch = (T_max + kChunk - 1) / kChunk;
+    return (nch + kCandLists - 1) / kCandLists * kChunk;
+}
 
 struct ProposeWs {
     size_t hist1, ctrl_bytes;
@@ -51,11 +57,11 @@ inline ProposeWs propose_ws(int64_t units, int64_t T_max) {
     w.hist1 = o;     o = align256(o + size_t(units) * kHistBins * 4);
     w.ctrl_bytes = o;
     w.hist2 = o;     o = align256(o + size_t(units) * kHistBins * 4);
-    w.cand_cnt = o;  o = align256(o + size_t(units) * kCtrStride * 4);
+    w.cand_cnt = o;  o = align256(o + size_t(units) * kCandLists * kCtrStride * 4);
     w.state = o;     o = align256(o + size_t(units) * 8 * 4);
     w.cnt_gt = o;    o = align256(o + size_t(units) * nch * 4);
     w.keys = o;      o = align256(o + size_t(units) * key_stride(T_max) * 4);
-    w.cand = o;      o = align256(o + size_t(units) * T_max * 8);
+    w.cand = o;      o = align256(o + size_t(units) * kCandLists * cand_list_cap(T_max) * 8);
     w.total = o;
     return w;
 }
@@ -122,11 +128,12 @@ struct ProposeArgs {
     float* scores;          // optional
     uint32_t* hist1;        // [U][kHistBins]  top 12 bits of every key
     uint32_t* hist2;        // [U][kHistBins]  bits 19..8 of the keys in the threshold bin
-    uint32_t* cand_cnt;     // [U][kCtrStride]
+    uint32_t* cand_cnt;     // [U][kCandLists][kCtrStride]
+    int64_t cand_cap;       // cand_list_cap(T_max)
     uint32_t* state;        // [U][8]: bin, above, kp_eff
     uint32_t* cnt_gt;       // [U][nchunks] keys above the threshold bin per chunk
     uint32_t* keys;         // [U][kstride]
-    uint2* cand;            // [U][T_max]: (key, token) of the threshold bin
+    uint2* cand;            // [U][kCandLists][cand_cap]: (key, token) of the threshold bin
 };
 
 struct RefineArgs {
