@@ -126,16 +126,22 @@ REFINE_CASES = [
     (256, 2, 1, PB.AGG_SUM, "f32", 1500, 900, 900, None),     # kappa = kp: static reuse
     (128, 4, 2, PB.AGG_SUM, "bf16", 1200, 2048, 1500, [1200, 0]),  # pool padding, empty sequence
     (128, 4, 1, PB.AGG_SUM, "bf16", 3000, 400, 1, None),        # kappa = 1
+    (128, 1, 2, PB.AGG_SUM, "bf16", 4000, 1500, 400, None),      # one head per KV head
+    (128, 2, 1, PB.AGG_MAX, "bf16", 4000, 1500, 400, None),
+    (128, 3, 2, PB.AGG_SUM, "bf16", 4000, 1200, 333, None),      # G padded to 4
+    (64, 8, 1, PB.AGG_MAX, "bf16", 3000, 1000, 250, None),       # MAX across two lane groups
+    (128, 16, 1, PB.AGG_MAX, "bf16", 3000, 1000, 250, None),     # MAX across four lane groups
+    (64, 4, 1, PB.AGG_SUM, "bf16", 20000, 10000, 3000, None),    # pool above one 8192-slot tile
 ]
 
 
 @pytest.mark.parametrize("case", REFINE_CASES, ids=lambda c: f"D{c[0]}G{c[1]}a{c[3]}{c[4]}kp{c[6]}k{c[7]}")
-@pytest.mark.parametrize("variant", ["random", "zero_q"])
+@pytest.mark.parametrize("variant", ["random", "zero_q", "ties"])
 def test_refine_parity(case, variant):
     D, G, Hkv, agg, dtype, T, kp, kappa, lens = case
     Bn = len(lens) if lens else 1
     q, K, V, lens = make_inputs(seed_of(D, G, T, kp, kappa, variant), Bn, G * Hkv, Hkv, D, T, dtype, lens,
-                                zero_q=variant == "zero_q")
+                                zero_q=variant == "zero_q", ties=variant == "ties")
     rng = np.random.default_rng(kp + kappa)
     q0 = rnd(rng, q.shape, dtype)
     oKq, osc = oracle.quantize_rows(K)
