@@ -26,8 +26,9 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
 
     const Dims& d = a.d;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const int unit = blockIdx.y;
-    const int chunk = blockIdx.x;
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
+    const int chunk = ui.x;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
     const int64_t Tb = seq_len_of(d, b);

@@ -52,12 +52,13 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
 
     const Dims& d = a.d;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const int unit = blockIdx.y;
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
     const int64_t Tb = seq_len_of(d, b);
 
-    if (blockIdx.x == 0) {  // per-call state of the later kernels
+    if (ui.x == 0) {  // per-call state of the later kernels
         uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
         for (int i = tid; i < kHistBins; i += kThreads) h2[i] = 0u;
         if (tid < kCandLists) a.cand_cnt[(int64_t(unit) * kCandLists + tid) * kCtrStride] = 0u;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         qraw[i] = p < npieces ? load16(static_cast<const uint8_t*>(a.q) + (qoff * (a.q_bf16 ? 2 : 4)) + p * 16)
                               : make_uint4(0, 0, 0, 0);
     }
-    int chunk = blockIdx.x;
+    int chunk = ui.x;
     int64_t c0 = int64_t(chunk) * kChunk;
     int nvalid = chunk < a.nchunks ? chunk_tokens(Tb, c0) : 0;
     float scl_pre[kChunk / kThreads];
@@ -239,8 +240,9 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
 
     const Dims& d = a.d;
     const int tid = threadIdx.x;
-    const int unit = blockIdx.y;
-    const int chunk = blockIdx.x;
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
+    const int chunk = ui.x;
     const int b = unit / d.Hkv;
     const int64_t Tb = seq_len_of(d, b);
     const int64_t kp_eff = Tb < a.kp ? Tb : a.kp;
@@ -313,8 +315,9 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 
     const Dims& d = a.d;
     const int tid = threadIdx.x;
-    const int unit = blockIdx.y;
-    const int chunk = blockIdx.x;
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
+    const int chunk = ui.x;
     const int b = unit / d.Hkv;
     const int64_t Tb = seq_len_of(d, b);
     const int64_t kp_eff = Tb < a.kp ? Tb : a.kp;

@@ -30,8 +30,9 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
 
     const Dims& d = a.d;
     const int lane = lane_id(), wave = wave_id();
-    const int unit = blockIdx.y;
-    const int slice = blockIdx.x;
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
+    const int slice = ui.x;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
     const int64_t Tb = seq_len_of(d, b);
@@ -103,13 +104,14 @@ __global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
     static_assert(SLOTS == kScoreSlice, "one slice of slots per workgroup");
     const Dims& d = a.d;
     const int lane = lane_id(), wave = wave_id();
-    const int unit = blockIdx.y;
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
     const int64_t Tb = seq_len_of(d, b);
     const int64_t kp = a.kp;
     const int n = lane & 15, kg = lane >> 4;
-    const int64_t j = int64_t(blockIdx.x) * SLOTS + wave * 16 + n;
+    const int64_t j = int64_t(ui.x) * SLOTS + wave * 16 + n;
 
     const int32_t t = j < kp ? a.pool[int64_t(unit) * kp + j] : -1;
     const bool valid = t >= 0 && t < Tb;
@@ -180,8 +182,9 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
 
     const Dims& d = a.d;
     const int tid = threadIdx.x;
-    const int unit = blockIdx.y;
-    const int slice = blockIdx.x;
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
+    const int slice = ui.x;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
     const int64_t kp = a.kp;

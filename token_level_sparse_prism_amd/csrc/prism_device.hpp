@@ -343,6 +343,18 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
 }
 
+// Workgroup (x, unit) of an (nx, units) grid, taken from the linear workgroup id so that the
+// workgroups of a unit share one XCD when units is a multiple of 8 (workgroups are dealt to the
+// eight XCDs round-robin by linear id).  A unit's scratch then stays in one XCD's L2 from one
+// kernel to the next.  Any other placement gives the same results.
+struct UnitIdx {
+    int unit, x;
+};
+__device__ __forceinline__ UnitIdx unit_major() {
+    const int L = int(blockIdx.x + blockIdx.y * gridDim.x);
+    return {L % int(gridDim.y), L / int(gridDim.y)};
+}
+
 __device__ __forceinline__ int64_t seq_len_of(const Dims& d, int b) {
     if (!d.seq_lens) return d.T_max;
     int64_t t = d.seq_lens[b];
