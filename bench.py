@@ -44,6 +44,10 @@ def parse():
                         "the scan kernel's HBM traffic per launch to " + os.path.relpath(PMC_FILE, ROOT))
     p.add_argument("--pmc-command", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("", ""),
                    help="the two rocprofv3 command lines, recorded beside the ingested figures")
+    p.add_argument("--recall", action="store_true",
+                   help="quality readout on the 262144-token stress workloads instead of the benchmark: "
+                        "salient, attention-mass and exact top-kappa recall of Prism (kp = rho*kappa) "
+                        "against static reuse (kp = kappa); one JSON line per (D, kappa, rho)")
     return p.parse_args()
 
 
@@ -108,10 +112,69 @@ def ingest_pmc(args):
     return 0
 
 
+def recall_readout():
+    """Per stress workload (8 query heads on one KV head, T = 262144, Student-t keys, 3 refined
+    layers) and pool factor rho, averaged over the refined layers (and heads for the mass):
+      salient: |idx_l & S_l| / |S_l|, the planted tokens each refined layer should attend to;
+      mass:    softmax mass of the selected tokens within the full-context softmax, per head,
+               exp(lse over idx_l - lse over the whole context);
+      exact:   |idx_l & E_l| / kappa, E_l = the layer's exact top-kappa over the whole context;
+               the softmax mass that E_l itself holds is reported beside it as the reference.
+    Everything runs through the library: E_l is refine_attend with the whole context as the pool,
+    the full-context lse is dense_ref.  rho = 1 is static reuse of the anchor's selection.  Both
+    aggregations of the G heads' scores (SUM, MAX) are read out."""
+    import numpy as np
+    import torch
+
+    from token_level_sparse_prism_amd import binding as PB
+    from token_level_sparse_prism_amd import workload as W
+
+    PB.load()
+    for D in (64, 256):
+        for kappa in (512, 2048, 8192):
+            cfg = W.CONFIGS[f"cfg5_D{D}_k{kappa}_r1"]
+            w = W.generate(cfg)  # the data do not depend on rho
+            dev = lambda x: torch.from_numpy(x).to(device="cuda", dtype=torch.bfloat16)
+            lens = torch.from_numpy(w.seq_lens).cuda()
+            Kq, sc = PB.quantize_keys(dev(w.K[0]), seq_lens=lens)
+            q0 = dev(w.q[0])
+            layers = [(dev(w.q[l]), dev(w.K[l]), dev(w.V[l])) for l in range(1, w.layers)]
+            full_pool = torch.arange(cfg.T, dtype=torch.int32, device="cuda").view(1, 1, cfg.T)
+            lse_full = [PB.dense_ref(q, K, V, seq_lens=lens)[1] for q, K, V in layers]
+            S0, Sl = w.salient[(0, 0)]
+            for agg, agg_name in ((PB.AGG_SUM, "sum"), (PB.AGG_MAX, "max")):
+                exact, exact_mass = [], []
+                for l, (q, K, V) in enumerate(layers):
+                    _, idx_e, lse_e = PB.refine_attend(q, K, V, full_pool, kappa, agg, seq_lens=lens)
+                    exact.append(set(idx_e.cpu().numpy().ravel().tolist()))
+                    exact_mass.append(float(torch.exp(lse_e - lse_full[l]).mean()))
+                for rho in (1, 2, 4, 8):
+                    kp = rho * kappa
+                    pool = PB.propose(q0, Kq, sc, kp, agg, seq_lens=lens)
+                    sal, mass, ex = [], [], []
+                    for l, (q, K, V) in enumerate(layers):
+                        _, idx, lse = PB.refine_attend(q, K, V, pool, kappa, agg, seq_lens=lens)
+                        sel = set(idx.cpu().numpy().ravel().tolist()) - {-1}
+                        sal.append(len(sel & set(Sl[l].tolist())) / max(1, len(Sl[l])))
+                        mass.append(float(torch.exp(lse - lse_full[l]).mean()))
+                        ex.append(len(sel & exact[l]) / kappa)
+                    torch.cuda.synchronize()
+                    print(json.dumps({"workload": f"stress D={D} kappa={kappa} rho={rho} agg={agg_name}", "D": D,
+                                      "kappa": kappa, "rho": rho, "kp": kp, "agg": agg_name, "T": cfg.T,
+                                      "salient_recall": round(float(np.mean(sal)), 4),
+                                      "mass_recall": round(float(np.mean(mass)), 4),
+                                      "exact_topk_recall": round(float(np.mean(ex)), 4),
+                                      "exact_topk_mass": round(float(np.mean(exact_mass)), 4),
+                                      "kind": "static reuse" if rho == 1 else "prism"}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.ingest_pmc:
         return ingest_pmc(args)
+    if args.recall:
+        return recall_readout()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the hot path needs no exchange between GPUs "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
