@@ -32,10 +32,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--config", default="cfg3")
     p.add_argument("--rotate", type=int, default=6, help="buffer sets cycled by the steps")
+    p.add_argument("--repeats", type=int, default=5, help="repeats of the timed region (median reported)")
     p.add_argument("--profile-steps", type=int, default=100, help="steps of the per-kernel event pass")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-graph", action="store_true", help="time stream launches instead of HIP graphs")
+    p.add_argument("--no-graph", action="store_true", help="time stream launches only (no HIP graph replay)")
     p.add_argument("--pmc-pass", action="store_true",
                    help="counter pass for rocprofv3 --pmc: --steps stream-launched steps, then one plain "
                         "copy of CALIB_BYTES as the counters' scale; no timing, no JSON line")
@@ -259,15 +260,23 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, time.perf_counter() - w0
 
-    ms_stream, wall_stream = timed(lambda i: steps[i % R]())
-    ms_graph = wall_graph = None
+    # the timed region, repeated per launch mode: median, p10 and p90 of the per-step time; the
+    # faster mode gives `value` (both are the same work)
+    modes = {"stream": [timed(lambda i: steps[i % R]()) for _ in range(args.repeats)]}
+    ms_warm = None
     if not args.no_graph:
         graphs = [st.capture() for st in steps]
         for i in range(args.warmup):
             graphs[i % R].replay()
-        ms_graph, wall_graph = timed(lambda i: graphs[i % R].replay())
-    ms_per_step = ms_graph if ms_graph is not None else ms_stream
-    wall = wall_graph if wall_graph is not None else wall_stream
+        modes["hip_graph"] = [timed(lambda i: graphs[i % R].replay()) for _ in range(args.repeats)]
+    med = {m: float(np.median([t for t, _ in v])) for m, v in modes.items()}
+    launch = min(med, key=med.get)
+    rep_ms = sorted(t for t, _ in modes[launch])
+    ms_per_step = med[launch]
+    ms_p10, ms_p90 = float(np.percentile(rep_ms, 10)), float(np.percentile(rep_ms, 90))
+    wall = sum(w for _, w in modes[launch])
+    # warm: one buffer set, so the 256 MB Infinity Cache may serve repeats (reported, labelled)
+    ms_warm, _ = timed(lambda i: graphs[0].replay()) if launch == "hip_graph" else timed(lambda i: steps[0]())
 
     # per-kernel durations: a separate pass with HIP events around every launch (same work)
     PB.profile_reset()
@@ -335,8 +344,11 @@ def main():
         "hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(ab["step"]),
         "roofline": roofline,
-        "launch": "hip_graph" if ms_graph is not None else "stream",
-        "ms_per_step_stream_launch": round(ms_stream, 5),
+        "launch": launch,
+        "repeats": len(rep_ms), "ms_per_step_p10": round(ms_p10, 5), "ms_per_step_p90": round(ms_p90, 5),
+        "tokens_per_s": round(cfg.B * steps_per_s, 2),
+        "ms_per_step_by_launch": {m: round(v, 5) for m, v in med.items()},
+        "ms_per_step_warm": round(ms_warm, 5),
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3), "gen_s": round(gen_s, 1),

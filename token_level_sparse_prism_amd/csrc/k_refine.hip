@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     __shared__ __align__(16) uint32_t s_big[kRowsAccFloats];  // selection histograms, then the waves' V partials
     __shared__ __align__(16) uint32_t s_cand[kSelCandTotal];
     __shared__ uint32_t s_ccount[NW];
-    __shared__ uint32_t s_tmp[NW * 2];
+    __shared__ uint32_t s_tmp[sel_tmp_words<NT>()];
     __shared__ uint32_t s_res[16];
     __shared__ int32_t s_slot[NR];
     __shared__ int32_t s_tok[NR];

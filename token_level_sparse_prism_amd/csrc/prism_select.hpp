@@ -20,6 +20,8 @@ namespace prism {
 
 constexpr int64_t kSelTile = 8192;
 template <int NT> constexpr int sel_rows() { return int(kSelTile / (2 * NT)); }
+// LDS words of the selection's scan scratch (s_tmp)
+template <int NT> constexpr int sel_tmp_words() { return (NT / 64) * (sel_rows<NT>() > 2 ? sel_rows<NT>() : 2); }
 constexpr int kSelCandTotal = 2048;  // LDS list of the threshold bin's keys, split over the waves
 template <int NT> constexpr int sel_cand_per_wave() { return kSelCandTotal / (NT / 64); }
 
@@ -115,7 +117,7 @@ __device__ __forceinline__ void sel_digit_hist(const uint2* __restrict__ gk, int
 }
 
 // gk: the unit's [kp] {key, token} slots (16-byte aligned).
-// LDS: s_hist kSelHistWords words, 16-byte aligned; s_tmp (NT/64)*2 words; s_res 16 words;
+// LDS: s_hist kSelHistWords words, 16-byte aligned; s_tmp sel_tmp_words<NT>() words; s_res 16 words;
 // s_cand kSelCandTotal words (16-byte aligned), s_ccount NT/64 words, s_slot / s_tok nmax each.
 template <int NT>
 __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, int64_t kp, uint32_t kappa, int r0, int nmax, uint32_t* s_hist,
@@ -279,9 +281,52 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
     if (n == 0) return res;
 
     // ---- ranks in slot order; ranks [r0, r0 + n) land in s_slot / s_tok ----
+    const bool take_all_eq = need >= eq_total;  // every key equal to tau is taken: select key >= tau
+    if (ntiles == 1 && take_all_eq) {
+        // one tile: per row, two wave ballots give every slot's rank among the wave's slots; the
+        // waves' counts per row are exchanged once and prefixed with a 16-lane DPP scan
+        static_assert(NW <= 16 && ROWS * NW <= sel_tmp_words<NT>(), "wave counts fit s_tmp");
+        uint64_t m0[ROWS], m1[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            m0[r] = ballot64(kv[r].x >= tau);
+            m1[r] = ballot64(kv[r].z >= tau);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) s_tmp[r * NW + wave] = uint32_t(__popcll(m0[r]) + __popcll(m1[r]));
+        }
+        __syncthreads();
+        uint32_t base = 0;
+        const int wu = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            uint32_t x = lane < NW ? s_tmp[r * NW + lane] : 0u;
+            x += dpp_u32<0x111>(x);
+            x += dpp_u32<0x112>(x);
+            x += dpp_u32<0x114>(x);
+            x += dpp_u32<0x118>(x);
+            const uint32_t before = wu > 0 ? readlane_u32(x, wu - 1) : 0u;
+            const uint32_t rank0 = base + before + lanes_below(m0[r]) + lanes_below(m1[r]);
+            const bool s0 = kv[r].x >= tau, s1 = kv[r].z >= tau;
+            const int32_t slot0 = int32_t(r * 2 * NT + tid * 2);
+            const uint32_t off0 = rank0 - uint32_t(r0);  // wraps for ranks below r0
+            const uint32_t off1 = off0 + (s0 ? 1u : 0u);
+            if (s0 && off0 < uint32_t(n)) {
+                s_slot[off0] = slot0;
+                s_tok[off0] = int32_t(kv[r].y);
+            }
+            if (s1 && off1 < uint32_t(n)) {
+                s_slot[off1] = slot0 + 1;
+                s_tok[off1] = int32_t(kv[r].w);
+            }
+            base += readlane_u32(x, NW - 1);
+        }
+        __syncthreads();
+        return res;
+    }
     // per-row counts of one thread are at most 2, two rows share a 32-bit word (16 bits each)
     constexpr int NP = ROWS / 2 > 0 ? ROWS / 2 : 1;
-    const bool take_all_eq = need >= eq_total;  // every key equal to tau is taken: select key >= tau
     uint32_t eq_base = 0, rank_base = 0;
     for (int t = 0; t < ntiles && rank_base < uint32_t(r0 + n); ++t) {
         if (t > 0) sel_load_tile<NT>(gk, kp, int64_t(t) * kSelTile, kv);
