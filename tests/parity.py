@@ -40,8 +40,9 @@ def assert_pool_equal(gpu_pool, orc_pool):
                              f"oracle-only {sorted(set(oi) - set(gi))[:10]}")
 
 
-def check_refine_unit(gpu_idx, gpu_out, gpu_lse, q_group, K, V, T_b, pool, kappa, agg, dtype, where=""):
-    """One unit: tie-banded index parity, then attention on the GPU's own selection."""
+def check_refine_unit(gpu_idx, gpu_out, gpu_lse, q_group, K, V, T_b, pool, kappa, agg, dtype, where="", exact=False):
+    """One unit: tie-banded index parity (identical sets when `exact`: scores that both sides
+    compute without rounding), then attention on the GPU's own selection."""
     r = oracle.refine_unit(q_group, K, V, T_b, pool, kappa, agg)
     gi = np.asarray(gpu_idx, dtype=np.int64)
     oi = r["idx"].astype(np.int64)
@@ -52,6 +53,7 @@ def check_refine_unit(gpu_idx, gpu_out, gpu_lse, q_group, K, V, T_b, pool, kappa
     gs, os_ = set(gi[:nv].tolist()), set(oi[:nv].tolist())
     assert gs <= valid_pool, f"{where}: idx not inside the pool"
     diff = gs ^ os_
+    assert not (exact and diff), f"{where}: idx differs from the oracle's: {sorted(diff)[:10]}"
     if diff:
         S_of = {int(t): r["S"][j] for j, t in enumerate(pool) if 0 <= t < T_b}
         Ssorted = sorted(S_of.values(), reverse=True)
@@ -74,7 +76,7 @@ def check_refine_unit(gpu_idx, gpu_out, gpu_lse, q_group, K, V, T_b, pool, kappa
     return len(diff)
 
 
-def check_refine_batch(idx, out, lse, q, K, V, lens, pool, kappa, agg, dtype, units=None):
+def check_refine_batch(idx, out, lse, q, K, V, lens, pool, kappa, agg, dtype, units=None, exact=False):
     """Every (or the listed) unit of a batched refine call."""
     Bn, Hkv = pool.shape[:2]
     G = q.shape[1] // Hkv
@@ -86,7 +88,7 @@ def check_refine_batch(idx, out, lse, q, K, V, lens, pool, kappa, agg, dtype, un
             h0 = g * G
             nties += check_refine_unit(idx[b, g], out[b, h0:h0 + G], None if lse is None else lse[b, h0:h0 + G],
                                        q[b, h0:h0 + G], K[b, g], V[b, g], int(lens[b]), pool[b, g], kappa, agg,
-                                       dtype, where=f"unit ({b},{g})")
+                                       dtype, where=f"unit ({b},{g})", exact=exact)
     return nties
 
 

@@ -27,7 +27,7 @@ def rnd(rng, shape, dtype):
     return W.bf16_round(x) if dtype == "bf16" else x
 
 
-def make_inputs(seed, Bn, Hq, Hkv, D, T, dtype, lens=None, ties=False, zero_q=False):
+def make_inputs(seed, Bn, Hq, Hkv, D, T, dtype, lens=None, ties=False, zero_q=False, clustered=False):
     rng = np.random.default_rng(seed)
     q = rnd(rng, (Bn, Hq, D), dtype)
     K = rnd(rng, (Bn, Hkv, T, D), dtype)
@@ -35,6 +35,16 @@ def make_inputs(seed, Bn, Hq, Hkv, D, T, dtype, lens=None, ties=False, zero_q=Fa
     if ties:
         proto = rnd(rng, (7, D), dtype)
         K[:] = proto[rng.integers(0, 7, size=(Bn, Hkv, T))]
+    if clustered:
+        # q.K = a + b / 256 per head with a in 1 + {0..15}/128 and b in 1 + {0..127}/128: 2048
+        # distinct scores inside one octave's eighth (two for G = 3), exact in bf16 products and
+        # fp32 sums, so both sides rank the same values; some tokens share a score
+        K[:] = 0.0
+        K[..., 0] = 1.0 + rng.integers(0, 16, size=(Bn, Hkv, T)) / 128.0
+        K[..., 1] = 1.0 + rng.integers(0, 128, size=(Bn, Hkv, T)) / 128.0
+        q[:] = 0.0
+        q[..., 0] = 1.0
+        q[..., 1] = 2.0 ** -8
     if zero_q:
         q[:] = 0.0
     lens = np.full(Bn, T, np.int32) if lens is None else np.asarray(lens, np.int32)
@@ -132,16 +142,22 @@ REFINE_CASES = [
     (64, 8, 1, PB.AGG_MAX, "bf16", 3000, 1000, 250, None),       # MAX across two lane groups
     (128, 16, 1, PB.AGG_MAX, "bf16", 3000, 1000, 250, None),     # MAX across four lane groups
     (64, 4, 1, PB.AGG_SUM, "bf16", 20000, 10000, 3000, None),    # pool above one 8192-slot tile
+    (128, 4, 1, PB.AGG_SUM, "bf16", 6000, 5000, 1000, None),     # one tile, clustered bin above 2048 keys
+    (64, 4, 1, PB.AGG_MAX, "f32", 2000, 450, 100, None),         # clustered bin of 450 keys
+    (128, 2, 1, PB.AGG_SUM, "bf16", 1000, 200, 50, None),        # clustered bin of 200 keys
 ]
 
 
 @pytest.mark.parametrize("case", REFINE_CASES, ids=lambda c: f"D{c[0]}G{c[1]}a{c[3]}{c[4]}kp{c[6]}k{c[7]}")
-@pytest.mark.parametrize("variant", ["random", "zero_q", "ties"])
+@pytest.mark.parametrize("variant", ["random", "zero_q", "ties", "clustered"])
 def test_refine_parity(case, variant):
+    """'clustered' puts the whole pool in one or two top-12-bit score bins with exact scores, so
+    the threshold is resolved from a long candidate list (direct counting up to 512 keys, the
+    8-bit sub-histogram up to 2048, radix digits beyond) and the index sets must be identical."""
     D, G, Hkv, agg, dtype, T, kp, kappa, lens = case
     Bn = len(lens) if lens else 1
     q, K, V, lens = make_inputs(seed_of(D, G, T, kp, kappa, variant), Bn, G * Hkv, Hkv, D, T, dtype, lens,
-                                zero_q=variant == "zero_q", ties=variant == "ties")
+                                zero_q=variant == "zero_q", ties=variant == "ties", clustered=variant == "clustered")
     rng = np.random.default_rng(kp + kappa)
     q0 = rnd(rng, q.shape, dtype)
     oKq, osc = oracle.quantize_rows(K)
@@ -150,7 +166,8 @@ def test_refine_parity(case, variant):
     out, idx, lse = PB.refine_attend(dev(q, dtype), dev(K, dtype), dev(V, dtype), torch.from_numpy(pool).cuda(),
                                      kappa, agg, seq_lens=ld)
     torch.cuda.synchronize()
-    check_refine_batch(idx.cpu().numpy(), host(out), lse.cpu().numpy(), q, K, V, lens, pool, kappa, agg, dtype)
+    check_refine_batch(idx.cpu().numpy(), host(out), lse.cpu().numpy(), q, K, V, lens, pool, kappa, agg, dtype,
+                       exact=variant == "clustered")
     if variant == "zero_q":  # every score ties: the lowest pool slots win
         gi = idx.cpu().numpy()
         for b in range(Bn):

@@ -377,13 +377,14 @@ __device__ __forceinline__ void softmax_v_rows(const T* __restrict__ Vu, const f
 }
 
 // Log-sum-exp merge of `np` partials (partial s at g_ml + s*GP*2, g_acc + s*GP*D), read at
-// device scope, eight partials per batch of independent loads.  Writes out[h][d] (dtype T) and
-// lse[h] (natural log) for h < G; np == 0 gives out = 0, lse = -inf.
+// device scope, sixteen partials per batch of independent loads: the batch's maximum first, then
+// every partial's weight on its own.  Writes out[h][d] (dtype T) and lse[h] (natural log) for
+// h < G; np == 0 gives out = 0, lse = -inf.
 template <typename T, int D, int GP, int NT = kThreads>
 __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, const float* __restrict__ g_acc, int np, int G,
                                T* __restrict__ out, float* __restrict__ lse) {
     constexpr float kLn2 = 0.6931471805599453f;
-    constexpr int BATCH = 8;
+    constexpr int BATCH = 16;
     for (int i = threadIdx.x; i < G * D; i += NT) {
         const int h = i / D, dd = i % D;
         float M = -INFINITY, L = 0.0f, acc = 0.0f;
@@ -397,17 +398,19 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, c
                 l[u] = ok ? ld_dev(&g_ml[(s * GP + h) * 2 + 1]) : 0.0f;
                 v[u] = ok ? ld_dev(&g_acc[(int64_t(s) * GP + h) * D + dd]) : 0.0f;
             }
+            float Mn = M;
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) Mn = fmaxf(Mn, m[u]);  // finite: the batch holds a partial
+            const float c_old = exp2_le0(M - Mn);
+            L *= c_old;
+            acc *= c_old;
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                if (s0 + u < np) {
-                    const float Mn = fmaxf(M, m[u]);
-                    const float c_old = exp2_le0(M - Mn);
-                    const float c_new = exp2_le0(m[u] - Mn);
-                    L = L * c_old + l[u] * c_new;
-                    acc = acc * c_old + v[u] * c_new;
-                    M = Mn;
-                }
+                const float c = exp2_le0(m[u] - Mn);  // 0 for the batch's unused entries
+                L = fmaf(l[u], c, L);
+                acc = fmaf(v[u], c, acc);
             }
+            M = Mn;
         }
         const bool empty = np == 0;
         store_elem<T>(&out[int64_t(h) * D + dd], empty ? 0.0f : acc / L);
