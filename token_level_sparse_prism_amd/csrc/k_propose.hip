@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
 // ---------------------------------------------------------------------------------------------
 // k_compact: grid (chunks, units).  Chunk 0 also writes the -1 padding and clears hist1.
 __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
-    __shared__ uint32_t s_tmp[kThreads / 64 * 3];
+    __shared__ uint32_t s_tmp[kThreads / 64 * 5];
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_hist[256];
     __shared__ uint2 s_few[kFewCand];  // candidates sharing tau's top 24 bits
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
     if (tid == 0) s_nfew = 0u;
     __syncthreads();
     uint32_t cgt = 0;
-    constexpr int CB = 8;  // candidate loads in flight per thread
+    constexpr int CB = 16;  // candidate loads in flight per thread
     for (uint32_t i0 = 0; i0 < cn; i0 += CB * 32) {
         uint2 e[CB];
 #pragma unroll
@@ -420,34 +420,31 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
             }
         }
     }
-    uint32_t v3[3] = {gt_before, cgt, ceq}, p3[3], t3[3];
-    block_excl_scan_n<3>(v3, p3, t3, s_tmp);
-    const uint32_t eq_before = t3[2];
-    const uint32_t offset = t3[0] + t3[1] + min(eq_before, need);
-
-    // ordered compaction of the chunk
-    uint32_t neq = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) neq += (tid * 4 + i < nvalid && k[i] == tau) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t eqr = eq_before + block_excl_scan(neq, s_tmp, &tot);
-    bool sel[4];
-    uint32_t nsel = 0;
+    // one workgroup scan gives the chunk's output offset and every thread's first output slot:
+    // the keys above tau before it plus the ties taken before it (ties go to the lowest tokens)
+    uint32_t ngt_t = 0, neq_t = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        bool s = false;
         if (tid * 4 + i < nvalid) {
-            if (k[i] > tau) s = true;
-            else if (k[i] == tau) { s = eqr < need; ++eqr; }
+            ngt_t += k[i] > tau ? 1u : 0u;
+            neq_t += k[i] == tau ? 1u : 0u;
         }
-        sel[i] = s;
-        nsel += s ? 1u : 0u;
     }
-    uint32_t pos = offset + block_excl_scan(nsel, s_tmp, &tot);
+    uint32_t v5[5] = {gt_before, cgt, ceq, ngt_t, neq_t}, p5[5], t5[5];
+    block_excl_scan_n<5>(v5, p5, t5, s_tmp);
+    const uint32_t eq_before = t5[2];                                  // ties in earlier chunks
+    const uint32_t eq_left = need > eq_before ? need - eq_before : 0u;  // ties still to take
+    uint32_t pos = t5[0] + t5[1] + min(eq_before, need) + p5[3] + min(p5[4], eq_left);
+    uint32_t eqr = p5[4];  // ties of this chunk before this thread's keys
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (sel[i] && pos < uint32_t(a.kp)) pool[pos] = int32_t(c0 + tid * 4 + i);
-        pos += sel[i] ? 1u : 0u;
+        bool sel = false;
+        if (tid * 4 + i < nvalid) {
+            if (k[i] > tau) sel = true;
+            else if (k[i] == tau) { sel = eqr < eq_left; ++eqr; }
+        }
+        if (sel && pos < uint32_t(a.kp)) pool[pos] = int32_t(c0 + tid * 4 + i);
+        pos += sel ? 1u : 0u;
     }
 }
 
