@@ -15,6 +15,7 @@ from .oracle import (  # noqa: F401
     propose_unit,
     quantize_query,
     quantize_rows,
+    quantize_rows_int2,
     refine,
     refine_unit,
 )

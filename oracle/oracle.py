@@ -35,6 +35,7 @@ def load():
         _build.build()
     lib = ctypes.CDLL(LIB_PATH)
     lib.orc_quantize_rows.argtypes = [_f32p, _i64, _int, _i8p, _f32p]
+    lib.orc_quantize_rows_int2.argtypes = [_f32p, _i64, _int, _i8p, _f32p]
     lib.orc_quantize_query.argtypes = [_f32p, _int, _int, _i8p, _f32p]
     lib.orc_propose_unit.argtypes = [_f32p, _int, _int, _i8p, _f32p, _i64, _i64, _int, _i32p, _f32p]
     lib.orc_refine_unit.argtypes = [_f32p, _int, _int, _f32p, _f32p, _i64, _i32p, _i64, _i64,
@@ -49,7 +50,7 @@ def load():
                                _i64, _i64, _int, ctypes.c_double, _i32p, _f64p, _f64p, _int]
     lib.orc_dense.argtypes = [_f32p, _int, _int, _int, _int, _f32p, _f32p, _i64, _i32p,
                               ctypes.c_double, _f64p, _f64p, _int]
-    for name in ("orc_quantize_rows", "orc_quantize_query", "orc_propose_unit", "orc_refine_unit",
+    for name in ("orc_quantize_rows", "orc_quantize_rows_int2", "orc_quantize_query", "orc_propose_unit", "orc_refine_unit",
                  "orc_attend_unit", "orc_dense_unit", "orc_propose", "orc_refine", "orc_dense",
                  "orc_max_threads"):
         getattr(lib, name).restype = ctypes.c_int
@@ -86,6 +87,20 @@ def quantize_rows(K):
     _check(load().orc_quantize_rows(_p(K, ctypes.c_float), n, D, _p(Kq, ctypes.c_int8),
                                     _p(s, ctypes.c_float)), "quantize_rows")
     return Kq, s
+
+
+def quantize_rows_int2(K):
+    """O1' (INT2 keys): per-row 2-bit codes. K [..., D] -> (levels int8 [..., D] in {-3,-1,1,3},
+    scales f32 [...]); K is reconstructed as scales[..., None] * levels.  Scoring these levels
+    with propose() is the INT2 proposal."""
+    K = _f32(K)
+    D = K.shape[-1]
+    n = K.size // D if D else 0
+    lv = np.empty(K.shape, dtype=np.int8)
+    s = np.empty(K.shape[:-1], dtype=np.float32)
+    _check(load().orc_quantize_rows_int2(_p(K, ctypes.c_float), n, D, _p(lv, ctypes.c_int8),
+                                         _p(s, ctypes.c_float)), "quantize_rows_int2")
+    return lv, s
 
 
 def quantize_query(q_group):

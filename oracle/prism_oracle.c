@@ -14,8 +14,10 @@
  *     following refined (shared) layer re-selects its own top-kappa inside
  *     that pool and attends to it.
  *   - Sec. 4.2: the proposal layer scores with a compressed key cache.  The
- *     page names INT2; this oracle implements the int8 per-token absmax
- *     scheme fixed for this library (readings R1/R2 below).
+ *     page names INT2 and prints no scheme; this oracle implements the int8
+ *     per-token absmax scheme fixed for this library (readings R1/R2 below)
+ *     and, as a second key format, a 2-bit per-token scheme (reading R1'
+ *     at orc_quantize_rows_int2).
  *   - Sec. 5.1 Implementation Details: pool size n = rho * kappa.
  *   - Sec. 1 and Sec. 2.1: token-level top-kappa sparse attention.
  * Every equation on the page is missing, so each step below states the
@@ -102,6 +104,52 @@ int orc_quantize_rows(const float* K, int64_t n_rows, int D, int8_t* Kq, float* 
 #pragma omp parallel for schedule(static) reduction(max : err)
     for (int64_t r = 0; r < n_rows; ++r) {
         int e = quantize_vector(K + r * D, D, Kq + r * D, &scales[r]);
+        if (e > err) err = e;
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step O1' (INT2 keys).  Sec. 4.2 says the proposal layer scores with a key  */
+/* cache compressed to INT2 but prints no scheme.  Reading R1': per token,   */
+/* the range [-amax, amax] is cut into four equal cells and each value is    */
+/* coded by the centre of its cell:                                          */
+/*   scale s = amax / 4 (exact);  u = K * (2 / amax) (one fp32 product,      */
+/*   2/amax correctly rounded);  c = 2 * floor(u) + 1 clamped to [-3, 3],    */
+/*   so c is in {-3, -1, +1, +3} and K is reconstructed as s * c.            */
+/* A value on a cell boundary (u an integer) takes the upper cell.  An       */
+/* all-zero row gives s = 0 and c = +1 everywhere (u = 0).  The codes are    */
+/* returned one per element as signed levels; scoring them is step O3 with   */
+/* these levels in place of the int8 codes.                                  */
+/* ------------------------------------------------------------------------ */
+static int quantize_vector_int2(const float* x, int64_t n, int8_t* codes, float* scale_out)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!isfinite(x[i])) return ORC_ERR_NONFINITE;
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    float inv = amax > 0.0f ? 2.0f / amax : 0.0f; /* fp32, correctly rounded */
+    for (int64_t i = 0; i < n; ++i) {
+        float u = x[i] * inv;                     /* one fp32 product */
+        float c = 2.0f * floorf(u) + 1.0f;        /* centre of the cell, in units of s */
+        if (c > 3.0f) c = 3.0f;
+        if (c < -3.0f) c = -3.0f;
+        codes[i] = (int8_t)c;
+    }
+    *scale_out = amax * 0.25f;
+    return ORC_OK;
+}
+
+/* O1' over a flat array of rows: K [n_rows][D] -> levels [n_rows][D] in {-3,-1,1,3}, scales. */
+int orc_quantize_rows_int2(const float* K, int64_t n_rows, int D, int8_t* levels, float* scales)
+{
+    if (!K || !levels || !scales || D <= 0 || n_rows < 0) return ORC_ERR_ARG;
+    int err = ORC_OK;
+#pragma omp parallel for schedule(static) reduction(max : err)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int e = quantize_vector_int2(K + r * D, D, levels + r * D, &scales[r]);
         if (e > err) err = e;
     }
     return err;

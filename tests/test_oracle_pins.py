@@ -100,6 +100,93 @@ def test_query_group_shares_one_scale():
     assert not qi[2].any()
 
 
+# ---------------------------------------------------------------- INT2 key quantizer (O1')
+# Sec. 4.2 names an INT2 key cache and prints no scheme; the reading is four equal cells over
+# [-amax, amax], coded by their centres: levels c in {-3, -1, 1, 3} times s = amax / 4.
+def test_int2_levels_bounds_and_extremes():
+    rng = np.random.default_rng(21)
+    K = rng.standard_normal((400, 128)).astype(np.float32)
+    K *= (10.0 ** rng.uniform(-6, 6, size=(400, 1))).astype(np.float32)
+    K[9] = 0.0
+    lv, s = oracle.quantize_rows_int2(K)
+    assert set(np.unique(lv).tolist()) <= {-3, -1, 1, 3}
+    assert s[9] == 0.0 and np.all(lv[9] == 1)  # u = 0 lies in the cell [0, 1)
+    for r in range(400):
+        if r == 9:
+            continue
+        amax = np.abs(K[r]).max()
+        assert s[r] == np.float32(amax) * np.float32(0.25)
+        j = int(np.argmax(np.abs(K[r])))
+        assert lv[r, j] == (3 if K[r, j] > 0 else -3)
+        # every value lies in its cell: |K - s c| <= half a cell = s (plus the rounding of 2/amax)
+        err = np.abs(K[r].astype(np.float64) - float(s[r]) * lv[r].astype(np.float64)).max()
+        assert err <= float(s[r]) * (1 + 1e-6)
+
+
+def test_int2_cell_boundaries_by_hand():
+    # amax = 2 makes 2/amax = 1 exactly, so u is the value itself: cells [-2,-1) [-1,0) [0,1) [1,2]
+    K = np.array([[2.0, -2.0, 0.0, 1.0, -1.0, 0.999, -0.001, 1.5, -1.5, 0.5]], dtype=np.float32)
+    lv, s = oracle.quantize_rows_int2(K)
+    assert lv[0].tolist() == [3, -3, 1, 3, -1, 1, -1, 3, -3, 1]
+    assert s[0] == 0.5
+
+
+def test_int2_monotone_symmetric_and_scale_free():
+    rng = np.random.default_rng(22)
+    K = rng.standard_normal((50, 256)).astype(np.float32)
+    lv, s = oracle.quantize_rows_int2(K)
+    for r in range(50):
+        o = np.argsort(K[r], kind="stable")
+        assert np.all(np.diff(lv[r, o].astype(int)) >= 0)  # a non-decreasing step function
+    lvn, sn = oracle.quantize_rows_int2(-K)
+    u = K * (np.float32(2.0) / np.abs(K).max(axis=1, keepdims=True))
+    interior = np.abs(u - np.round(u)) > 1e-4  # away from the cell edges
+    assert np.array_equal(lvn[interior], -lv[interior]) and np.array_equal(sn, s)
+    lv2, s2 = oracle.quantize_rows_int2(K * np.float32(2.0 ** 9))
+    assert np.array_equal(lv2, lv) and np.array_equal(s2, s * np.float32(2.0 ** 9))
+
+
+def test_int2_reconstruction_error_of_uniform_cells():
+    """Uniform values over [-amax, amax]: four equal cells coded at their centres give the
+    textbook mean squared error (cell width)^2 / 12 = (amax / 2)^2 / 12."""
+    rng = np.random.default_rng(23)
+    K = rng.uniform(-1.0, 1.0, size=(2000, 256)).astype(np.float32)
+    K[:, 0] = 1.0  # amax = 1 in every row
+    lv, s = oracle.quantize_rows_int2(K)
+    mse = np.mean((K[:, 1:].astype(np.float64) - s[:, None].astype(np.float64) * lv[:, 1:]) ** 2)
+    assert abs(mse / (0.25 / 12.0) - 1.0) < 0.01
+
+
+@pytest.mark.parametrize("G,agg", [(1, oracle.AGG_SUM), (4, oracle.AGG_SUM), (8, oracle.AGG_MAX)])
+def test_int2_pool_equals_repeated_argmax(G, agg):
+    """The INT2 proposal: scores of the levels (numpy integer matmul, one fp32 product with the
+    scale) and the pool by repeated argmax."""
+    rng = np.random.default_rng(24 + G)
+    D, T, kp = 64, 300, 37
+    q = rng.standard_normal((G, D)).astype(np.float32)
+    K = rng.standard_normal((T, D)).astype(np.float32)
+    K[5::7] = K[3]  # equal rows -> equal scores
+    lv, s = oracle.quantize_rows_int2(K)
+    qi, _ = oracle.quantize_query(q)
+    acc = qi.astype(np.int64) @ lv.astype(np.int64).T  # [G, T]
+    A = acc.sum(0) if agg == oracle.AGG_SUM else acc.max(0)
+    ref_scores = A.astype(np.float32) * s
+    ref_scores[ref_scores == 0] = 0.0
+    pool, scores = oracle.propose_unit(q, lv, s, T, kp, agg)
+    assert np.array_equal(scores, ref_scores)
+    assert pool.tolist() == pad(argmax_select(ref_scores.tolist(), kp), kp).tolist()
+
+
+def test_int2_planted_recovery_cfg1():
+    """P8 with INT2 proposal keys: the 16 planted tokens (K = 4 q) are all in the pool."""
+    c = W.CONFIGS["cfg1"]
+    w = W.generate(c)
+    lv, s = oracle.quantize_rows_int2(w.K[0])
+    pool = oracle.propose(w.q[0], lv, s, c.kp)
+    S0, _ = w.salient[(0, 0)]
+    assert np.isin(S0, pool[0, 0]).all()
+
+
 # ---------------------------------------------------------------- hand-derived example
 def test_hand_example():
     ex = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
