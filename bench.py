@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="time stream launches only (no HIP graph replay)")
+    p.add_argument("--no-int2", action="store_true",
+                   help="skip the second measurement of the same step with INT2 proposal keys")
     p.add_argument("--pmc-pass", action="store_true",
                    help="counter pass for rocprofv3 --pmc: --steps stream-launched steps, then one plain "
                         "copy of CALIB_BYTES as the counters' scale; no timing, no JSON line")
@@ -309,6 +311,70 @@ def main():
                 "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
                 "avg_launch_us": round(scan_us, 3) if scan_us else None}
 
+    # the same step with INT2 proposal keys (a second key format; the headline above is int8):
+    # stream-launched, same buffer rotation and workspaces, plus how its pools compare with int8's
+    int2 = None
+    if not args.no_int2:
+        K0 = dev(w.K[0])
+        Kq2, sc2 = PB.quantize_keys_int2(K0, seq_lens=lens_d)
+        del K0
+        steps2 = []
+        for j, s in enumerate(sets):
+            k2, c2 = (Kq2, sc2) if j == 0 else (Kq2.clone(), sc2.clone())
+            steps2.append(PrismStep(s["q0"], k2, c2, [LayerInputs(*L) for L in s["layers"]], cfg.kp, cfg.kappa,
+                                    seq_lens=lens_d, ws_propose=ws_p, ws_refine=ws_r, key_bits=2))
+        steps2[0]()
+        torch.cuda.synchronize()
+        pool2 = steps2[0].pool.cpu().numpy()
+        for i in range(args.warmup):
+            steps2[i % R]()
+        reps2 = sorted(timed(lambda i: steps2[i % R]())[0] for _ in range(args.repeats))
+        ms2 = float(np.median(reps2))
+        PB.profile_reset()
+        PB.profile_enable(True)
+        for i in range(args.profile_steps):
+            steps2[i % R]()
+        torch.cuda.synchronize()
+        PB.profile_enable(False)
+        k2us = {}
+        for k in PB.KERNELS:
+            n, ms = PB.profile_query(k)
+            if n:
+                k2us[k] = round(1000.0 * ms / n, 3)
+        PB.profile_reset()
+        ab2 = W.algorithmic_bytes(cfg, w.seq_lens, key_bits=2)
+        scan2_bytes = sum(int(w.seq_lens[b]) * (cfg.D // 4 + 4) + cfg.G * cfg.D * e
+                          for b in range(cfg.B) for _ in range(cfg.Hkv))
+        scan2_us = k2us.get("k_scan")
+        ach2 = scan2_bytes / (scan2_us * 1e-6) / 1e9 if scan2_us else None
+        # pool quality against the int8 pool: shared tokens, and the planted tokens each pool holds
+        shared, sal8, sal2, tgt8, tgt2, nunits = 0.0, 0.0, 0.0, 0.0, 0.0, 0
+        for b in range(cfg.B):
+            for g in range(cfg.Hkv):
+                p8, p2 = pool[b, g][pool[b, g] >= 0], pool2[b, g][pool2[b, g] >= 0]
+                shared += len(np.intersect1d(p8, p2)) / max(1, len(p8))
+                S0, Sl = w.salient[(b, g)]
+                tg = np.unique(np.concatenate(list(Sl)))
+                sal8 += np.isin(S0, p8).mean()
+                sal2 += np.isin(S0, p2).mean()
+                tgt8 += np.isin(tg, p8).mean()
+                tgt2 += np.isin(tg, p2).mean()
+                nunits += 1
+        int2 = {"ms_per_step": round(ms2, 5), "steps_per_s": round(1000.0 / ms2, 2),
+                "ms_per_step_p10": round(float(np.percentile(reps2, 10)), 5),
+                "ms_per_step_p90": round(float(np.percentile(reps2, 90)), 5), "launch": "stream",
+                "algorithmic_bytes_per_step": int(ab2["step"]),
+                "hbm_GBps": round(ab2["step"] / (ms2 * 1e-3) / 1e9, 1),
+                "kernels_us": k2us,
+                "scan_roofline": {"kernel": "k_scan (2-bit keys)", "bound": "hbm",
+                                  "achieved": round(ach2, 1) if ach2 else None, "peak": PEAK_HBM_GBPS,
+                                  "unit": "GB/s", "frac": round(ach2 / PEAK_HBM_GBPS, 4) if ach2 else None,
+                                  "algorithmic_bytes_per_launch": scan2_bytes},
+                "pool_shared_with_int8": round(shared / nunits, 4),
+                "anchor_salient_in_pool": {"int8": round(sal8 / nunits, 4), "int2": round(sal2 / nunits, 4)},
+                "refined_salient_in_pool": {"int8": round(tgt8 / nunits, 4), "int2": round(tgt2 / nunits, 4)}}
+        del steps2, Kq2, sc2
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -350,6 +416,7 @@ def main():
         "ms_per_step_by_launch": {m: round(v, 5) for m, v in med.items()},
         "ms_per_step_warm": round(ms_warm, 5),
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
+        "int2_keys": int2,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3), "gen_s": round(gen_s, 1),
     }

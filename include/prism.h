@@ -20,6 +20,7 @@
  *      q          [B][Hq][D]            dtype (fp32 or bf16)
  *      K, V       [B][Hkv][T_max][D]    dtype
  *      Kq         [B][Hkv][T_max][D]    int8
+ *      Kq2        [B][Hkv][T_max][D/4]  uint8 (four 2-bit codes per byte)
  *      scales     [B][Hkv][T_max]       fp32
  *      pool       [B][Hkv][kp]          int32
  *      idx        [B][Hkv][kappa]       int32
@@ -85,7 +86,8 @@ prism_status prism_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Key-cache compression for proposal scoring (Sec. 4.2 "Quantized Proposal
- * Construction"; the page names INT2, this library uses int8).  For every
+ * Construction"; the page names INT2: this int8 format is the library's main
+ * one, prism_quantize_keys_int2 below gives a 2-bit format).  For every
  * (b, g, t < T_b): amax = max_d |K|; scale = amax / 127 (fp32, correctly
  * rounded); codes = clamp(rint(K * (127 / amax)), -127, 127) with one fp32
  * product and round-half-to-even; an all-zero row gives scale 0 and codes 0.
@@ -111,6 +113,34 @@ prism_status prism_quantize_keys(const void* K, prism_dtype dt, const prism_shap
 prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, const float* scales,
                            const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool,
                            float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * INT2 key cache for proposal scoring (Sec. 4.2 compresses the proposal
+ * layer's key cache to INT2 and prints no scheme; this is the library's
+ * reading).  For every (b, g, t < T_b): amax = max_d |K|; scale = amax / 4
+ * (exact); u = K * (2 / amax) (one fp32 product, the reciprocal correctly
+ * rounded); level c = clamp(2 * floor(u) + 1, -3, 3) in {-3, -1, +1, +3}, so
+ * [-amax, amax] is cut into four equal cells coded by their centres and K is
+ * reconstructed as scale * c.  A value on a cell edge takes the upper cell;
+ * an all-zero row gives scale 0 and c = +1.  Storage: 2-bit codes
+ * b = (c + 3) / 2, D/4 bytes per row; 32-bit word w of a row (little endian)
+ * holds dims 16w .. 16w + 15, dim 16w + 4j + i in bits 8i + 2j .. 8i + 2j + 1.
+ * Rows t >= T_b are not written.  In: K (dtype).  Out: Kq2
+ * [B][Hkv][T_max][D/4] bytes (16-byte aligned), scales [B][Hkv][T_max] fp32.
+ */
+prism_status prism_quantize_keys_int2(const void* K, prism_dtype dt, const prism_shape* s,
+                                      uint8_t* Kq2, float* scales, void* stream);
+
+/*
+ * Proposal layer over the INT2 key cache: prism_propose with the levels c of
+ * prism_quantize_keys_int2 in place of the int8 codes, i.e.
+ * A[t] = sum (SUM) or max (MAX) over heads of the int32 dot products
+ * qi[h] . c[t], score[t] = float(A[t]) * scales[t], and the same pool rule.
+ * Same arguments, outputs, workspace and errors as prism_propose.
+ */
+prism_status prism_propose_int2(const void* q, prism_dtype qdt, const uint8_t* Kq2, const float* scales,
+                                const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool,
+                                float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Refined layer (Sec. 4.1: the refined layer re-selects its own top-kappa

@@ -29,6 +29,18 @@ def f32_bits(a):
     return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
 
 
+def unpack_int2(Kq2, D):
+    """Levels {-3,-1,1,3} [..., D] of packed 2-bit keys [..., D/4] bytes: 32-bit word w of a row
+    (little endian) holds dim 16w + 4j + i in bits 8i + 2j .. 8i + 2j + 1, code b, level 2b - 3."""
+    a = np.ascontiguousarray(Kq2, dtype=np.uint8)
+    words = a.reshape(a.shape[:-1] + (D // 16, 4)).view(np.uint32)[..., 0]  # [..., D/16]
+    out = np.empty(a.shape[:-1] + (D // 16, 4, 4), dtype=np.int8)  # [..., w, j, i]
+    for j in range(4):
+        for i in range(4):
+            out[..., j, i] = ((words >> (8 * i + 2 * j)) & 3).astype(np.int8) * 2 - 3
+    return out.reshape(a.shape[:-1] + (D,))
+
+
 def assert_pool_equal(gpu_pool, orc_pool):
     g, o = np.asarray(gpu_pool), np.asarray(orc_pool)
     assert g.shape == o.shape

@@ -27,13 +27,13 @@ def lib():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(prism_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(prism_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("prism_propose", "prism_refine_attend", "prism_dense_ref", "prism_quantize_keys",
-                 "prism_workspace_bytes", "prism_workspace_init"):
+                 "prism_quantize_keys_int2", "prism_propose_int2", "prism_workspace_bytes", "prism_workspace_init"):
         assert name in fns
 
 
@@ -94,5 +94,16 @@ def test_invalid_arguments_return_before_device_work(lib):
     r = lib.prism_dense_ref(f(256), f(256), f(256), 1, ctypes.byref(s), 0.0, f(256), None, f(256), 16, None)
     assert r == 3
     assert lib.prism_quantize_keys(None, 1, ctypes.byref(s), f(256), f(256), None) == 1
+    # INT2 proposal: same validation as the int8 one
+    def p2(kp=64, kq=256, s_=s):
+        return lib.prism_propose_int2(f(256), 1, f(kq), f(256), ctypes.byref(s_), kp, 0, f(256), None, f(256),
+                                      1 << 40, None)
+    assert p2(kp=0) == 1
+    assert p2(kq=0) == 1
+    assert p2(kq=256 + 4) == 1                                    # misaligned codes
+    assert p2(s_=shape(D=96, T=4096)) == 2
+    assert lib.prism_quantize_keys_int2(None, 1, ctypes.byref(s), f(256), f(256), None) == 1
+    assert lib.prism_quantize_keys_int2(f(256), 1, ctypes.byref(s), f(256 + 8), f(256), None) == 1
+    assert lib.prism_quantize_keys_int2(f(256), 1, ctypes.byref(shape(D=32, T=64)), f(256), f(256), None) == 2
     assert lib.prism_workspace_init(f(128), 1024, None) == 1
     assert lib.prism_status_str(3) == b"PRISM_ERR_WORKSPACE"

@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import oracle
-from tests.parity import (assert_pool_equal, check_dense_batch, check_refine_batch, dev, f32_bits, host)
+from tests.parity import (assert_pool_equal, check_dense_batch, check_refine_batch, dev, f32_bits, host,
+                          unpack_int2)
 from token_level_sparse_prism_amd import binding as PB
 from token_level_sparse_prism_amd import workload as W
 
@@ -112,6 +113,46 @@ def test_propose_bitexact(case, variant):
     assert_pool_equal(pool.cpu().numpy(), opool)
 
 
+# ------------------------------------------------------------------------------- INT2 proposal
+@pytest.mark.parametrize("D,dtype,T,lens", [(128, "f32", 3000, None), (64, "bf16", 3000, [3000, 1777]),
+                                            (256, "bf16", 2500, [0, 2500]), (128, "bf16", 5000, None)])
+def test_quantize_keys_int2_bitexact(D, dtype, T, lens):
+    q, K, V, lens = make_inputs(D + T + 1, 2 if lens else 1, 4, 2, D, T, dtype, lens)
+    K[0, 0, 5] = 0.0                    # an all-zero row
+    K[0, 1, 7, :16] = 0.0               # values on the cell edge u = 0
+    Kd = dev(K, dtype)
+    ld = torch.from_numpy(lens).cuda()
+    Kq2, sc = PB.quantize_keys_int2(Kd, seq_lens=ld)
+    torch.cuda.synchronize()
+    lv = unpack_int2(Kq2.cpu().numpy(), D)
+    sc = sc.cpu().numpy()
+    for b in range(K.shape[0]):
+        n = lens[b]
+        olv, osc = oracle.quantize_rows_int2(K[b, :, :n])
+        assert np.array_equal(lv[b, :, :n], olv)
+        assert np.array_equal(f32_bits(sc[b, :, :n]), f32_bits(osc))
+
+
+@pytest.mark.parametrize("case", PROPOSE_CASES, ids=lambda c: f"D{c[0]}G{c[1]}a{c[3]}{c[4]}T{c[5]}kp{c[6]}")
+@pytest.mark.parametrize("variant", ["random", "ties", "zero_q"])
+def test_propose_int2_bitexact(case, variant):
+    D, G, Hkv, agg, dtype, T, kp, lens = case
+    Bn = len(lens) if lens else 1
+    q, K, V, lens = make_inputs(seed_of(D, G, T, kp, variant, 2), Bn, G * Hkv, Hkv, D, T, dtype, lens,
+                                ties=variant == "ties", zero_q=variant == "zero_q")
+    ld = torch.from_numpy(lens).cuda()
+    Kq2, sc = PB.quantize_keys_int2(dev(K, dtype), seq_lens=ld)
+    scores = torch.zeros((Bn, Hkv, T), dtype=torch.float32, device="cuda")
+    pool = PB.propose_int2(dev(q, dtype), Kq2, sc, kp, agg, seq_lens=ld, scores=scores)
+    torch.cuda.synchronize()
+    olv, osc = oracle.quantize_rows_int2(K)
+    opool, oscores = oracle.propose(q, olv, osc, kp, seq_lens=lens, agg=agg, want_scores=True)
+    gs = scores.cpu().numpy()
+    for b in range(Bn):
+        assert np.array_equal(f32_bits(gs[b, :, :lens[b]]), f32_bits(oscores[b, :, :lens[b]])), "scores differ"
+    assert_pool_equal(pool.cpu().numpy(), opool)
+
+
 def test_propose_large_candidate_set():
     """Every score equal over 262144 tokens: the threshold bin holds the whole context."""
     D, T, kp = 64, 262144, 65536
@@ -203,14 +244,15 @@ def test_dense_parity(D, G, dtype, T, lens):
 
 
 # ------------------------------------------------------------------------------------- whole steps
-def run_step_gpu(w, kp, kappa, agg=PB.AGG_SUM):
+def run_step_gpu(w, kp, kappa, agg=PB.AGG_SUM, key_bits=8):
     from token_level_sparse_prism_amd.step import LayerInputs, PrismStep
     c = w.cfg
     ld = torch.from_numpy(w.seq_lens).cuda()
-    Kq, sc = PB.quantize_keys(dev(w.K[0], c.dtype), seq_lens=ld)
+    quant = PB.quantize_keys_int2 if key_bits == 2 else PB.quantize_keys
+    Kq, sc = quant(dev(w.K[0], c.dtype), seq_lens=ld)
     layers = [LayerInputs(dev(w.q[l], c.dtype), dev(w.K[l], c.dtype), dev(w.V[l], c.dtype))
               for l in range(1, w.layers)]
-    step = PrismStep(dev(w.q[0], c.dtype), Kq, sc, layers, kp, kappa, agg, seq_lens=ld)
+    step = PrismStep(dev(w.q[0], c.dtype), Kq, sc, layers, kp, kappa, agg, seq_lens=ld, key_bits=key_bits)
     pool, idx, out, lse = step()
     torch.cuda.synchronize()
     return step, Kq, sc
@@ -274,6 +316,27 @@ def test_full_size_128k_sampled_units():
             assert set(gidx[0, g].tolist()) <= set(gpool[0, g].tolist())
         check_refine_batch(gidx, host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(), w.q[l], w.K[l], w.V[l],
                            w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype, units={(0, 0), (0, 5)})
+
+
+def test_full_size_128k_int2():
+    """The 128K-context workload with INT2 proposal keys: the packed codes and scales, every
+    unit's pool bit for bit, two units' refined layers in full, and the anchor's unshifted planted
+    tokens in every pool."""
+    c = W.CONFIGS["cfg3"]
+    w = W.generate(c)
+    step, Kq2, sc = run_step_gpu(w, c.kp, c.kappa, key_bits=2)
+    olv, osc = oracle.quantize_rows_int2(w.K[0])
+    assert np.array_equal(unpack_int2(Kq2.cpu().numpy(), c.D), olv)
+    assert np.array_equal(f32_bits(sc.cpu().numpy()), f32_bits(osc))
+    opool = oracle.propose(w.q[0], olv, osc, c.kp, seq_lens=w.seq_lens)
+    gpool = step.pool.cpu().numpy()
+    assert_pool_equal(gpool, opool)
+    for g in range(c.Hkv):
+        assert np.isin(w.salient[(0, g)][0], gpool[0, g]).all()
+    for l in range(1, w.layers):
+        check_refine_batch(step.idx[l - 1].cpu().numpy(), host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(),
+                           w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype,
+                           units={(0, 1), (0, 6)})
 
 
 def test_graph_replay_matches_eager():

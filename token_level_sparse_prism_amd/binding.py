@@ -19,9 +19,10 @@ OP_PROPOSE, OP_REFINE, OP_DENSE = 0, 1, 2
 STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_INVALID_ARG", 2: "PRISM_ERR_UNSUPPORTED",
           3: "PRISM_ERR_WORKSPACE", 4: "PRISM_ERR_HIP"}
 EXPORTS = ("prism_workspace_bytes", "prism_workspace_init", "prism_quantize_keys", "prism_propose",
+           "prism_quantize_keys_int2", "prism_propose_int2",
            "prism_refine_attend", "prism_dense_ref", "prism_profile_enable", "prism_profile_query",
            "prism_profile_reset", "prism_last_hip_error", "prism_status_str")
-KERNELS = ("k_quantize_keys", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense")
+KERNELS = ("k_quantize_keys", "k_quantize_keys_int2", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense")
 
 
 class PrismError(RuntimeError):
@@ -54,11 +55,15 @@ def load():
     lib.prism_quantize_keys.argtypes = [_vp, ctypes.c_int, sp, _vp, _vp, _vp]
     lib.prism_propose.argtypes = [_vp, ctypes.c_int, _vp, _vp, sp, ctypes.c_int32, ctypes.c_int, _vp, _vp,
                                   _vp, ctypes.c_size_t, _vp]
+    lib.prism_quantize_keys_int2.argtypes = [_vp, ctypes.c_int, sp, _vp, _vp, _vp]
+    lib.prism_propose_int2.argtypes = [_vp, ctypes.c_int, _vp, _vp, sp, ctypes.c_int32, ctypes.c_int, _vp, _vp,
+                                       _vp, ctypes.c_size_t, _vp]
     lib.prism_refine_attend.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, _vp, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.prism_dense_ref.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, ctypes.c_float, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp]
-    for fn in ("prism_workspace_init", "prism_quantize_keys", "prism_propose", "prism_refine_attend",
+    for fn in ("prism_workspace_init", "prism_quantize_keys", "prism_propose", "prism_quantize_keys_int2",
+               "prism_propose_int2", "prism_refine_attend",
                "prism_dense_ref", "prism_last_hip_error"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.prism_profile_enable.argtypes = [ctypes.c_int]
@@ -101,10 +106,13 @@ def _need(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be a contiguous device tensor")
 
 
-def make_shape(q: torch.Tensor, K: torch.Tensor, seq_lens: Optional[torch.Tensor] = None) -> Shape:
+def make_shape(q: torch.Tensor, K: torch.Tensor, seq_lens: Optional[torch.Tensor] = None,
+               k_cols_per_dim: int = 1) -> Shape:
+    """k_cols_per_dim: K's last dimension per head-dim element (1, or 1/4 for packed 2-bit keys
+    given as 4)."""
     B, Hq, D = q.shape
     B2, Hkv, T_max, D2 = K.shape
-    if B != B2 or D != D2:
+    if B != B2 or D != D2 * k_cols_per_dim:
         raise ValueError("q [B,Hq,D] and K [B,Hkv,T_max,D] disagree")
     if seq_lens is not None:
         _need(seq_lens, "seq_lens")
@@ -158,6 +166,39 @@ def propose(q: torch.Tensor, Kq: torch.Tensor, scales: torch.Tensor, kp: int, ag
     _check("prism_propose", load().prism_propose(_ptr(q), _dtype_code(q), _ptr(Kq), _ptr(scales),
                                                  ctypes.byref(shape), kp, agg, _ptr(pool), _ptr(scores),
                                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return pool
+
+
+def quantize_keys_int2(K: torch.Tensor, seq_lens: Optional[torch.Tensor] = None, Kq2: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """INT2 key cache: returns (Kq2 [B,Hkv,T_max,D/4] uint8, four 2-bit codes per byte; scales)."""
+    _need(K, "K")
+    B, Hkv, T_max, D = K.shape
+    q_dummy = torch.empty((B, Hkv, D), device=K.device, dtype=K.dtype)
+    shape = make_shape(q_dummy, K, seq_lens)
+    if Kq2 is None:
+        Kq2 = torch.zeros((B, Hkv, T_max, D // 4), dtype=torch.uint8, device=K.device)
+    if scales is None:
+        scales = torch.zeros((B, Hkv, T_max), dtype=torch.float32, device=K.device)
+    _check("prism_quantize_keys_int2", load().prism_quantize_keys_int2(_ptr(K), _dtype_code(K), ctypes.byref(shape),
+                                                                       _ptr(Kq2), _ptr(scales), _stream(stream)))
+    return Kq2, scales
+
+
+def propose_int2(q: torch.Tensor, Kq2: torch.Tensor, scales: torch.Tensor, kp: int, agg: int = AGG_SUM,
+                 seq_lens: Optional[torch.Tensor] = None, pool: Optional[torch.Tensor] = None,
+                 scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """Proposal layer over the INT2 key cache: returns pool [B,Hkv,kp] int32."""
+    for t, n in ((q, "q"), (Kq2, "Kq2"), (scales, "scales")):
+        _need(t, n)
+    shape = make_shape(q, Kq2, seq_lens, k_cols_per_dim=4)
+    if pool is None:
+        pool = torch.empty((shape.B, shape.Hkv, kp), dtype=torch.int32, device=q.device)
+    if ws is None:
+        ws = new_workspace(OP_PROPOSE, shape, kp, 0, device=q.device, stream=stream)
+    _check("prism_propose_int2", load().prism_propose_int2(_ptr(q), _dtype_code(q), _ptr(Kq2), _ptr(scales),
+                                                           ctypes.byref(shape), kp, agg, _ptr(pool), _ptr(scores),
+                                                           _ptr(ws), ws.numel(), _stream(stream)))
     return pool
 
 

@@ -3,9 +3,9 @@
 // Sec. 4.2: the scoring uses the compressed key cache; Sec. 5.1: pool size n = rho * kappa).
 //
 // Three launches per call, none of which waits on another workgroup:
-//   k_scan     streams the int8 keys once (the HBM-bound pass), writes a 32-bit order key per
-//              token and adds each workgroup's histogram of the keys' top 12 bits into the unit's
-//              histogram (hist1).
+//   k_scan     streams the compressed keys once (the HBM-bound pass: int8 codes, or the 2-bit
+//              INT2 codes), writes a 32-bit order key per token and adds each workgroup's
+//              histogram of the keys' top 12 bits into the unit's histogram (hist1).
 //   k_cand     (per 1024-token chunk) finds from hist1 the bin that holds the kp-th largest key,
 //              counts the chunk's keys above that bin, appends the keys inside it to the unit's
 //              candidate list and histograms their bits 19..8 (hist2).
@@ -33,15 +33,77 @@ __device__ __forceinline__ int chunk_tokens(int64_t Tb, int64_t c0) {
 //   agg SUM, G  > 1: NQ = 2, the group's code sums split as qsum = 16*hi + lo with lo in
 //                    [-8, 7] and |hi| <= 127, so A = 16*(hi.K) + lo.K exactly in int32;
 //   agg MAX:         NQ = GP (G rounded up to a power of two), one vector per head.
-// A lane holds 16 bytes of a key row (D/16 lanes per token); a wave reads 1 KiB of
-// consecutive rows per load.  Workgroup x of unit y handles chunks x, x + gridDim.x, ...
-template <int D, int NQ, bool kMax>
+// A lane covers DPL dims of a key row (D/DPL lanes per token) and loads them as one piece per
+// row: 16 bytes of int8 codes (DPL = 16, a wave reads 1 KiB of consecutive rows per load), or
+// for 2-bit codes 16 bytes (DPL = 64, when at most two query vectors hold registers) or one
+// 32-bit word (DPL = 16, agg MAX).  A 2-bit code b stands for the level c = 2b - 3, so a lane's
+// share of q.c is 2 (q.b) - 3 (sum of its q codes), exact in int32; q.b over one 32-bit word is
+// four byte-wise dot products of its bit pairs.  Workgroup x of unit y handles chunks
+// x, x + gridDim.x, ...
+template <int KB, int DPL> struct ScanRow;
+template <> struct ScanRow<8, 16> {
+    using R = uint4;
+    static constexpr int kLoads = 8;  // loads in flight per lane
+    static __device__ __forceinline__ R load(const int8_t* p) { return load16_stream(p); }
+    static __device__ __forceinline__ R zero() { return make_uint4(0u, 0u, 0u, 0u); }
+};
+template <> struct ScanRow<2, 64> {
+    using R = uint4;
+    static constexpr int kLoads = 4;  // the q words take the registers of the other four
+    static __device__ __forceinline__ R load(const int8_t* p) { return load16_stream(p); }
+    static __device__ __forceinline__ R zero() { return make_uint4(0u, 0u, 0u, 0u); }
+};
+template <> struct ScanRow<2, 16> {
+    using R = uint32_t;
+    static constexpr int kLoads = 32;
+    static __device__ __forceinline__ R load(const int8_t* p) {
+        return uint32_t(__builtin_nontemporal_load(reinterpret_cast<const int*>(p)));
+    }
+    static __device__ __forceinline__ R zero() { return 0u; }
+};
+
+// The lane's contribution to q_n . key for one row: qw = the lane's q words of vector n (four
+// per 16 dims), c3 = -3 * (sum of the lane's q codes) for 2-bit keys.
+__device__ __forceinline__ int dot_2bit_word(const int* qw, uint32_t w, int acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(qw[j], int((w >> (2 * j)) & 0x03030303u), acc, false);
+    return acc;
+}
+template <int KB>
+__device__ __forceinline__ int lane_dot(const int* qw, uint4 k, int c3) {
+    if constexpr (KB == 8) {
+        int acc = 0;
+        acc = __builtin_amdgcn_sdot4(qw[0], int(k.x), acc, false);
+        acc = __builtin_amdgcn_sdot4(qw[1], int(k.y), acc, false);
+        acc = __builtin_amdgcn_sdot4(qw[2], int(k.z), acc, false);
+        acc = __builtin_amdgcn_sdot4(qw[3], int(k.w), acc, false);
+        return acc;
+    } else {
+        int acc = dot_2bit_word(qw, k.x, 0);
+        acc = dot_2bit_word(qw + 4, k.y, acc);
+        acc = dot_2bit_word(qw + 8, k.z, acc);
+        acc = dot_2bit_word(qw + 12, k.w, acc);
+        return 2 * acc + c3;
+    }
+}
+template <int KB>
+__device__ __forceinline__ int lane_dot(const int* qw, uint32_t w, int c3) {
+    return 2 * dot_2bit_word(qw, w, 0) + c3;
+}
+
+template <int D, int NQ, bool kMax, int KB>
 __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
-    constexpr int LPT = D / 16;            // lanes per token
+    constexpr int DPL = (KB == 2 && NQ <= 2) ? 64 : 16;  // dims per lane
+    using SR = ScanRow<KB, DPL>;
+    constexpr int QW = DPL / 4;            // q words per vector and lane
+    constexpr int LPT = D / DPL;           // lanes per token
     constexpr int TPW = 64 / LPT;          // tokens per wave per load
     constexpr int TPR = TPW * (kThreads / 64);
     constexpr int ROUNDS = kChunk / TPR;
-    constexpr int U = 8;                   // loads in flight per lane
+    // loads in flight per lane: fewer 2-bit row words when many query vectors hold registers
+    constexpr int UW = KB == 8 ? SR::kLoads : (NQ <= 2 ? SR::kLoads : (NQ <= 8 ? SR::kLoads / 2 : SR::kLoads / 4));
+    constexpr int U = UW < ROUNDS ? UW : ROUNDS;
+    constexpr int RB = D * KB / 8;         // bytes per key row
     static_assert(ROUNDS % U == 0, "chunk must hold whole unrolled rounds");
 
     __shared__ uint32_t s_hist[kHistBins];
@@ -95,10 +157,10 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     }
     // rolling buffer of U rows per lane: a register is refilled with the row U rounds ahead as
     // soon as it has been used, so about U loads stay in flight through the whole chunk
-    uint4 kv[U];
-    const int8_t* krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * D + sub * 16;  // this lane's first row
-    auto load_row = [&](int r) -> uint4 {
-        return r * TPR + tok_lane < nvalid ? load16_stream(krow + r * (TPR * D)) : make_uint4(0, 0, 0, 0);
+    typename SR::R kv[U];
+    const int8_t* krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * RB + sub * (RB / LPT);  // this lane's first row
+    auto load_row = [&](int r) -> typename SR::R {
+        return r * TPR + tok_lane < nvalid ? SR::load(krow + r * (TPR * RB)) : SR::zero();
     };
 #pragma unroll
     for (int u = 0; u < U; ++u) kv[u] = load_row(u);
@@ -141,11 +203,19 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         }
     }
     __syncthreads();
-    int qv[NQ][4];
+    int qv[NQ][QW];
+    int c3[NQ];  // 2-bit keys: -3 * (sum of the lane's q codes) per vector
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * 16]);
-        qv[n][0] = int(w.x); qv[n][1] = int(w.y); qv[n][2] = int(w.z); qv[n][3] = int(w.w);
+        int qs = 0;
+#pragma unroll
+        for (int m = 0; m < QW / 4; ++m) {
+            const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * DPL + 16 * m]);
+            qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
+        }
+#pragma unroll
+        for (int i = 0; i < QW; ++i) qs = __builtin_amdgcn_sdot4(qv[n][i], 0x01010101, qs, false);
+        c3[n] = -3 * qs;
     }
     for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;  // q is in registers now
 #pragma unroll
@@ -157,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         if (!first) {
             c0 = int64_t(chunk) * kChunk;
             nvalid = chunk_tokens(Tb, c0);
-            krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * D + sub * 16;
+            krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * RB + sub * (RB / LPT);
         }
         if (nvalid == 0) break;  // later chunks of this workgroup are past T_b too
         if (!first) {
@@ -177,31 +247,19 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int tok = (r0 + u) * TPR + tok_lane;
-                const int k4[4] = {int(kv[u].x), int(kv[u].y), int(kv[u].z), int(kv[u].w)};
                 int A;
                 if constexpr (kMax) {
                     int best = 0;
 #pragma unroll
                     for (int h = 0; h < NQ; ++h) {
-                        int acc = 0;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_sdot4(qv[h][i], k4[i], acc, false);
-                        acc = group_sum_i<LPT>(acc);
+                        const int acc = group_sum_i<LPT>(lane_dot<KB>(qv[h], kv[u], c3[h]));
                         if (h < G) best = (h == 0 || acc > best) ? acc : best;
                     }
                     A = best;
                 } else {
-                    int acc0 = 0;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc0 = __builtin_amdgcn_sdot4(qv[0][i], k4[i], acc0, false);
-                    if constexpr (NQ == 2) {
-                        int acc1 = 0;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc1 = __builtin_amdgcn_sdot4(qv[1][i], k4[i], acc1, false);
-                        acc0 = acc0 * 16 + acc1;
-                    }
-                    acc0 = group_sum_i<LPT>(acc0);
-                    A = acc0;
+                    int acc0 = lane_dot<KB>(qv[0], kv[u], c3[0]);
+                    if constexpr (NQ == 2) acc0 = acc0 * 16 + lane_dot<KB>(qv[1], kv[u], c3[1]);
+                    A = group_sum_i<LPT>(acc0);
                 }
                 if (sub == 0 && tok < nvalid) {
                     const float score = float(A) * s_scale[tok];  // one fp32 product
@@ -449,19 +507,19 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D>
+template <int D, int KB>
 static hipError_t launch_scan(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
     const int G = a.d.G;
     if (!agg_max) {
-        if (G == 1) launch_k("k_scan", (k_scan<D, 1, false>), grid, dim3(kThreads), st, a);
-        else launch_k("k_scan", (k_scan<D, 2, false>), grid, dim3(kThreads), st, a);
+        if (G == 1) launch_k("k_scan", (k_scan<D, 1, false, KB>), grid, dim3(kThreads), st, a);
+        else launch_k("k_scan", (k_scan<D, 2, false, KB>), grid, dim3(kThreads), st, a);
     } else {
         switch (padded_g(G)) {
-            case 1: launch_k("k_scan", (k_scan<D, 1, true>), grid, dim3(kThreads), st, a); break;
-            case 2: launch_k("k_scan", (k_scan<D, 2, true>), grid, dim3(kThreads), st, a); break;
-            case 4: launch_k("k_scan", (k_scan<D, 4, true>), grid, dim3(kThreads), st, a); break;
-            case 8: launch_k("k_scan", (k_scan<D, 8, true>), grid, dim3(kThreads), st, a); break;
-            case 16: launch_k("k_scan", (k_scan<D, 16, true>), grid, dim3(kThreads), st, a); break;
+            case 1: launch_k("k_scan", (k_scan<D, 1, true, KB>), grid, dim3(kThreads), st, a); break;
+            case 2: launch_k("k_scan", (k_scan<D, 2, true, KB>), grid, dim3(kThreads), st, a); break;
+            case 4: launch_k("k_scan", (k_scan<D, 4, true, KB>), grid, dim3(kThreads), st, a); break;
+            case 8: launch_k("k_scan", (k_scan<D, 8, true, KB>), grid, dim3(kThreads), st, a); break;
+            case 16: launch_k("k_scan", (k_scan<D, 16, true, KB>), grid, dim3(kThreads), st, a); break;
             default: return hipErrorInvalidValue;
         }
     }
@@ -475,10 +533,11 @@ hipError_t launch_propose(const ProposeArgs& a, int agg_max, hipStream_t st) {
     per_unit = per_unit < 1 ? 1 : (per_unit > a.nchunks ? a.nchunks : per_unit);
     const dim3 sgrid(per_unit, units);
     hipError_t e;
+    const bool two = a.key_bits == 2;
     switch (a.d.D) {
-        case 64: e = launch_scan<64>(a, agg_max, sgrid, st); break;
-        case 128: e = launch_scan<128>(a, agg_max, sgrid, st); break;
-        case 256: e = launch_scan<256>(a, agg_max, sgrid, st); break;
+        case 64: e = two ? launch_scan<64, 2>(a, agg_max, sgrid, st) : launch_scan<64, 8>(a, agg_max, sgrid, st); break;
+        case 128: e = two ? launch_scan<128, 2>(a, agg_max, sgrid, st) : launch_scan<128, 8>(a, agg_max, sgrid, st); break;
+        case 256: e = two ? launch_scan<256, 2>(a, agg_max, sgrid, st) : launch_scan<256, 8>(a, agg_max, sgrid, st); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

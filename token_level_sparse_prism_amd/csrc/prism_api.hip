@@ -87,9 +87,9 @@ prism_status prism_quantize_keys(const void* K, prism_dtype dt, const prism_shap
     return hip_status(launch_quantize_keys(K, dt == PRISM_BF16, d, Kq, scales, static_cast<hipStream_t>(stream)));
 }
 
-prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, const float* scales,
-                           const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool, float* scores,
-                           void* ws, size_t ws_bytes, void* stream) {
+static prism_status propose_impl(const void* q, prism_dtype qdt, const void* Kq, int key_bits, const float* scales,
+                                 const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool, float* scores,
+                                 void* ws, size_t ws_bytes, void* stream) {
     prism_status st = check_shape(s);
     if (st != PRISM_OK) return st;
     if (!valid_dtype(qdt) || !valid_agg(agg) || kp < 1) return PRISM_ERR_INVALID_ARG;
@@ -105,7 +105,8 @@ prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, con
     a.d = dims_of(s);
     a.q = q;
     a.q_bf16 = qdt == PRISM_BF16;
-    a.Kq = Kq;
+    a.Kq = static_cast<const int8_t*>(Kq);
+    a.key_bits = key_bits;
     a.scales = scales;
     a.kp = kp;
     a.nchunks = int((s->T_max + kChunk - 1) / kChunk);
@@ -121,6 +122,29 @@ prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, con
     a.cand = reinterpret_cast<uint2*>(carve(ws, L.cand));
     a.cand_cap = cand_list_cap(s->T_max);
     return hip_status(launch_propose(a, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream)));
+}
+
+prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, const float* scales,
+                           const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool, float* scores,
+                           void* ws, size_t ws_bytes, void* stream) {
+    return propose_impl(q, qdt, Kq, 8, scales, s, kp, agg, pool, scores, ws, ws_bytes, stream);
+}
+
+prism_status prism_quantize_keys_int2(const void* K, prism_dtype dt, const prism_shape* s, uint8_t* Kq2,
+                                      float* scales, void* stream) {
+    prism_status st = check_shape(s);
+    if (st != PRISM_OK) return st;
+    if (!valid_dtype(dt)) return PRISM_ERR_INVALID_ARG;
+    if (!K || !Kq2 || !scales) return PRISM_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Kq2, 16) || !aligned(scales, 4)) return PRISM_ERR_INVALID_ARG;
+    const Dims d = dims_of(s);
+    return hip_status(launch_quantize_keys_int2(K, dt == PRISM_BF16, d, Kq2, scales, static_cast<hipStream_t>(stream)));
+}
+
+prism_status prism_propose_int2(const void* q, prism_dtype qdt, const uint8_t* Kq2, const float* scales,
+                                const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool, float* scores,
+                                void* ws, size_t ws_bytes, void* stream) {
+    return propose_impl(q, qdt, Kq2, 2, scales, s, kp, agg, pool, scores, ws, ws_bytes, stream);
 }
 
 prism_status prism_refine_attend(const void* q, const void* K, const void* V, prism_dtype dt,

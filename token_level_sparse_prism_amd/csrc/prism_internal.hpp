@@ -119,7 +119,8 @@ struct ProposeArgs {
     Dims d;
     const void* q;
     int q_bf16;
-    const int8_t* Kq;
+    const int8_t* Kq;       // int8 codes [U][T_max][D], or 2-bit codes [U][T_max][D/4] bytes
+    int key_bits;           // 8 or 2
     const float* scales;
     int32_t kp;
     int nchunks;
@@ -169,6 +170,8 @@ struct DenseArgs {
 };
 
 // ---- launchers (defined in the kernel files) ----------------------------------------------
+hipError_t launch_quantize_keys_int2(const void* K, int bf16, const Dims& d, uint8_t* Kq2, float* scales,
+                                     hipStream_t st);
 hipError_t launch_quantize_keys(const void* K, int bf16, const Dims& d, int8_t* Kq, float* scales,
                                 hipStream_t st);
 hipError_t launch_propose(const ProposeArgs& a, int agg_max, hipStream_t st);

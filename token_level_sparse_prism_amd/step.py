@@ -21,19 +21,23 @@ class LayerInputs:
 
 
 class PrismStep:
-    """Proposal on layer 0 (int8 keys Kq/scales), then refine_attend on layers 1..L."""
+    """Proposal on layer 0 (compressed keys Kq/scales: int8 codes, or with key_bits=2 the packed
+    INT2 codes of quantize_keys_int2), then refine_attend on layers 1..L."""
 
     def __init__(self, q0: torch.Tensor, Kq: torch.Tensor, scales: torch.Tensor, refined: List[LayerInputs],
                  kp: int, kappa: int, agg: int = B.AGG_SUM, seq_lens: Optional[torch.Tensor] = None,
                  want_lse: bool = True, stream=None, ws_propose: Optional[torch.Tensor] = None,
-                 ws_refine: Optional[torch.Tensor] = None):
+                 ws_refine: Optional[torch.Tensor] = None, key_bits: int = 8):
+        if key_bits not in (8, 2):
+            raise ValueError("key_bits must be 8 or 2")
+        self.key_bits = key_bits
         self.q0, self.Kq, self.scales = q0, Kq, scales
         self.refined = refined
         self.kp, self.kappa, self.agg = kp, kappa, agg
         self.seq_lens = seq_lens
         self.stream = stream
         dev = q0.device
-        shape = B.make_shape(q0, Kq, seq_lens)
+        shape = B.make_shape(q0, Kq, seq_lens, k_cols_per_dim=4 if key_bits == 2 else 1)
         Bn, Hkv = shape.B, shape.Hkv
         self.pool = torch.empty((Bn, Hkv, kp), dtype=torch.int32, device=dev)
         # workspaces may be shared by steps that run one after another on the same stream
@@ -49,8 +53,9 @@ class PrismStep:
                     for L in refined]
 
     def propose(self):
-        return B.propose(self.q0, self.Kq, self.scales, self.kp, self.agg, seq_lens=self.seq_lens, pool=self.pool,
-                         ws=self.ws_p, stream=self.stream)
+        fn = B.propose_int2 if self.key_bits == 2 else B.propose
+        return fn(self.q0, self.Kq, self.scales, self.kp, self.agg, seq_lens=self.seq_lens, pool=self.pool,
+                  ws=self.ws_p, stream=self.stream)
 
     def refine(self, i: int):
         L = self.refined[i]

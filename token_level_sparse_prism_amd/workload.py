@@ -315,9 +315,10 @@ def generate(cfg: Config, layers: Optional[Sequence[int]] = None, threads: int =
     return Workload(cfg=cfg, seq_lens=lens, q=qs, K=Ks, V=Vs, salient=sal)
 
 
-def algorithmic_bytes(cfg: Config, seq_lens: Optional[np.ndarray] = None) -> Dict[str, float]:
+def algorithmic_bytes(cfg: Config, seq_lens: Optional[np.ndarray] = None, key_bits: int = 8) -> Dict[str, float]:
     """Bytes the method must move per decode step (proposal + each refined layer), per unit:
-    propose = T_b*D (int8 keys) + 4*T_b (scales) + G*D*e (query) + 4*kp (pool write)
+    propose = T_b*D*key_bits/8 (compressed keys: int8, or 2-bit) + 4*T_b (scales) + G*D*e (query)
+              + 4*kp (pool write)
     refine  = 4*kp (pool) + kp*D*e (gathered K rows) + kappa*D*e (gathered V rows)
               + 2*G*D*e (query in, output out) + 4*kappa (index write)
     where kp and kappa are capped by T_b as the method caps them."""
@@ -330,6 +331,6 @@ def algorithmic_bytes(cfg: Config, seq_lens: Optional[np.ndarray] = None) -> Dic
         kp_e = min(cfg.kp, T_b)
         ka_e = min(cfg.kappa, kp_e)
         for _ in range(cfg.Hkv):
-            prop += T_b * cfg.D + 4 * T_b + cfg.G * cfg.D * e + 4 * cfg.kp
+            prop += T_b * cfg.D * key_bits // 8 + 4 * T_b + cfg.G * cfg.D * e + 4 * cfg.kp
             ref += 4 * cfg.kp + kp_e * cfg.D * e + ka_e * cfg.D * e + 2 * cfg.G * cfg.D * e + 4 * cfg.kappa
     return {"propose": prop, "refine_per_layer": ref, "step": prop + cfg.n_refined * ref}
