@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time stream launches only (no HIP graph replay)")
     p.add_argument("--no-int2", action="store_true",
                    help="skip the second measurement of the same step with INT2 proposal keys")
+    p.add_argument("--page-size", type=int, default=64,
+                   help="page size of the paged-cache measurement of the same step (0 = skip it)")
     p.add_argument("--pmc-pass", action="store_true",
                    help="counter pass for rocprofv3 --pmc: --steps stream-launched steps, then one plain "
                         "copy of CALIB_BYTES as the counters' scale; no timing, no JSON line")
@@ -375,6 +377,68 @@ def main():
                 "refined_salient_in_pool": {"int8": round(tgt8 / nunits, 4), "int2": round(tgt2 / nunits, 4)}}
         del steps2, Kq2, sc2
 
+    # the same step on paged caches: every sequence's pages shuffled through one pool per KV head
+    paged = None
+    if args.page_size > 0:
+        P = args.page_size
+        max_pages = -(-cfg.T // P)
+        n_pages = cfg.B * max_pages + 7
+        g = torch.Generator().manual_seed(1234)
+        table = torch.randperm(n_pages, generator=g)[:cfg.B * max_pages].reshape(cfg.B, max_pages).to(torch.int32)
+        slots = n_pages * P
+        rows = [(table[b][:, None] * P + torch.arange(P)[None, :]).reshape(-1)[:cfg.T].cuda() for b in range(cfg.B)]
+        tab_d = table.cuda()
+
+        def to_pool(X):  # [B, Hkv, T, ...] -> [Hkv, slots, ...]
+            out = torch.zeros((X.shape[1], slots) + tuple(X.shape[3:]), dtype=X.dtype, device=X.device)
+            for b in range(cfg.B):
+                out[:, rows[b]] = X[b]
+            return out
+
+        def one_set(s):
+            return (s["q0"], to_pool(s["Kq"]), to_pool(s["sc"]),
+                    [(L[0], to_pool(L[1]), to_pool(L[2])) for L in s["layers"]])
+        psets = [one_set(s) for s in sets]
+        torch.cuda.synchronize()
+        pws_p = PB.new_workspace(PB.OP_PROPOSE, PB.make_shape(psets[0][0], base["Kq"], lens_d), cfg.kp)
+        pws_r = ws_r
+        ppool = torch.empty((cfg.B, cfg.Hkv, cfg.kp), dtype=torch.int32, device="cuda")
+        pidx = [torch.empty((cfg.B, cfg.Hkv, cfg.kappa), dtype=torch.int32, device="cuda") for _ in range(cfg.n_refined)]
+        pout = [torch.empty((cfg.B, cfg.Hq, cfg.D), dtype=dt, device="cuda") for _ in range(cfg.n_refined)]
+        plse = [torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device="cuda") for _ in range(cfg.n_refined)]
+
+        def pstep(i):
+            q0, kqp, scp, lay = psets[i % R]
+            PB.propose_paged(q0, kqp, scp, tab_d, P, cfg.kp, T_max=cfg.T, seq_lens=lens_d, pool=ppool, ws=pws_p)
+            for l, (qq, kk, vv) in enumerate(lay):
+                PB.refine_attend_paged(qq, kk, vv, tab_d, P, ppool, cfg.kappa, T_max=cfg.T, seq_lens=lens_d,
+                                       out=pout[l], idx=pidx[l], lse=plse[l], ws=pws_r)
+        pstep(0)
+        torch.cuda.synchronize()
+        assert torch.equal(ppool.cpu(), torch.from_numpy(pool)), "paged and contiguous pools differ"
+        for i in range(args.warmup):
+            pstep(i)
+        repsp = sorted(timed(pstep)[0] for _ in range(args.repeats))
+        msp = float(np.median(repsp))
+        PB.profile_reset()
+        PB.profile_enable(True)
+        for i in range(args.profile_steps):
+            pstep(i)
+        torch.cuda.synchronize()
+        PB.profile_enable(False)
+        kpus = {}
+        for k in PB.KERNELS:
+            n, ms = PB.profile_query(k)
+            if n:
+                kpus[k] = round(1000.0 * ms / n, 3)
+        PB.profile_reset()
+        paged = {"page_size": P, "pages_per_sequence": max_pages, "ms_per_step": round(msp, 5),
+                 "steps_per_s": round(1000.0 / msp, 2), "launch": "stream",
+                 "ms_per_step_p10": round(float(np.percentile(repsp, 10)), 5),
+                 "ms_per_step_p90": round(float(np.percentile(repsp, 90)), 5),
+                 "vs_contiguous_stream": round(msp / med["stream"], 4), "kernels_us": kpus}
+        del psets
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -417,6 +481,7 @@ def main():
         "ms_per_step_warm": round(ms_warm, 5),
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
         "int2_keys": int2,
+        "paged_kv": paged,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3), "gen_s": round(gen_s, 1),
     }

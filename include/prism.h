@@ -166,6 +166,46 @@ prism_status prism_refine_attend(const void* q, const void* K, const void* V, pr
                                  void* stream);
 
 /*
+ * Paged caches (a serving layout: sequences of different lengths share one
+ * pool of fixed-size pages).  Each KV head g owns a pool of num_slots rows;
+ * token t of sequence b is stored in row
+ *     g * num_slots + page_table[b * max_pages + t / page_size] * page_size
+ *       + t % page_size
+ * of every per-row cache (K, V, int8 or 2-bit keys, scales), i.e. the pools
+ * are [Hkv][num_slots][D] (K, V: dtype; Kq: int8; Kq2: D/4 bytes) and
+ * [Hkv][num_slots] (scales).  page_size is a power of two (1 .. 2^20, 1 is
+ * a per-token map); max_pages * page_size >= T_max; num_slots is a multiple
+ * of page_size (at most 2^23, else PRISM_ERR_UNSUPPORTED).  Page ids outside [0, num_slots/page_size)
+ * are clamped into the pool (a wrong row is read, nothing outside the pool).
+ * The key quantizers are per row, so a pool is compressed by
+ * prism_quantize_keys[_int2] with shape {B = 1, Hkv, T_max = num_slots}.
+ * Pools, index sets, scores and outputs keep logical token ids and the
+ * layouts above; seq_lens works as before.  Results equal those of the same
+ * call on contiguous caches holding the same rows, bit for bit.
+ */
+typedef struct prism_paging {
+    const int32_t* page_table; /* device [B][max_pages], physical page ids */
+    int32_t max_pages;
+    int32_t page_size;
+    int64_t num_slots;
+} prism_paging;
+
+/* prism_propose (key_bits 8) or prism_propose_int2 (key_bits 2) over paged
+ * key pools.  Same outputs, workspace and errors; an invalid paging
+ * descriptor or key_bits gives PRISM_ERR_INVALID_ARG. */
+prism_status prism_propose_paged(const void* q, prism_dtype qdt, const void* Kq_pool, int32_t key_bits,
+                                 const float* scales_pool, const prism_shape* s, const prism_paging* paging,
+                                 int32_t kp, prism_agg agg, int32_t* pool, float* scores, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* prism_refine_attend over paged K and V pools (same outputs, workspace and
+ * errors). */
+prism_status prism_refine_attend_paged(const void* q, const void* K_pool, const void* V_pool, prism_dtype dt,
+                                       const prism_shape* s, const prism_paging* paging, const int32_t* pool,
+                                       int32_t kp, int32_t kappa, prism_agg agg, float sm_scale, void* out,
+                                       int32_t* idx, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dense decode attention over every t < T_b (the kappa = kp = T_b special
  * case of the refined layer): out[h] = softmax(q[h] . K[0..T_b) * sm_scale)
  * . V[0..T_b), lse as above.  A reference and a baseline, not part of the

@@ -33,7 +33,8 @@ def header_functions():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for name in ("prism_propose", "prism_refine_attend", "prism_dense_ref", "prism_quantize_keys",
-                 "prism_quantize_keys_int2", "prism_propose_int2", "prism_workspace_bytes", "prism_workspace_init"):
+                 "prism_quantize_keys_int2", "prism_propose_int2", "prism_propose_paged", "prism_refine_attend_paged",
+                 "prism_workspace_bytes", "prism_workspace_init"):
         assert name in fns
 
 
@@ -105,5 +106,20 @@ def test_invalid_arguments_return_before_device_work(lib):
     assert lib.prism_quantize_keys_int2(None, 1, ctypes.byref(s), f(256), f(256), None) == 1
     assert lib.prism_quantize_keys_int2(f(256), 1, ctypes.byref(s), f(256 + 8), f(256), None) == 1
     assert lib.prism_quantize_keys_int2(f(256), 1, ctypes.byref(shape(D=32, T=64)), f(256), f(256), None) == 2
+    # paged calls: the page descriptor is checked before any launch
+    def pp(pg, kb=8):
+        return lib.prism_propose_paged(f(256), 1, f(256), kb, f(256), ctypes.byref(s), ctypes.byref(pg) if pg else None,
+                                       64, 0, f(256), None, f(256), 1 << 40, None)
+    good = B.Paging(256, 64, 64, 64 * 64)      # 64 pages of 64 tokens cover T_max = 4096
+    assert pp(None) == 1
+    assert pp(B.Paging(0, 64, 64, 4096)) == 1          # no table
+    assert pp(B.Paging(256, 64, 48, 4096)) == 1        # page size not a power of two
+    assert pp(B.Paging(256, 32, 64, 4096)) == 1        # table covers 2048 < T_max tokens
+    assert pp(B.Paging(256, 64, 64, 4000)) == 1        # pool not a whole number of pages
+    assert pp(B.Paging(258, 64, 64, 4096)) == 1        # misaligned table
+    assert pp(good, kb=4) == 1                         # key bits
+    r = lib.prism_refine_attend_paged(f(256), f(256), f(256), 1, ctypes.byref(s), ctypes.byref(B.Paging(256, 64, 0, 4096)),
+                                      f(256), 64, 16, 0, 0.0, f(256), f(256), None, f(256), 1 << 40, None)
+    assert r == 1                                      # page size 0
     assert lib.prism_workspace_init(f(128), 1024, None) == 1
     assert lib.prism_status_str(3) == b"PRISM_ERR_WORKSPACE"

@@ -243,6 +243,73 @@ def test_dense_parity(D, G, dtype, T, lens):
     check_dense_batch(host(out), lse.cpu().numpy(), q, K, V, lens, dtype)
 
 
+# ------------------------------------------------------------------------------------- paged caches
+def to_pages(X, P, rng, spare=3):
+    """Logical [B, Hkv, T_max, ...] -> (pool [Hkv, S, ...], page table [B, max_pages] int32): every
+    logical page of every sequence gets its own physical page, in shuffled order, with spare pages
+    (zero) in between."""
+    B, Hkv, T_max = X.shape[:3]
+    max_pages = -(-T_max // P)
+    n_pages = B * max_pages + spare
+    table = rng.permutation(n_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    pool = np.zeros((Hkv, n_pages * P) + X.shape[3:], dtype=X.dtype)
+    for b in range(B):
+        for p in range(max_pages):
+            t0, t1 = p * P, min((p + 1) * P, T_max)
+            pool[:, table[b, p] * P: table[b, p] * P + (t1 - t0)] = X[b, :, t0:t1]
+    return pool, table
+
+
+PAGED_CASES = [
+    # D, G, Hkv, agg, dtype, T, kp, kappa, lens, page size
+    (128, 4, 2, PB.AGG_SUM, "bf16", 5000, 2048, 512, [5000, 3333], 16),
+    (64, 8, 1, PB.AGG_SUM, "f32", 3000, 1000, 300, None, 1),
+    (256, 1, 2, PB.AGG_MAX, "bf16", 2000, 700, 200, [0, 2000], 64),
+    (128, 3, 2, PB.AGG_SUM, "bf16", 2600, 1200, 333, [2600, 77], 4096),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: f"D{c[0]}G{c[1]}a{c[3]}{c[4]}P{c[9]}")
+@pytest.mark.parametrize("key_bits", [8, 2])
+def test_paged_matches_contiguous(case, key_bits):
+    """The paged calls on shuffled page pools give the contiguous calls' pools, scores, index sets,
+    outputs and lse bit for bit, and the pools equal the oracle's."""
+    D, G, Hkv, agg, dtype, T, kp, kappa, lens, P = case
+    Bn = len(lens) if lens else 1
+    q, K, V, lens = make_inputs(seed_of(D, G, T, P, key_bits), Bn, G * Hkv, Hkv, D, T, dtype, lens)
+    rng = np.random.default_rng(P + key_bits)
+    Kp, table = to_pages(K, P, rng)
+    Vp, table2 = to_pages(V, P, np.random.default_rng(P + key_bits))
+    assert np.array_equal(table, table2)
+    ld = torch.from_numpy(lens).cuda()
+    tab = torch.from_numpy(table).cuda()
+    quant = PB.quantize_keys_int2 if key_bits == 2 else PB.quantize_keys
+    qd = dev(q, dtype)
+    # contiguous reference run
+    Kq, sc = quant(dev(K, dtype), seq_lens=ld)
+    prop = PB.propose_int2 if key_bits == 2 else PB.propose
+    sc_c = torch.zeros((Bn, Hkv, T), dtype=torch.float32, device="cuda")
+    pool_c = prop(qd, Kq, sc, kp, agg, seq_lens=ld, scores=sc_c)
+    out_c, idx_c, lse_c = PB.refine_attend(qd, dev(K, dtype), dev(V, dtype), pool_c, kappa, agg, seq_lens=ld)
+    # paged run: the pools are compressed as one [1, Hkv, S] cache
+    Kq_p, sc_p = quant(dev(Kp, dtype)[None])
+    sc_g = torch.zeros((Bn, Hkv, T), dtype=torch.float32, device="cuda")
+    pool_p = PB.propose_paged(qd, Kq_p[0], sc_p[0], tab, P, kp, agg, key_bits=key_bits, T_max=T, seq_lens=ld,
+                              scores=sc_g)
+    out_p, idx_p, lse_p = PB.refine_attend_paged(qd, dev(Kp, dtype), dev(Vp, dtype), tab, P, pool_p, kappa, agg,
+                                                 T_max=T, seq_lens=ld)
+    torch.cuda.synchronize()
+    assert torch.equal(pool_p, pool_c)
+    for b in range(Bn):
+        n = int(lens[b])
+        assert torch.equal(sc_g[b, :, :n], sc_c[b, :, :n])
+    assert torch.equal(idx_p, idx_c)
+    assert torch.equal(out_p, out_c)
+    assert torch.equal(lse_p, lse_c)
+    lv, osc = (oracle.quantize_rows_int2 if key_bits == 2 else oracle.quantize_rows)(K)
+    assert_pool_equal(pool_p.cpu().numpy(), oracle.propose(q, lv, osc, kp, seq_lens=lens, agg=agg))
+
+
 # ------------------------------------------------------------------------------------- whole steps
 def run_step_gpu(w, kp, kappa, agg=PB.AGG_SUM, key_bits=8):
     from token_level_sparse_prism_amd.step import LayerInputs, PrismStep

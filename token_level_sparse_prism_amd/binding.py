@@ -19,7 +19,7 @@ OP_PROPOSE, OP_REFINE, OP_DENSE = 0, 1, 2
 STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_INVALID_ARG", 2: "PRISM_ERR_UNSUPPORTED",
           3: "PRISM_ERR_WORKSPACE", 4: "PRISM_ERR_HIP"}
 EXPORTS = ("prism_workspace_bytes", "prism_workspace_init", "prism_quantize_keys", "prism_propose",
-           "prism_quantize_keys_int2", "prism_propose_int2",
+           "prism_quantize_keys_int2", "prism_propose_int2", "prism_propose_paged", "prism_refine_attend_paged",
            "prism_refine_attend", "prism_dense_ref", "prism_profile_enable", "prism_profile_query",
            "prism_profile_reset", "prism_last_hip_error", "prism_status_str")
 KERNELS = ("k_quantize_keys", "k_quantize_keys_int2", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense")
@@ -34,6 +34,11 @@ class PrismError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("D", ctypes.c_int32), ("T_max", ctypes.c_int64), ("seq_lens", ctypes.c_void_p)]
+
+
+class Paging(ctypes.Structure):
+    _fields_ = [("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_slots", ctypes.c_int64)]
 
 
 _lib = None
@@ -58,12 +63,18 @@ def load():
     lib.prism_quantize_keys_int2.argtypes = [_vp, ctypes.c_int, sp, _vp, _vp, _vp]
     lib.prism_propose_int2.argtypes = [_vp, ctypes.c_int, _vp, _vp, sp, ctypes.c_int32, ctypes.c_int, _vp, _vp,
                                        _vp, ctypes.c_size_t, _vp]
+    pgp = ctypes.POINTER(Paging)
+    lib.prism_propose_paged.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int32, _vp, sp, pgp, ctypes.c_int32,
+                                        ctypes.c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.prism_refine_attend_paged.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, pgp, _vp, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                              ctypes.c_size_t, _vp]
     lib.prism_refine_attend.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, _vp, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.prism_dense_ref.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, ctypes.c_float, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp]
     for fn in ("prism_workspace_init", "prism_quantize_keys", "prism_propose", "prism_quantize_keys_int2",
-               "prism_propose_int2", "prism_refine_attend",
+               "prism_propose_int2", "prism_propose_paged", "prism_refine_attend_paged", "prism_refine_attend",
                "prism_dense_ref", "prism_last_hip_error"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.prism_profile_enable.argtypes = [ctypes.c_int]
@@ -225,6 +236,72 @@ def refine_attend(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool: torch
     _check("prism_refine_attend", load().prism_refine_attend(
         _ptr(q), _ptr(K), _ptr(V), _dtype_code(q), ctypes.byref(shape), _ptr(pool), kp, kappa, agg,
         float(sm_scale), _ptr(out), _ptr(idx), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, idx, lse
+
+
+def _paged_shape(q: torch.Tensor, pool_rows: torch.Tensor, page_table: torch.Tensor, page_size: int,
+                 T_max: Optional[int], seq_lens: Optional[torch.Tensor]) -> Tuple[Shape, Paging]:
+    """Shape and page descriptor of a paged call: pools are [Hkv][num_slots][...]; T_max defaults to
+    the table's capacity max_pages * page_size."""
+    _need(page_table, "page_table")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2:
+        raise ValueError("page_table must be int32 [B, max_pages]")
+    B, Hq, D = q.shape
+    Hkv, num_slots = pool_rows.shape[0], pool_rows.shape[1]
+    if page_table.shape[0] != B:
+        raise ValueError("page_table must have one row per sequence")
+    T = int(T_max) if T_max is not None else page_table.shape[1] * page_size
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens")
+        if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+            raise ValueError("seq_lens must be int32 [B]")
+    shape = Shape(B, Hq, Hkv, D, T, None if seq_lens is None else seq_lens.data_ptr())
+    return shape, Paging(page_table.data_ptr(), page_table.shape[1], int(page_size), int(num_slots))
+
+
+def propose_paged(q: torch.Tensor, Kq_pool: torch.Tensor, scales_pool: torch.Tensor, page_table: torch.Tensor,
+                  page_size: int, kp: int, agg: int = AGG_SUM, key_bits: int = 8, T_max: Optional[int] = None,
+                  seq_lens: Optional[torch.Tensor] = None, pool: Optional[torch.Tensor] = None,
+                  scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """Proposal layer over paged key pools (Kq_pool [Hkv, num_slots, D] int8, or [Hkv, num_slots, D/4]
+    uint8 with key_bits=2; scales_pool [Hkv, num_slots]): returns pool [B,Hkv,kp] int32."""
+    for t, n in ((q, "q"), (Kq_pool, "Kq_pool"), (scales_pool, "scales_pool")):
+        _need(t, n)
+    shape, pg = _paged_shape(q, Kq_pool, page_table, page_size, T_max, seq_lens)
+    if pool is None:
+        pool = torch.empty((shape.B, shape.Hkv, kp), dtype=torch.int32, device=q.device)
+    if ws is None:
+        ws = new_workspace(OP_PROPOSE, shape, kp, 0, device=q.device, stream=stream)
+    _check("prism_propose_paged", load().prism_propose_paged(
+        _ptr(q), _dtype_code(q), _ptr(Kq_pool), int(key_bits), _ptr(scales_pool), ctypes.byref(shape),
+        ctypes.byref(pg), kp, agg, _ptr(pool), _ptr(scores), _ptr(ws), ws.numel(), _stream(stream)))
+    return pool
+
+
+def refine_attend_paged(q: torch.Tensor, K_pool: torch.Tensor, V_pool: torch.Tensor, page_table: torch.Tensor,
+                        page_size: int, pool: torch.Tensor, kappa: int, agg: int = AGG_SUM, sm_scale: float = 0.0,
+                        T_max: Optional[int] = None, seq_lens: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                        ws: Optional[torch.Tensor] = None, stream=None):
+    """Refined layer over paged K / V pools [Hkv, num_slots, D]: returns (out, idx, lse)."""
+    for t, n in ((q, "q"), (K_pool, "K_pool"), (V_pool, "V_pool"), (pool, "pool")):
+        _need(t, n)
+    if not (q.dtype == K_pool.dtype == V_pool.dtype):
+        raise TypeError("q, K and V must share one dtype")
+    shape, pg = _paged_shape(q, K_pool, page_table, page_size, T_max, seq_lens)
+    kp = pool.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    if idx is None:
+        idx = torch.empty((shape.B, shape.Hkv, kappa), dtype=torch.int32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((shape.B, shape.Hq), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = new_workspace(OP_REFINE, shape, kp, kappa, device=q.device, stream=stream)
+    _check("prism_refine_attend_paged", load().prism_refine_attend_paged(
+        _ptr(q), _ptr(K_pool), _ptr(V_pool), _dtype_code(q), ctypes.byref(shape), ctypes.byref(pg), _ptr(pool),
+        kp, kappa, agg, float(sm_scale), _ptr(out), _ptr(idx), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
     return out, idx, lse
 
 

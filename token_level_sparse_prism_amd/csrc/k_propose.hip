@@ -91,7 +91,7 @@ __device__ __forceinline__ int lane_dot(const int* qw, uint32_t w, int c3) {
     return 2 * dot_2bit_word(qw, w, 0) + c3;
 }
 
-template <int D, int NQ, bool kMax, int KB>
+template <int D, int NQ, bool kMax, int KB, bool kPaged>
 __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     constexpr int DPL = (KB == 2 && NQ <= 2) ? 64 : 16;  // dims per lane
     using SR = ScanRow<KB, DPL>;
@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     __shared__ float s_scale[kChunk];
     __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
     __shared__ float s_red[kThreads / 64];
+    __shared__ int32_t s_pg[kPaged ? kChunk : 1];  // paged: the physical pages of the chunk's tokens
 
     const Dims& d = a.d;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -146,13 +147,37 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     int chunk = ui.x;
     int64_t c0 = int64_t(chunk) * kChunk;
     int nvalid = chunk < a.nchunks ? chunk_tokens(Tb, c0) : 0;
+    constexpr bool paged = kPaged;  // rows through the page table (d.pg.table != nullptr)
+    // paged: the chunk's page ids go to LDS once (clamped into the pool), and a row of the chunk is
+    // found there; pg0 = the chunk's first page, lp = log2 of the page size
+    const int lp = d.pg.log2p;
+    const int64_t npool = d.pg.slots >> lp;
+    auto fill_pages = [&](int64_t cc0, int nv) {
+        const int64_t p0 = cc0 >> lp;
+        const int npg = nv > 0 ? int(((cc0 + nv - 1) >> lp) - p0 + 1) : 0;
+        for (int i = tid; i < npg; i += kThreads) {
+            int64_t pg = d.pg.table[int64_t(b) * d.pg.max_pages + p0 + i];
+            s_pg[i] = int32_t(pg < 0 ? 0 : (pg >= npool ? npool - 1 : pg));
+        }
+    };
+    // the row of token t of the current chunk inside KV head g's pool (< 2^23, so 32-bit offsets)
+    auto paged_slot = [&](int64_t t) -> uint32_t {
+        return (uint32_t(s_pg[(t >> lp) - (c0 >> lp)]) << lp) + uint32_t(t & ((int64_t(1) << lp) - 1));
+    };
+    const int8_t* kq_head = a.Kq + int64_t(g) * d.pg.slots * RB;
+    const float* sc_head = a.scales + int64_t(g) * d.pg.slots;
+    if constexpr (paged) {
+        fill_pages(c0, nvalid);
+        __syncthreads();
+    }
     float scl_pre[kChunk / kThreads];
     {
         const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
 #pragma unroll
         for (int i = 0; i < kChunk / kThreads; ++i) {
             const int t = tid + i * kThreads;
-            scl_pre[i] = t < nvalid ? scl[t] : 0.0f;
+            if constexpr (paged) scl_pre[i] = t < nvalid ? sc_head[paged_slot(c0 + t)] : 0.0f;
+            else scl_pre[i] = t < nvalid ? scl[t] : 0.0f;
         }
     }
     // rolling buffer of U rows per lane: a register is refilled with the row U rounds ahead as
@@ -160,7 +185,9 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     typename SR::R kv[U];
     const int8_t* krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * RB + sub * (RB / LPT);  // this lane's first row
     auto load_row = [&](int r) -> typename SR::R {
-        return r * TPR + tok_lane < nvalid ? SR::load(krow + r * (TPR * RB)) : SR::zero();
+        if (r * TPR + tok_lane >= nvalid) return SR::zero();
+        if constexpr (paged) return SR::load(kq_head + paged_slot(c0 + r * TPR + tok_lane) * uint32_t(RB) + uint32_t(sub * (RB / LPT)));
+        else return SR::load(krow + r * (TPR * RB));
     };
 #pragma unroll
     for (int u = 0; u < U; ++u) kv[u] = load_row(u);
@@ -231,9 +258,16 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         }
         if (nvalid == 0) break;  // later chunks of this workgroup are past T_b too
         if (!first) {
+            if constexpr (paged) {
+                fill_pages(c0, nvalid);
+                __syncthreads();
+            }
             const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
 #pragma unroll 4
-            for (int i = tid; i < nvalid; i += kThreads) s_scale[i] = scl[i];
+            for (int i = tid; i < nvalid; i += kThreads) {
+                if constexpr (paged) s_scale[i] = sc_head[paged_slot(c0 + i)];
+                else s_scale[i] = scl[i];
+            }
             __syncthreads();
         }
 
@@ -507,23 +541,29 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, int KB>
-static hipError_t launch_scan(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
+template <int D, int KB, bool P>
+static hipError_t launch_scan_p(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
     const int G = a.d.G;
     if (!agg_max) {
-        if (G == 1) launch_k("k_scan", (k_scan<D, 1, false, KB>), grid, dim3(kThreads), st, a);
-        else launch_k("k_scan", (k_scan<D, 2, false, KB>), grid, dim3(kThreads), st, a);
+        if (G == 1) launch_k("k_scan", (k_scan<D, 1, false, KB, P>), grid, dim3(kThreads), st, a);
+        else launch_k("k_scan", (k_scan<D, 2, false, KB, P>), grid, dim3(kThreads), st, a);
     } else {
         switch (padded_g(G)) {
-            case 1: launch_k("k_scan", (k_scan<D, 1, true, KB>), grid, dim3(kThreads), st, a); break;
-            case 2: launch_k("k_scan", (k_scan<D, 2, true, KB>), grid, dim3(kThreads), st, a); break;
-            case 4: launch_k("k_scan", (k_scan<D, 4, true, KB>), grid, dim3(kThreads), st, a); break;
-            case 8: launch_k("k_scan", (k_scan<D, 8, true, KB>), grid, dim3(kThreads), st, a); break;
-            case 16: launch_k("k_scan", (k_scan<D, 16, true, KB>), grid, dim3(kThreads), st, a); break;
+            case 1: launch_k("k_scan", (k_scan<D, 1, true, KB, P>), grid, dim3(kThreads), st, a); break;
+            case 2: launch_k("k_scan", (k_scan<D, 2, true, KB, P>), grid, dim3(kThreads), st, a); break;
+            case 4: launch_k("k_scan", (k_scan<D, 4, true, KB, P>), grid, dim3(kThreads), st, a); break;
+            case 8: launch_k("k_scan", (k_scan<D, 8, true, KB, P>), grid, dim3(kThreads), st, a); break;
+            case 16: launch_k("k_scan", (k_scan<D, 16, true, KB, P>), grid, dim3(kThreads), st, a); break;
             default: return hipErrorInvalidValue;
         }
     }
     return hipGetLastError();
+}
+
+template <int D, int KB>
+static hipError_t launch_scan(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
+    if (a.d.pg.table) return launch_scan_p<D, KB, true>(a, agg_max, grid, st);
+    return launch_scan_p<D, KB, false>(a, agg_max, grid, st);
 }
 
 hipError_t launch_propose(const ProposeArgs& a, int agg_max, hipStream_t st) {

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
 
     QRegs<T, D, GP> q;
     q.load(static_cast<const T*>(a.q) + (int64_t(b) * d.Hq + int64_t(g) * G) * D, G, sub);
-    const T* Ku = static_cast<const T*>(a.K) + int64_t(unit) * d.T_max * D;
+    const T* Kb = static_cast<const T*>(a.K);
     const int32_t* pool = a.pool + int64_t(unit) * kp;
     uint2* skey = a.skey + int64_t(unit) * a.kstride;
     float* logits = a.logits + int64_t(unit) * kp * LS;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
         uint4 raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            raw[u] = (t[u] >= 0 && t[u] < Tb) ? load16(Ku + int64_t(t[u]) * D + sub * EPL) : make_uint4(0, 0, 0, 0);
+            raw[u] = (t[u] >= 0 && t[u] < Tb) ? load16(Kb + cache_row(d, b, g, t[u]) * D + sub * EPL) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t j = j0 + (r0 + u) * RPR + rl;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
         const uint4 v = n < G ? load16(qh + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
         qa[s] = __builtin_bit_cast(bf16x8, v);
     }
-    const uint16_t* kr = static_cast<const uint16_t*>(a.K) + (int64_t(unit) * d.T_max + (valid ? t : 0)) * D + 8 * kg;
+    const uint16_t* kr = static_cast<const uint16_t*>(a.K) + (valid ? cache_row(d, b, g, t) : cache_row0(d, b, g)) * D + 8 * kg;
     uint4 kb[STEPS];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) kb[s] = load16(kr + 32 * s);
@@ -200,8 +200,9 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     float* part_ml = a.part_ml + int64_t(unit) * nsa * GP * 2;
     float* part_acc = a.part_acc + int64_t(unit) * nsa * GP * D;
     if (n > 0) {
-        const T* Vu = static_cast<const T*>(a.V) + int64_t(unit) * d.T_max * D;
-        softmax_v_rows<T, D, GP, NR, NT>(Vu, a.logits + int64_t(unit) * kp * LS, LS, a.y_scale, s_slot, s_tok, n, G,
+        const T* Vb = static_cast<const T*>(a.V);
+        auto vrow = [&](int32_t t) -> const T* { return Vb + cache_row(d, b, g, t) * D; };
+        softmax_v_rows<T, D, GP, NR, NT>(vrow, a.logits + int64_t(unit) * kp * LS, LS, a.y_scale, s_slot, s_tok, n, G,
                                          s_p, s_red, reinterpret_cast<float*>(s_big), part_acc + int64_t(slice) * GP * D,
                                          part_ml + int64_t(slice) * GP * 2);
     }

@@ -38,6 +38,7 @@ Dims dims_of(const prism_shape* s) {
     d.D = s->D;
     d.T_max = s->T_max;
     d.seq_lens = s->seq_lens;
+    d.pg = Paging{nullptr, 0, 0, 0};
     return d;
 }
 
@@ -87,9 +88,23 @@ prism_status prism_quantize_keys(const void* K, prism_dtype dt, const prism_shap
     return hip_status(launch_quantize_keys(K, dt == PRISM_BF16, d, Kq, scales, static_cast<hipStream_t>(stream)));
 }
 
+// A page descriptor: page_size a power of two up to 2^20, a table of max_pages >= 1 columns that
+// covers T_max logical tokens, a pool of num_slots rows (a multiple of page_size) per KV head.
+static prism_status paging_of(const prism_paging* p, const prism_shape* s, Paging* out) {
+    if (!p || !p->page_table || !aligned(p->page_table, 4)) return PRISM_ERR_INVALID_ARG;
+    if (p->page_size < 1 || p->page_size > (1 << 20) || (p->page_size & (p->page_size - 1))) return PRISM_ERR_INVALID_ARG;
+    if (p->max_pages < 1 || p->num_slots < p->page_size || p->num_slots % p->page_size) return PRISM_ERR_INVALID_ARG;
+    if (int64_t(p->max_pages) * p->page_size < s->T_max) return PRISM_ERR_INVALID_ARG;
+    if (p->num_slots > kMaxT) return PRISM_ERR_UNSUPPORTED;  // 2^23 rows per head: 32-bit row offsets
+    int lg = 0;
+    while ((1 << lg) < p->page_size) ++lg;
+    *out = Paging{p->page_table, p->max_pages, lg, p->num_slots};
+    return PRISM_OK;
+}
+
 static prism_status propose_impl(const void* q, prism_dtype qdt, const void* Kq, int key_bits, const float* scales,
-                                 const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool, float* scores,
-                                 void* ws, size_t ws_bytes, void* stream) {
+                                 const prism_shape* s, const prism_paging* paging, int32_t kp, prism_agg agg,
+                                 int32_t* pool, float* scores, void* ws, size_t ws_bytes, void* stream) {
     prism_status st = check_shape(s);
     if (st != PRISM_OK) return st;
     if (!valid_dtype(qdt) || !valid_agg(agg) || kp < 1) return PRISM_ERR_INVALID_ARG;
@@ -103,6 +118,7 @@ static prism_status propose_impl(const void* q, prism_dtype qdt, const void* Kq,
 
     ProposeArgs a{};
     a.d = dims_of(s);
+    if (paging && (st = paging_of(paging, s, &a.d.pg)) != PRISM_OK) return st;
     a.q = q;
     a.q_bf16 = qdt == PRISM_BF16;
     a.Kq = static_cast<const int8_t*>(Kq);
@@ -127,7 +143,7 @@ static prism_status propose_impl(const void* q, prism_dtype qdt, const void* Kq,
 prism_status prism_propose(const void* q, prism_dtype qdt, const int8_t* Kq, const float* scales,
                            const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool, float* scores,
                            void* ws, size_t ws_bytes, void* stream) {
-    return propose_impl(q, qdt, Kq, 8, scales, s, kp, agg, pool, scores, ws, ws_bytes, stream);
+    return propose_impl(q, qdt, Kq, 8, scales, s, nullptr, kp, agg, pool, scores, ws, ws_bytes, stream);
 }
 
 prism_status prism_quantize_keys_int2(const void* K, prism_dtype dt, const prism_shape* s, uint8_t* Kq2,
@@ -144,13 +160,21 @@ prism_status prism_quantize_keys_int2(const void* K, prism_dtype dt, const prism
 prism_status prism_propose_int2(const void* q, prism_dtype qdt, const uint8_t* Kq2, const float* scales,
                                 const prism_shape* s, int32_t kp, prism_agg agg, int32_t* pool, float* scores,
                                 void* ws, size_t ws_bytes, void* stream) {
-    return propose_impl(q, qdt, Kq2, 2, scales, s, kp, agg, pool, scores, ws, ws_bytes, stream);
+    return propose_impl(q, qdt, Kq2, 2, scales, s, nullptr, kp, agg, pool, scores, ws, ws_bytes, stream);
 }
 
-prism_status prism_refine_attend(const void* q, const void* K, const void* V, prism_dtype dt,
-                                 const prism_shape* s, const int32_t* pool, int32_t kp, int32_t kappa,
-                                 prism_agg agg, float sm_scale, void* out, int32_t* idx, float* lse,
-                                 void* ws, size_t ws_bytes, void* stream) {
+prism_status prism_propose_paged(const void* q, prism_dtype qdt, const void* Kq_pool, int32_t key_bits,
+                                 const float* scales_pool, const prism_shape* s, const prism_paging* paging,
+                                 int32_t kp, prism_agg agg, int32_t* pool, float* scores, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    if (!paging || (key_bits != 8 && key_bits != 2)) return PRISM_ERR_INVALID_ARG;
+    return propose_impl(q, qdt, Kq_pool, key_bits, scales_pool, s, paging, kp, agg, pool, scores, ws, ws_bytes, stream);
+}
+
+static prism_status refine_impl(const void* q, const void* K, const void* V, prism_dtype dt,
+                                const prism_shape* s, const prism_paging* paging, const int32_t* pool, int32_t kp,
+                                int32_t kappa, prism_agg agg, float sm_scale, void* out, int32_t* idx, float* lse,
+                                void* ws, size_t ws_bytes, void* stream) {
     prism_status st = check_shape(s);
     if (st != PRISM_OK) return st;
     if (!valid_dtype(dt) || !valid_agg(agg)) return PRISM_ERR_INVALID_ARG;
@@ -167,6 +191,7 @@ prism_status prism_refine_attend(const void* q, const void* K, const void* V, pr
 
     RefineArgs a{};
     a.d = dims_of(s);
+    if (paging && (st = paging_of(paging, s, &a.d.pg)) != PRISM_OK) return st;
     a.q = q;
     a.K = K;
     a.V = V;
@@ -185,6 +210,22 @@ prism_status prism_refine_attend(const void* q, const void* K, const void* V, pr
     a.part_ml = reinterpret_cast<float*>(carve(ws, L.part_ml));
     a.part_acc = reinterpret_cast<float*>(carve(ws, L.part_acc));
     return hip_status(launch_refine(a, dt == PRISM_BF16, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream)));
+}
+
+prism_status prism_refine_attend(const void* q, const void* K, const void* V, prism_dtype dt,
+                                 const prism_shape* s, const int32_t* pool, int32_t kp, int32_t kappa,
+                                 prism_agg agg, float sm_scale, void* out, int32_t* idx, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream) {
+    return refine_impl(q, K, V, dt, s, nullptr, pool, kp, kappa, agg, sm_scale, out, idx, lse, ws, ws_bytes, stream);
+}
+
+prism_status prism_refine_attend_paged(const void* q, const void* K_pool, const void* V_pool, prism_dtype dt,
+                                       const prism_shape* s, const prism_paging* paging, const int32_t* pool,
+                                       int32_t kp, int32_t kappa, prism_agg agg, float sm_scale, void* out,
+                                       int32_t* idx, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (!paging) return PRISM_ERR_INVALID_ARG;
+    return refine_impl(q, K_pool, V_pool, dt, s, paging, pool, kp, kappa, agg, sm_scale, out, idx, lse, ws, ws_bytes,
+                       stream);
 }
 
 prism_status prism_dense_ref(const void* q, const void* K, const void* V, prism_dtype dt, const prism_shape* s,

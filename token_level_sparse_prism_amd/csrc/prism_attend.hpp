@@ -218,6 +218,7 @@ template <> struct LaneRow<float, 4> {
 constexpr int kRowsAccFloats = 8192;  // LDS floats for the waves' V partials (one round of heads)
 
 // softmax(y) V partial over the n (1 <= n <= NR) selected rows of one workgroup of NT threads.
+//   vrow(t)              the V row of token t (contiguous or paged cache)
 //   s_slot[r], s_tok[r]  pool slot and token id of row r
 //   logits               the unit's [kp][LS] fp32 logits per pool slot; y = logit * y_scale is
 //                        the base-2 exponent-domain logit (heads >= G unused)
@@ -228,8 +229,8 @@ constexpr int kRowsAccFloats = 8192;  // LDS floats for the waves' V partials (o
 // are summed in LDS in wave order, HB heads per round.  Writes g_ml[h] = (max_r y,
 // sum_r 2^(y - max)) and g_acc[h][d] = sum_r 2^(y - max) V[r][d] for h < G at device scope.
 // LDS: s_red 2*(NT/64)*GP floats, s_wacc kRowsAccFloats floats.
-template <typename T, int D, int GP, int NR, int NT>
-__device__ __forceinline__ void softmax_v_rows(const T* __restrict__ Vu, const float* __restrict__ logits, int LS,
+template <typename T, int D, int GP, int NR, int NT, typename VRow>
+__device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restrict__ logits, int LS,
                                                float y_scale, const int32_t* s_slot, const int32_t* s_tok, int n,
                                                int G, float* s_p, float* s_red, float* s_wacc,
                                                float* __restrict__ g_acc, float* __restrict__ g_ml) {
@@ -262,7 +263,7 @@ __device__ __forceinline__ void softmax_v_rows(const T* __restrict__ Vu, const f
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
         const int r = row0 + u;
-        raw[u] = LR::load(Vu + int64_t(s_tok[r < n ? r : 0]) * D + lane * NE);
+        raw[u] = LR::load(vrow(s_tok[r < n ? r : 0]) + lane * NE);
     }
 
     // statistics
@@ -320,7 +321,7 @@ __device__ __forceinline__ void softmax_v_rows(const T* __restrict__ Vu, const f
 #pragma unroll
             for (int u = 0; u < UB; ++u) {
                 const int r = row0 + i0 + u;
-                raw[u] = LR::load(Vu + int64_t(s_tok[r < n ? r : 0]) * D + lane * NE);
+                raw[u] = LR::load(vrow(s_tok[r < n ? r : 0]) + lane * NE);
             }
         }
 #pragma unroll

@@ -361,4 +361,19 @@ __device__ __forceinline__ int64_t seq_len_of(const Dims& d, int b) {
     return t < 0 ? 0 : (t > d.T_max ? d.T_max : t);
 }
 
+// Cache row (K, V, compressed keys, scales) of token t of sequence b at KV head g.  Page ids are
+// clamped into the pool, so a bad table entry reads a wrong row of the pool, never memory
+// outside it.
+__device__ __forceinline__ int64_t cache_row(const Dims& d, int b, int g, int64_t t) {
+    if (d.pg.table == nullptr) return (int64_t(b) * d.Hkv + g) * d.T_max + t;
+    int64_t page = d.pg.table[int64_t(b) * d.pg.max_pages + (t >> d.pg.log2p)];
+    const int64_t npages = d.pg.slots >> d.pg.log2p;
+    page = page < 0 ? 0 : (page >= npages ? npages - 1 : page);
+    return int64_t(g) * d.pg.slots + (page << d.pg.log2p) + (t & ((int64_t(1) << d.pg.log2p) - 1));
+}
+// The first cache row of unit (b, g): a safe row for lanes that hold no token.
+__device__ __forceinline__ int64_t cache_row0(const Dims& d, int b, int g) {
+    return d.pg.table == nullptr ? (int64_t(b) * d.Hkv + g) * d.T_max : int64_t(g) * d.pg.slots;
+}
+
 }  // namespace prism

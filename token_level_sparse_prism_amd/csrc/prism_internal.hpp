@@ -109,10 +109,21 @@ inline DenseWs dense_ws(int64_t units, int64_t T_max, int GP, int D) {
 }
 
 // ---- kernel argument blocks ---------------------------------------------------------------
+// Where a KV head's cache rows live.  Contiguous (table == nullptr): unit (b, g) owns rows
+// [unit * T_max, (unit + 1) * T_max).  Paged: KV head g owns a pool of `slots` rows, and token t
+// of sequence b is in row g * slots + page * P + (t mod P), page = table[b][t / P], P = 2^log2p.
+struct Paging {
+    const int32_t* table;  // [B][max_pages] device, or nullptr
+    int32_t max_pages;
+    int32_t log2p;
+    int64_t slots;
+};
+
 struct Dims {
     int B, Hq, Hkv, G, D;
     int64_t T_max;
     const int32_t* seq_lens;
+    Paging pg;             // table == nullptr: contiguous [B][Hkv][T_max] caches
 };
 
 struct ProposeArgs {
