@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
             }
             if (sub == 0 && j < kp && (r0 + u) * RPR + rl < kScoreSlice) {
                 const uint32_t key = valid ? order_key(S) : 0u;
-                st_stream(&skey[j], make_uint2(key, valid ? uint32_t(t[u]) : 0xFFFFFFFFu));
+                const uint32_t id = d.pg.table ? uint32_t(cache_row(d, b, g, t[u]) - cache_row0(d, b, g)) : uint32_t(t[u]);
+                st_stream(&skey[j], make_uint2(key, valid ? id : 0xFFFFFFFFu));
 #pragma unroll
                 for (int h4 = 0; h4 < LS; h4 += 4) {
                     float4 v;
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
         const uint4 v = n < G ? load16(qh + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
         qa[s] = __builtin_bit_cast(bf16x8, v);
     }
-    const uint16_t* kr = static_cast<const uint16_t*>(a.K) + (valid ? cache_row(d, b, g, t) : cache_row0(d, b, g)) * D + 8 * kg;
+    const int64_t krow = valid ? cache_row(d, b, g, t) : cache_row0(d, b, g);
+    const uint16_t* kr = static_cast<const uint16_t*>(a.K) + krow * D + 8 * kg;
     uint4 kb[STEPS];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) kb[s] = load16(kr + 32 * s);
@@ -157,7 +159,8 @@ __global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
         }
         if (kg == 0) {
             const uint32_t key = valid ? order_key(S) : 0u;
-            st_stream(a.skey + int64_t(unit) * a.kstride + j, make_uint2(key, valid ? uint32_t(t) : 0xFFFFFFFFu));
+            const uint32_t id = d.pg.table ? uint32_t(krow - cache_row0(d, b, g)) : uint32_t(t);
+            st_stream(a.skey + int64_t(unit) * a.kstride + j, make_uint2(key, valid ? id : 0xFFFFFFFFu));
         }
     }
 }
@@ -194,17 +197,23 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
                                           s_tmp, s_res, s_cand, s_ccount, s_slot, s_tok);
     const int n = sr.n;
 
-    // ---- idx, then the slice's softmax(.)V partial ----
-    if (tid < NR && r0 + tid < a.kappa) a.idx[int64_t(unit) * a.kappa + r0 + tid] = tid < n ? s_tok[tid] : -1;
+    // ---- the slice's softmax(.)V partial, then idx.  s_tok holds the selected slots' record ids:
+    // token ids, or with paged caches the row inside the KV head's pool (pool scoring found it) ----
+    const bool paged = d.pg.table != nullptr;
     const int nsa = int(gridDim.x);
     float* part_ml = a.part_ml + int64_t(unit) * nsa * GP * 2;
     float* part_acc = a.part_acc + int64_t(unit) * nsa * GP * D;
     if (n > 0) {
-        const T* Vb = static_cast<const T*>(a.V);
-        auto vrow = [&](int32_t t) -> const T* { return Vb + cache_row(d, b, g, t) * D; };
+        const T* Vb = static_cast<const T*>(a.V) + cache_row0(d, b, g) * D;
+        auto vrow = [&](int32_t id) -> const T* { return Vb + int64_t(uint32_t(id)) * D; };
         softmax_v_rows<T, D, GP, NR, NT>(vrow, a.logits + int64_t(unit) * kp * LS, LS, a.y_scale, s_slot, s_tok, n, G,
                                          s_p, s_red, reinterpret_cast<float*>(s_big), part_acc + int64_t(slice) * GP * D,
                                          part_ml + int64_t(slice) * GP * 2);
+    }
+    if (tid < NR && r0 + tid < a.kappa) {
+        int32_t t = -1;
+        if (tid < n) t = paged ? a.pool[int64_t(unit) * kp + s_slot[tid]] : s_tok[tid];
+        a.idx[int64_t(unit) * a.kappa + r0 + tid] = t;
     }
 
     if (!arrive_last(&a.done_a[int64_t(unit) * kCtrStride], gridDim.x, &s_flag)) return;

@@ -161,7 +161,8 @@ struct RefineArgs {
     int32_t* idx;
     float* lse;
     uint32_t* done_a;       // [U][kCtrStride]
-    uint2* skey;            // [U][kstride] {order key of S (0 = empty slot), token} per pool slot
+    uint2* skey;            // [U][kstride] {order key of S (0 = empty slot), id} per pool slot: id = the
+                            // token, or with paged caches its row in the KV head's pool
     float* logits;          // [U][kp][LS]
     float* part_ml;         // [U][nsa][GP][2]
     float* part_acc;        // [U][nsa][GP][D]

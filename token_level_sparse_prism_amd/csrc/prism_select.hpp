@@ -116,7 +116,7 @@ __device__ __forceinline__ void sel_digit_hist(const uint2* __restrict__ gk, int
     }
 }
 
-// gk: the unit's [kp] {key, token} slots (16-byte aligned).
+// gk: the unit's [kp] {key, id} slots (16-byte aligned); ids pass through to s_tok.
 // LDS: s_hist kSelHistWords words, 16-byte aligned; s_tmp sel_tmp_words<NT>() words; s_res 16 words;
 // s_cand kSelCandTotal words (16-byte aligned), s_ccount NT/64 words, s_slot / s_tok nmax each.
 template <int NT>
