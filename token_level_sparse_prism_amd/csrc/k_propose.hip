@@ -91,8 +91,11 @@ __device__ __forceinline__ int lane_dot(const int* qw, uint32_t w, int c3) {
     return 2 * dot_2bit_word(qw, w, 0) + c3;
 }
 
-template <int D, int NQ, bool kMax, int KB, bool kPaged>
+// kPg: 0 contiguous caches; 1 paged, a page id per row; 2 paged with pages of at least TPR tokens,
+// so the TPR tokens of a round share one page and its base is a scalar.
+template <int D, int NQ, bool kMax, int KB, int kPg>
 __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
+    constexpr bool kPaged = kPg != 0;
     constexpr int DPL = (KB == 2 && NQ <= 2) ? 64 : 16;  // dims per lane
     using SR = ScanRow<KB, DPL>;
     constexpr int QW = DPL / 4;            // q words per vector and lane
@@ -165,6 +168,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         return (uint32_t(s_pg[(t >> lp) - (c0 >> lp)]) << lp) + uint32_t(t & ((int64_t(1) << lp) - 1));
     };
     const int8_t* kq_head = a.Kq + int64_t(g) * d.pg.slots * RB;
+    const uint32_t lane_off = uint32_t(tok_lane * RB + sub * (RB / LPT));  // kPg == 2: a lane's offset in a round
     const float* sc_head = a.scales + int64_t(g) * d.pg.slots;
     if constexpr (paged) {
         fill_pages(c0, nvalid);
@@ -186,8 +190,15 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     const int8_t* krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * RB + sub * (RB / LPT);  // this lane's first row
     auto load_row = [&](int r) -> typename SR::R {
         if (r * TPR + tok_lane >= nvalid) return SR::zero();
-        if constexpr (paged) return SR::load(kq_head + paged_slot(c0 + r * TPR + tok_lane) * uint32_t(RB) + uint32_t(sub * (RB / LPT)));
-        else return SR::load(krow + r * (TPR * RB));
+        if constexpr (kPg == 2) {
+            const int64_t t0 = c0 + int64_t(r) * TPR;  // the round's first token, page-aligned run
+            const int64_t pg = __builtin_amdgcn_readfirstlane(s_pg[(t0 >> lp) - (c0 >> lp)]);
+            return SR::load(kq_head + ((pg << lp) + (t0 & ((int64_t(1) << lp) - 1))) * RB + lane_off);
+        } else if constexpr (paged) {
+            return SR::load(kq_head + paged_slot(c0 + r * TPR + tok_lane) * uint32_t(RB) + uint32_t(sub * (RB / LPT)));
+        } else {
+            return SR::load(krow + r * (TPR * RB));
+        }
     };
 #pragma unroll
     for (int u = 0; u < U; ++u) kv[u] = load_row(u);
@@ -541,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, int KB, bool P>
+template <int D, int KB, int P>
 static hipError_t launch_scan_p(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
     const int G = a.d.G;
     if (!agg_max) {
@@ -562,8 +573,12 @@ static hipError_t launch_scan_p(const ProposeArgs& a, int agg_max, dim3 grid, hi
 
 template <int D, int KB>
 static hipError_t launch_scan(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
-    if (a.d.pg.table) return launch_scan_p<D, KB, true>(a, agg_max, grid, st);
-    return launch_scan_p<D, KB, false>(a, agg_max, grid, st);
+    if (!a.d.pg.table) return launch_scan_p<D, KB, 0>(a, agg_max, grid, st);
+    // tokens per scan round: 256 threads over D/DPL lanes per token (see k_scan)
+    const int dpl = (KB == 2 && (agg_max ? padded_g(a.d.G) : (a.d.G == 1 ? 1 : 2)) <= 2) ? 64 : 16;
+    const int tpr = kThreads * dpl / D;
+    if ((1 << a.d.pg.log2p) >= tpr) return launch_scan_p<D, KB, 2>(a, agg_max, grid, st);
+    return launch_scan_p<D, KB, 1>(a, agg_max, grid, st);
 }
 
 hipError_t launch_propose(const ProposeArgs& a, int agg_max, hipStream_t st) {
