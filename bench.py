@@ -296,6 +296,25 @@ def main():
             kernels[k] = {"launches": n, "avg_us": 1000.0 * ms / n}
     PB.profile_reset()
 
+    # read-stream ceiling: a plain coalesced read of the int8 key cache (the scan's main input),
+    # cycling through the same buffer sets, timed like the kernels
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    for i in range(10):
+        PB.read_probe(sets[i % R]["Kq"], sink)
+    torch.cuda.synchronize()
+    PB.profile_reset()
+    PB.profile_enable(True)
+    for i in range(60):
+        PB.read_probe(sets[i % R]["Kq"], sink)
+    torch.cuda.synchronize()
+    PB.profile_enable(False)
+    n_rp, ms_rp = PB.profile_query("k_read_probe")
+    PB.profile_reset()
+    probe_bytes = base["Kq"].numel()
+    probe_us = 1000.0 * ms_rp / n_rp
+    ceiling = {"kernel": "k_read_probe", "GBps": round(probe_bytes / (probe_us * 1e-6) / 1e9, 1),
+               "bytes": int(probe_bytes), "avg_launch_us": round(probe_us, 3)}
+
     ab = W.algorithmic_bytes(cfg, w.seq_lens)
     e = 2 if cfg.dtype == "bf16" else 4
     scan_bytes = sum(int(w.seq_lens[b]) * (cfg.D + 4) + cfg.G * cfg.D * e
@@ -311,7 +330,8 @@ def main():
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4) if achieved else None,
                 "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
-                "avg_launch_us": round(scan_us, 3) if scan_us else None}
+                "avg_launch_us": round(scan_us, 3) if scan_us else None,
+                "frac_of_read_ceiling": round(achieved / ceiling["GBps"], 4) if achieved else None}
 
     # the same step with INT2 proposal keys (a second key format; the headline above is int8):
     # stream-launched, same buffer rotation and workspaces, plus how its pools compare with int8's
@@ -454,9 +474,23 @@ def main():
             if time.perf_counter() - c0 >= args.cpu_seconds:
                 break
         cs = time.perf_counter() - c0
+        c1 = time.perf_counter()  # one step on one thread
+        opool1 = oracle.propose(w.q[0], oKq, osc, cfg.kp, seq_lens=w.seq_lens, nthreads=1)
+        for l in range(1, w.layers):
+            oracle.refine(w.q[l], w.K[l], w.V[l], opool1, cfg.kappa, seq_lens=w.seq_lens, nthreads=1)
+        cs1 = time.perf_counter() - c1
+        model = ""
+        try:
+            for ln in open("/proc/cpuinfo"):
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         cpu = {"value": round(n / cs, 3), "unit": "steps/s", "cores": threads, "kind": "oracle",
                "sample": f"{n} full steps of the same workload ({cfg.units} units, proposal + "
-                         f"{cfg.n_refined} refined layers) in {cs:.1f} s, OpenMP over units"}
+                         f"{cfg.n_refined} refined layers) in {cs:.1f} s, OpenMP over units",
+               "value_1_thread": round(1.0 / cs1, 3), "cpu_model": model}
         assert np.array_equal(opool, pool), "oracle and GPU pools differ"
 
     steps_per_s = 1000.0 / ms_per_step
@@ -480,6 +514,7 @@ def main():
         "ms_per_step_by_launch": {m: round(v, 5) for m, v in med.items()},
         "ms_per_step_warm": round(ms_warm, 5),
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in kernels.items()},
+        "read_ceiling": ceiling,
         "int2_keys": int2,
         "paged_kv": paged,
         "cpu_baseline": cpu,

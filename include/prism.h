@@ -220,12 +220,22 @@ prism_status prism_dense_ref(const void* q, const void* K, const void* V, prism_
  * the calls above is bracketed by two events recorded on its stream (this adds event packets
  * between kernels, so it is for measurement passes, not for production steps).
  * prism_profile_query synchronises the recorded events and returns, for one kernel name
- * ("k_quantize_keys", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense"), the
+ * ("k_quantize_keys", "k_quantize_keys_int2", "k_scan", "k_cand", "k_compact", "k_rscore",
+ * "k_attend", "k_dense", "k_read_probe"), the
  * number of launches and their summed duration in milliseconds since the last reset.
  */
 prism_status prism_profile_enable(int on);
 prism_status prism_profile_query(const char* name, int* launches, double* total_ms);
 void prism_profile_reset(void);
+
+/*
+ * Diagnostics: the read-stream ceiling.  One plain coalesced read of `bytes` (a multiple of 16,
+ * src 16-byte aligned) with 16-byte streaming loads over 1024 workgroups, each reading one
+ * contiguous 1/1024 of the buffer; the XOR of what each wave read goes to sink (4096 words).
+ * Timed like the other kernels ("k_read_probe" in prism_profile_query), it gives the HBM read
+ * rate that the scan kernel is compared with.
+ */
+prism_status prism_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* The hipError_t of the last failed HIP call on this thread (0 if none). */
 int prism_last_hip_error(void);

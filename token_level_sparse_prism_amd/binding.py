@@ -21,8 +21,9 @@ STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_INVALID_ARG", 2: "PRISM_ERR_UNSUPPORTED",
 EXPORTS = ("prism_workspace_bytes", "prism_workspace_init", "prism_quantize_keys", "prism_propose",
            "prism_quantize_keys_int2", "prism_propose_int2", "prism_propose_paged", "prism_refine_attend_paged",
            "prism_refine_attend", "prism_dense_ref", "prism_profile_enable", "prism_profile_query",
-           "prism_profile_reset", "prism_last_hip_error", "prism_status_str")
-KERNELS = ("k_quantize_keys", "k_quantize_keys_int2", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense")
+           "prism_profile_reset", "prism_last_hip_error", "prism_status_str", "prism_read_probe")
+KERNELS = ("k_quantize_keys", "k_quantize_keys_int2", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense",
+           "k_read_probe")
 
 
 class PrismError(RuntimeError):
@@ -83,6 +84,8 @@ def load():
     lib.prism_profile_query.restype = ctypes.c_int
     lib.prism_profile_reset.argtypes = []
     lib.prism_profile_reset.restype = None
+    lib.prism_read_probe.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+    lib.prism_read_probe.restype = ctypes.c_int
     lib.prism_status_str.argtypes = [ctypes.c_int]
     lib.prism_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -322,6 +325,16 @@ def dense_ref(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, sm_scale: float
                                                      ctypes.byref(shape), float(sm_scale), _ptr(out),
                                                      _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
     return out, lse
+
+
+def read_probe(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One plain coalesced read of the whole of `src` (diagnostics: the read-stream ceiling)."""
+    _need(src, "src")
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.zeros(4096, dtype=torch.int32, device=src.device)
+    _check("prism_read_probe", load().prism_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream(stream)))
+    return sink
 
 
 def profile_enable(on: bool = True):

@@ -257,6 +257,12 @@ prism_status prism_dense_ref(const void* q, const void* K, const void* V, prism_
     return hip_status(launch_dense(a, dt == PRISM_BF16, static_cast<hipStream_t>(stream)));
 }
 
+prism_status prism_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (!src || !sink || bytes < 16 || bytes % 16 || !aligned(src, 16) || !aligned(sink, 4))
+        return PRISM_ERR_INVALID_ARG;
+    return hip_status(launch_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 int prism_last_hip_error(void) { return g_last_hip_error; }
 
 const char* prism_status_str(prism_status st) {

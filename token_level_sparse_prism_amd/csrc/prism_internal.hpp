@@ -182,6 +182,7 @@ struct DenseArgs {
 };
 
 // ---- launchers (defined in the kernel files) ----------------------------------------------
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_quantize_keys_int2(const void* K, int bf16, const Dims& d, uint8_t* Kq2, float* scales,
                                      hipStream_t st);
 hipError_t launch_quantize_keys(const void* K, int bf16, const Dims& d, int8_t* Kq, float* scales,
