@@ -385,6 +385,38 @@ def test_full_size_128k_sampled_units():
                            w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype, units={(0, 0), (0, 5)})
 
 
+@pytest.mark.parametrize("name", ["cfg5_D256_k8192_r8", "cfg5_D64_k2048_r4"])
+def test_full_size_262k_single_unit(name):
+    """The 262144-token stress workloads at full size (Student-t keys, 8 query heads on one KV
+    head): the pool bit for bit, and every refined layer in full against the oracle.  At
+    kp = 65536 the refine selection runs over eight 8192-slot tiles."""
+    c = W.CONFIGS[name]
+    w = W.generate(c)
+    step, Kq, sc = run_step_gpu(w, c.kp, c.kappa)
+    oKq, osc = oracle.quantize_rows(w.K[0])
+    assert np.array_equal(Kq.cpu().numpy(), oKq)
+    opool = oracle.propose(w.q[0], oKq, osc, c.kp, seq_lens=w.seq_lens)
+    assert_pool_equal(step.pool.cpu().numpy(), opool)
+    for l in range(1, w.layers):
+        check_refine_batch(step.idx[l - 1].cpu().numpy(), host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(),
+                           w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype)
+
+
+def test_full_size_cfg2_sampled_units():
+    """The 32K-context batch-4 workload at full size: every unit's pool bit for bit, and three
+    units' refined layers in full."""
+    c = W.CONFIGS["cfg2"]
+    w = W.generate(c)
+    step, Kq, sc = run_step_gpu(w, c.kp, c.kappa)
+    oKq, osc = oracle.quantize_rows(w.K[0])
+    opool = oracle.propose(w.q[0], oKq, osc, c.kp, seq_lens=w.seq_lens)
+    assert_pool_equal(step.pool.cpu().numpy(), opool)
+    for l in range(1, w.layers):
+        check_refine_batch(step.idx[l - 1].cpu().numpy(), host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(),
+                           w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype,
+                           units={(0, 0), (1, 3), (3, 7)})
+
+
 def test_full_size_128k_int2():
     """The 128K-context workload with INT2 proposal keys: the packed codes and scales, every
     unit's pool bit for bit, two units' refined layers in full, and the anchor's unshifted planted
