@@ -364,6 +364,49 @@ def test_determinism_and_workspace_reuse():
             assert torch.equal(a, b)
 
 
+def test_split_independence():
+    """The same unit alone and inside a batch of 128 units: the scan splits its 32 chunks over 32
+    workgroups alone and over 8 workgroups (4 chunks each) in the batch.  Pools, index sets,
+    outputs and lse of that unit are bit-identical (P10)."""
+    D, G, T, kp, kappa = 64, 2, 32768, 4096, 1024
+    Bn, Hkv = 8, 16
+    q, K, V, lens = make_inputs(31337, Bn, G * Hkv, Hkv, D, T, "bf16")
+    ld = torch.from_numpy(lens).cuda()
+    Kq, sc = PB.quantize_keys(dev(K, "bf16"), seq_lens=ld)
+    pool_b = PB.propose(dev(q, "bf16"), Kq, sc, kp, seq_lens=ld)
+    out_b, idx_b, lse_b = PB.refine_attend(dev(q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), pool_b, kappa, seq_lens=ld)
+    b, g = 5, 11
+    q1 = np.ascontiguousarray(q[b:b + 1, g * G:(g + 1) * G])
+    K1, V1 = np.ascontiguousarray(K[b:b + 1, g:g + 1]), np.ascontiguousarray(V[b:b + 1, g:g + 1])
+    ld1 = torch.from_numpy(lens[b:b + 1]).cuda()
+    Kq1, sc1 = PB.quantize_keys(dev(K1, "bf16"), seq_lens=ld1)
+    pool_1 = PB.propose(dev(q1, "bf16"), Kq1, sc1, kp, seq_lens=ld1)
+    out_1, idx_1, lse_1 = PB.refine_attend(dev(q1, "bf16"), dev(K1, "bf16"), dev(V1, "bf16"), pool_1, kappa,
+                                           seq_lens=ld1)
+    torch.cuda.synchronize()
+    assert torch.equal(pool_1[0, 0], pool_b[b, g])
+    assert torch.equal(idx_1[0, 0], idx_b[b, g])
+    assert torch.equal(out_1[0], out_b[b, g * G:(g + 1) * G])
+    assert torch.equal(lse_1[0], lse_b[b, g * G:(g + 1) * G])
+
+
+def test_graph_replay_int2():
+    """A HIP graph of a whole step with INT2 proposal keys replays to the eager step bit for bit."""
+    c = W.CONFIGS["cfg2"].with_(B=1, Hkv=2, Hq=8, T=12000)
+    w = W.generate(c)
+    step, _, _ = run_step_gpu(w, c.kp, c.kappa, key_bits=2)
+    ref = [step.pool.clone()] + [t.clone() for t in step.idx] + [t.clone() for t in step.out]
+    graph = step.capture()
+    for i in range(3):
+        for t in [step.pool] + list(step.idx) + list(step.out):
+            t.fill_(7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, [step.pool] + list(step.idx) + list(step.out)):
+            assert torch.equal(a, b), f"replay {i}"
+
+
 def test_full_size_128k_sampled_units():
     """The 128K-context workload at full size, in the launch configuration the benchmark times:
     every unit's pool, two units' refined layers in full against the oracle, and index sets
