@@ -499,7 +499,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8+bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: 128K-context GQA decode step, B={cfg.B}, Hq={cfg.Hq}, "
+        "config": {"workload": f"{cfg.name}: {cfg.T // 1024}K-context decode step, B={cfg.B}, Hq={cfg.Hq}, "
                                f"Hkv={cfg.Hkv}, D={cfg.D}, T={cfg.T}, kp={cfg.kp}, kappa={cfg.kappa}, "
                                f"1 proposal + {cfg.n_refined} refined layers, {cfg.dtype}",
                    "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU",
