@@ -216,12 +216,32 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
         a.idx[int64_t(unit) * a.kappa + r0 + tid] = t;
     }
 
-    if (!arrive_last(&a.done_a[int64_t(unit) * kCtrStride], gridDim.x, &s_flag)) return;
-
-    const int np = int((sr.kappa_eff + NR - 1) / NR);
+    const int np = int((sr.kappa_eff + NR - 1) / NR);  // slices that wrote a partial
     const int64_t hq0 = int64_t(b) * d.Hq + int64_t(g) * G;
-    merge_partials<T, D, GP, NT>(part_ml, part_acc, np, G, static_cast<T*>(a.out) + hq0 * D,
-                                 a.lse ? a.lse + hq0 : nullptr);
+    T* out = static_cast<T*>(a.out) + hq0 * D;
+    float* lse = a.lse ? a.lse + hq0 : nullptr;
+    if (nsa <= kMergeGroup) {  // one level: the last slice merges every partial
+        if (!arrive_last(&a.done_a[int64_t(unit) * kCtrStride], nsa, &s_flag)) return;
+        merge_partials<T, D, GP, NT>(part_ml, part_acc, np, G, out, lse);
+        if (tid == 0) a.done_a[int64_t(unit) * kCtrStride] = 0u;
+        return;
+    }
+    // two levels: the last slice of each group of kMergeGroup merges the group's partials into a
+    // group partial; the last group to finish merges the group partials
+    const int ngrp = (nsa + kMergeGroup - 1) / kMergeGroup;
+    const int grp = slice / kMergeGroup;
+    const int gsz = nsa - grp * kMergeGroup < kMergeGroup ? nsa - grp * kMergeGroup : kMergeGroup;
+    uint32_t* cg = a.done_g + (int64_t(unit) * ngrp + grp) * kCtrStride;
+    if (!arrive_last(cg, gsz, &s_flag)) return;
+    const int gnp = np - grp * kMergeGroup <= 0 ? 0 : (np - grp * kMergeGroup < kMergeGroup ? np - grp * kMergeGroup : kMergeGroup);
+    float* g2_ml = a.part2_ml + int64_t(unit) * ngrp * GP * 2;
+    float* g2_acc = a.part2_acc + int64_t(unit) * ngrp * GP * D;
+    merge_partials<T, D, GP, NT, true>(part_ml + int64_t(grp) * kMergeGroup * GP * 2,
+                                       part_acc + int64_t(grp) * kMergeGroup * GP * D, gnp, G, nullptr, nullptr,
+                                       g2_ml + int64_t(grp) * GP * 2, g2_acc + int64_t(grp) * GP * D);
+    if (tid == 0) *cg = 0u;
+    if (!arrive_last(&a.done_a[int64_t(unit) * kCtrStride], ngrp, &s_flag)) return;
+    merge_partials<T, D, GP, NT>(g2_ml, g2_acc, (np + kMergeGroup - 1) / kMergeGroup, G, out, lse);
     if (tid == 0) a.done_a[int64_t(unit) * kCtrStride] = 0u;
 }
 

@@ -205,6 +205,9 @@ static prism_status refine_impl(const void* q, const void* K, const void* V, pri
     a.idx = idx;
     a.lse = lse;
     a.done_a = reinterpret_cast<uint32_t*>(carve(ws, L.done_a));
+    a.done_g = reinterpret_cast<uint32_t*>(carve(ws, L.done_g));
+    a.part2_ml = reinterpret_cast<float*>(carve(ws, L.part2_ml));
+    a.part2_acc = reinterpret_cast<float*>(carve(ws, L.part2_acc));
     a.skey = reinterpret_cast<uint2*>(carve(ws, L.skey));
     a.logits = reinterpret_cast<float*>(carve(ws, L.logits));
     a.part_ml = reinterpret_cast<float*>(carve(ws, L.part_ml));

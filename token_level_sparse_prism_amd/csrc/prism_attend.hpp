@@ -380,10 +380,12 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
 // Log-sum-exp merge of `np` partials (partial s at g_ml + s*GP*2, g_acc + s*GP*D), read at
 // device scope, sixteen partials per batch of independent loads: the batch's maximum first, then
 // every partial's weight on its own.  Writes out[h][d] (dtype T) and lse[h] (natural log) for
-// h < G; np == 0 gives out = 0, lse = -inf.
-template <typename T, int D, int GP, int NT = kThreads>
+// h < G; np == 0 gives out = 0, lse = -inf.  With kToPartial it writes instead one partial of the
+// same form (o_ml, o_acc, at device scope): the merge of the np partials, m = -inf for np == 0.
+template <typename T, int D, int GP, int NT = kThreads, bool kToPartial = false>
 __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, const float* __restrict__ g_acc, int np, int G,
-                               T* __restrict__ out, float* __restrict__ lse) {
+                               T* __restrict__ out, float* __restrict__ lse, float* __restrict__ o_ml = nullptr,
+                               float* __restrict__ o_acc = nullptr) {
     constexpr float kLn2 = 0.6931471805599453f;
     constexpr int BATCH = 16;
     for (int i = threadIdx.x; i < G * D; i += NT) {
@@ -413,9 +415,17 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, c
             }
             M = Mn;
         }
-        const bool empty = np == 0;
-        store_elem<T>(&out[int64_t(h) * D + dd], empty ? 0.0f : acc / L);
-        if (dd == 0 && lse) lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+        if constexpr (kToPartial) {
+            st_dev(&o_acc[h * D + dd], acc);
+            if (dd == 0) {
+                st_dev(&o_ml[2 * h], M);
+                st_dev(&o_ml[2 * h + 1], L);
+            }
+        } else {
+            const bool empty = np == 0;
+            store_elem<T>(&out[int64_t(h) * D + dd], empty ? 0.0f : acc / L);
+            if (dd == 0 && lse) lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+        }
     }
 }
 

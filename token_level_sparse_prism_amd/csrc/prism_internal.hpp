@@ -20,6 +20,7 @@ constexpr int kChunk = 1024;           // tokens per chunk in the proposal kerne
 constexpr int kScanWgs = PRISM_SCAN_WGS;
 constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in pool scoring
 constexpr int kAttendRanks = 128;      // selected rows per workgroup in sparse attention
+constexpr int kMergeGroup = 16;        // partials merged by one workgroup (two levels above it)
 constexpr int kAttendThreads = 1024;   // 16 waves: the selection's latency is shared by 4 waves per SIMD
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
 constexpr int kCtrStride = 16;         // counters sit 64 bytes apart (no shared cache line)
@@ -67,8 +68,8 @@ inline ProposeWs propose_ws(int64_t units, int64_t T_max) {
 }
 
 struct RefineWs {
-    size_t done_a, ctrl_bytes;
-    size_t skey, logits, part_ml, part_acc, total;
+    size_t done_a, done_g, ctrl_bytes;
+    size_t skey, logits, part_ml, part_acc, part2_ml, part2_acc, total;
 };
 
 inline int padded_g(int G) {
@@ -82,12 +83,16 @@ inline RefineWs refine_ws(int64_t units, int64_t kp, int64_t kappa, int GP, int 
     RefineWs w{};
     const int64_t nsa = (kappa + kAttendRanks - 1) / kAttendRanks;
     size_t o = 0;
+    const int64_t ngrp = (nsa + kMergeGroup - 1) / kMergeGroup;
     w.done_a = o;   o = align256(o + size_t(units) * kCtrStride * 4);
+    w.done_g = o;   o = align256(o + size_t(units) * ngrp * kCtrStride * 4);
     w.ctrl_bytes = o;
     w.skey = o;     o = align256(o + size_t(units) * key_stride(kp) * 8);
     w.logits = o;   o = align256(o + size_t(units) * kp * logit_stride(GP) * 4);
     w.part_ml = o;  o = align256(o + size_t(units) * nsa * GP * 2 * 4);
     w.part_acc = o; o = align256(o + size_t(units) * nsa * GP * D * 4);
+    w.part2_ml = o; o = align256(o + size_t(units) * ngrp * GP * 2 * 4);
+    w.part2_acc = o; o = align256(o + size_t(units) * ngrp * GP * D * 4);
     w.total = o;
     return w;
 }
@@ -161,11 +166,14 @@ struct RefineArgs {
     int32_t* idx;
     float* lse;
     uint32_t* done_a;       // [U][kCtrStride]
+    uint32_t* done_g;       // [U][ngrp][kCtrStride]: per group of kMergeGroup slices (two-level merge)
     uint2* skey;            // [U][kstride] {order key of S (0 = empty slot), id} per pool slot: id = the
                             // token, or with paged caches its row in the KV head's pool
     float* logits;          // [U][kp][LS]
     float* part_ml;         // [U][nsa][GP][2]
     float* part_acc;        // [U][nsa][GP][D]
+    float* part2_ml;        // [U][ngrp][GP][2]: group partials of the two-level merge
+    float* part2_acc;       // [U][ngrp][GP][D]
 };
 
 struct DenseArgs {
