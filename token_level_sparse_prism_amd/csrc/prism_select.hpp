@@ -282,47 +282,51 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
 
     // ---- ranks in slot order; ranks [r0, r0 + n) land in s_slot / s_tok ----
     const bool take_all_eq = need >= eq_total;  // every key equal to tau is taken: select key >= tau
-    if (ntiles == 1 && take_all_eq) {
-        // one tile: per row, two wave ballots give every slot's rank among the wave's slots; the
-        // waves' counts per row are exchanged once and prefixed with a 16-lane DPP scan
+    if (take_all_eq) {
+        // every selected key is >= tau: per row, two wave ballots give every slot's rank among the
+        // wave's slots; the waves' counts per row are exchanged once per tile and prefixed with a
+        // 16-lane DPP scan; tiles follow one another in slot order
         static_assert(NW <= 16 && ROWS * NW <= sel_tmp_words<NT>(), "wave counts fit s_tmp");
-        uint64_t m0[ROWS], m1[ROWS];
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            m0[r] = ballot64(kv[r].x >= tau);
-            m1[r] = ballot64(kv[r].z >= tau);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int r = 0; r < ROWS; ++r) s_tmp[r * NW + wave] = uint32_t(__popcll(m0[r]) + __popcll(m1[r]));
-        }
-        __syncthreads();
         uint32_t base = 0;
         const int wu = __builtin_amdgcn_readfirstlane(wave);
+        for (int t = 0; t < ntiles && base < uint32_t(r0 + n); ++t) {
+            if (t > 0) sel_load_tile<NT>(gk, kp, int64_t(t) * kSelTile, kv);
+            uint64_t m0[ROWS], m1[ROWS];
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            uint32_t x = lane < NW ? s_tmp[r * NW + lane] : 0u;
-            x += dpp_u32<0x111>(x);
-            x += dpp_u32<0x112>(x);
-            x += dpp_u32<0x114>(x);
-            x += dpp_u32<0x118>(x);
-            const uint32_t before = wu > 0 ? readlane_u32(x, wu - 1) : 0u;
-            const uint32_t rank0 = base + before + lanes_below(m0[r]) + lanes_below(m1[r]);
-            const bool s0 = kv[r].x >= tau, s1 = kv[r].z >= tau;
-            const int32_t slot0 = int32_t(r * 2 * NT + tid * 2);
-            const uint32_t off0 = rank0 - uint32_t(r0);  // wraps for ranks below r0
-            const uint32_t off1 = off0 + (s0 ? 1u : 0u);
-            if (s0 && off0 < uint32_t(n)) {
-                s_slot[off0] = slot0;
-                s_tok[off0] = int32_t(kv[r].y);
+            for (int r = 0; r < ROWS; ++r) {
+                m0[r] = ballot64(kv[r].x >= tau);
+                m1[r] = ballot64(kv[r].z >= tau);
             }
-            if (s1 && off1 < uint32_t(n)) {
-                s_slot[off1] = slot0 + 1;
-                s_tok[off1] = int32_t(kv[r].w);
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r) s_tmp[r * NW + wave] = uint32_t(__popcll(m0[r]) + __popcll(m1[r]));
             }
-            base += readlane_u32(x, NW - 1);
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+                uint32_t x = lane < NW ? s_tmp[r * NW + lane] : 0u;
+                x += dpp_u32<0x111>(x);
+                x += dpp_u32<0x112>(x);
+                x += dpp_u32<0x114>(x);
+                x += dpp_u32<0x118>(x);
+                const uint32_t before = wu > 0 ? readlane_u32(x, wu - 1) : 0u;
+                const uint32_t rank0 = base + before + lanes_below(m0[r]) + lanes_below(m1[r]);
+                const bool s0 = kv[r].x >= tau, s1 = kv[r].z >= tau;
+                const int32_t slot0 = int32_t(int64_t(t) * kSelTile + r * 2 * NT + tid * 2);
+                const uint32_t off0 = rank0 - uint32_t(r0);  // wraps for ranks below r0
+                const uint32_t off1 = off0 + (s0 ? 1u : 0u);
+                if (s0 && off0 < uint32_t(n)) {
+                    s_slot[off0] = slot0;
+                    s_tok[off0] = int32_t(kv[r].y);
+                }
+                if (s1 && off1 < uint32_t(n)) {
+                    s_slot[off1] = slot0 + 1;
+                    s_tok[off1] = int32_t(kv[r].w);
+                }
+                base += readlane_u32(x, NW - 1);
+            }
+            __syncthreads();  // s_tmp is rewritten by the next tile
         }
-        __syncthreads();
         return res;
     }
     // per-row counts of one thread are at most 2, two rows share a 32-bit word (16 bits each)
