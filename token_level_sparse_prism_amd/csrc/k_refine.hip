@@ -165,11 +165,10 @@ __global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
     }
 }
 
-template <typename T, int D, int GP>
+template <typename T, int D, int GP, int NR>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     constexpr int NT = kAttendThreads;
     constexpr int NW = NT / 64;
-    constexpr int NR = kAttendRanks;
     constexpr int LS = GP < 4 ? 4 : GP;
     static_assert(kHistPadded <= kRowsAccFloats && kSelHistWords <= kRowsAccFloats, "LDS buffer too small");
     __shared__ __align__(16) uint32_t s_big[kRowsAccFloats];  // selection histograms, then the waves' V partials
@@ -245,11 +244,29 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     if (tid == 0) a.done_a[int64_t(unit) * kCtrStride] = 0u;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <typename T, int D, int GP>
 static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t st) {
     const int units = a.d.B * a.d.Hkv;
     const dim3 gs((a.kp + kScoreSlice - 1) / kScoreSlice, units);
-    const dim3 ga((a.kappa + kAttendRanks - 1) / kAttendRanks, units);
+    // one attention workgroup fits a CU: when 128 ranks per workgroup would need more workgroups
+    // than there are CUs, take 256 ranks each (half the workgroups, twice the rows each)
+    const int64_t n128 = int64_t(units) * ((a.kappa + kAttendRanks - 1) / kAttendRanks);
+    const bool wide = n128 > device_cus();
+    const int nr = wide ? 2 * kAttendRanks : kAttendRanks;
+    const dim3 ga((a.kappa + nr - 1) / nr, units);
     if constexpr (sizeof(T) == 2) {
         if (agg_max) launch_k("k_rscore", (k_rscore_mfma<D, GP, true>), gs, dim3(kThreads), st, a);
         else launch_k("k_rscore", (k_rscore_mfma<D, GP, false>), gs, dim3(kThreads), st, a);
@@ -260,7 +277,8 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
-        launch_k("k_attend", (k_attend<T, D, GP>), ga, dim3(kAttendThreads), st, a);
+        if (wide) launch_k("k_attend", (k_attend<T, D, GP, 2 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
+        else launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks>), ga, dim3(kAttendThreads), st, a);
     }
     return hipGetLastError();
 }
