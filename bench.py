@@ -58,7 +58,7 @@ def parse():
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for name in ("k_propose.hip", "prism_device.hpp", "prism_internal.hpp"):
+    for name in ("scan_kernel.hpp", "k_scan8.hip", "prism_device.hpp", "prism_internal.hpp"):
         with open(os.path.join(ROOT, "token_level_sparse_prism_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
