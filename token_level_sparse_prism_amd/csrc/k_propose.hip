@@ -58,7 +58,13 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
         for (int i = 0; i < 4; ++i) k[i] = tid * 4 + i < nvalid ? keys[tid * 4 + i] : 0u;
     }
     uint32_t h[16];
-    load_hist_desc(a.hist1 + int64_t(unit) * kHistBins, h);
+    load_hist_desc(a.hist1 + int64_t(unit) * a.hist_rep * kHistBins, h);
+    for (int r = 1; r < a.hist_rep; ++r) {  // the scan spread the histogram over hist_rep copies
+        uint32_t hr[16];
+        load_hist_desc(a.hist1 + (int64_t(unit) * a.hist_rep + r) * kHistBins, hr);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) h[k] += hr[k];
+    }
     find_crossing_regs<16>(h, kHistBins, uint32_t(kp_eff), s_tmp, s_res);
     const uint32_t bin = s_res[0];
     if (chunk == 0 && tid == 0) {
@@ -102,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_compact: grid (chunks, units).  Chunk 0 also writes the -1 padding and clears hist1.
+// k_compact: grid (chunks, units).  Chunk 0 also writes the -1 padding; every chunk clears its
+// slice of hist1.
 __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
     __shared__ uint32_t s_tmp[kThreads / 64 * 5];
     __shared__ uint32_t s_res[4];
@@ -124,8 +131,13 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 
     if (chunk == 0) {
         for (int64_t j = kp_eff + tid; j < a.kp; j += kThreads) pool[j] = -1;
-        uint32_t* h1 = a.hist1 + int64_t(unit) * kHistBins;
-        for (int i = tid; i < kHistBins; i += kThreads) h1[i] = 0u;  // zero for the next call
+    }
+    {  // the unit's histogram copies are zeroed for the next call, a slice per chunk
+        const int words = kHistBins * a.hist_rep;
+        const int per = (words + a.nchunks - 1) / a.nchunks;
+        uint32_t* h1 = a.hist1 + int64_t(unit) * words;
+        const int w1 = (chunk + 1) * per < words ? (chunk + 1) * per : words;
+        for (int i = chunk * per + tid; i < w1; i += kThreads) h1[i] = 0u;
     }
     if (Tb == 0 || nvalid == 0) return;
     if (kp_eff == Tb) {  // take all
@@ -248,8 +260,10 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 hipError_t launch_scan8(const ProposeArgs& a, int agg_max, hipStream_t st);
 hipError_t launch_scan2(const ProposeArgs& a, int agg_max, hipStream_t st);
 
-hipError_t launch_propose(const ProposeArgs& a, int agg_max, hipStream_t st) {
+hipError_t launch_propose(const ProposeArgs& args, int agg_max, hipStream_t st) {
+    ProposeArgs a = args;
     const int units = a.d.B * a.d.Hkv;
+    a.hist_rep = scan_plan(units, a.d.T_max, a.nchunks).rep;
     const dim3 grid(a.nchunks, units);
     hipError_t e = a.key_bits == 2 ? launch_scan2(a, agg_max, st) : launch_scan8(a, agg_max, st);
     if (e != hipSuccess) return e;

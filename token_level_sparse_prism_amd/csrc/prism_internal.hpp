@@ -20,6 +20,7 @@ constexpr int kChunk = 1024;           // tokens per chunk in the proposal kerne
 constexpr int kScanWgs = PRISM_SCAN_WGS;
 constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in pool scoring
 constexpr int kAttendRanks = 128;      // selected rows per workgroup in sparse attention
+constexpr int kHistRep = 8;            // most copies of a unit's key histogram (see ScanPlan)
 constexpr int kMergeGroup = 16;        // partials merged by one workgroup (two levels above it)
 constexpr int kAttendThreads = 1024;   // 16 waves: the selection's latency is shared by 4 waves per SIMD
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
@@ -44,6 +45,24 @@ inline int64_t cand_list_cap(int64_t T_max) {
     return (nch + kCandLists - 1) / kCandLists * kChunk;
 }
 
+// The proposal scan's grid: about kScanWgs workgroups over all units, each taking work items of
+// `ch` tokens (1024, or 256 when 1024-token items would give fewer than kScanWgs workgroups), and
+// the unit's key histogram spread over `rep` copies, one per 256 of its workgroups, so that at
+// most about 256 workgroups add into one copy's busiest bins.
+struct ScanPlan {
+    int ch, per_unit, rep;
+};
+inline ScanPlan scan_plan(int units, int64_t T_max, int nchunks) {
+    ScanPlan p;
+    p.ch = int64_t(units) * nchunks < kScanWgs ? 256 : kChunk;
+    const int nch = int((T_max + p.ch - 1) / p.ch);
+    int per_unit = (kScanWgs + units - 1) / units;
+    p.per_unit = per_unit < 1 ? 1 : (per_unit > nch ? nch : per_unit);
+    p.rep = (p.per_unit + 255) / 256;
+    p.rep = p.rep < 1 ? 1 : (p.rep > kHistRep ? kHistRep : p.rep);
+    return p;
+}
+
 struct ProposeWs {
     size_t hist1, ctrl_bytes;
     size_t hist2, cand_cnt, state, cnt_gt, keys, cand, total;
@@ -55,7 +74,7 @@ inline ProposeWs propose_ws(int64_t units, int64_t T_max) {
     ProposeWs w{};
     const int64_t nch = (T_max + kChunk - 1) / kChunk;
     size_t o = 0;
-    w.hist1 = o;     o = align256(o + size_t(units) * kHistBins * 4);
+    w.hist1 = o;     o = align256(o + size_t(units) * scan_plan(int(units), T_max, int((T_max + kChunk - 1) / kChunk)).rep * kHistBins * 4);
     w.ctrl_bytes = o;
     w.hist2 = o;     o = align256(o + size_t(units) * kHistBins * 4);
     w.cand_cnt = o;  o = align256(o + size_t(units) * kCandLists * kCtrStride * 4);
@@ -143,7 +162,8 @@ struct ProposeArgs {
     int64_t kstride;        // key_stride(T_max)
     int32_t* pool;
     float* scores;          // optional
-    uint32_t* hist1;        // [U][kHistBins]  top 12 bits of every key
+    uint32_t* hist1;        // [U][hist_rep][kHistBins]  top 12 bits of every key
+    int hist_rep;           // copies of hist1 the scan spreads its workgroups over (1 .. kHistRep)
     uint32_t* hist2;        // [U][kHistBins]  bits 19..8 of the keys in the threshold bin
     uint32_t* cand_cnt;     // [U][kCandLists][kCtrStride]
     int64_t cand_cap;       // cand_list_cap(T_max)

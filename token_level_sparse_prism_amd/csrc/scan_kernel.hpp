@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         }
         __syncthreads();
     }
-    uint32_t* gh = a.hist1 + int64_t(unit) * kHistBins;
+    uint32_t* gh = a.hist1 + (int64_t(unit) * a.hist_rep + ui.x % a.hist_rep) * kHistBins;
     for (int i = tid; i < kHistBins; i += kThreads) {
         const uint32_t c = s_hist[i];
         if (c) atomicAdd(&gh[i], c);
@@ -354,19 +354,13 @@ static hipError_t launch_scan_ch(const ProposeArgs& a, int agg_max, dim3 grid, h
     return launch_scan_p<D, KB, 1, CH>(a, agg_max, grid, st);
 }
 
-// The scan's grid: about kScanWgs workgroups over all units, each taking work items of CH tokens;
-// items of 256 tokens when 1024-token items would give fewer than kScanWgs workgroups and a unit
-// has at most 64 of them (every workgroup of a unit adds its histogram into the unit's, so more
-// than 256 workgroups per unit contend on its busiest bins).
+// The scan's launch for the grid of scan_plan (the caller sets a.hist_rep from the same plan).
 template <int KB>
 hipError_t launch_scan_kb(const ProposeArgs& a, int agg_max, hipStream_t st) {
     const int units = a.d.B * a.d.Hkv;
-    const bool small = int64_t(units) * a.nchunks < kScanWgs && a.nchunks <= 64;
-    const int ch = small ? 256 : kChunk;
-    const int nch = int((a.d.T_max + ch - 1) / ch);
-    int per_unit = (kScanWgs + units - 1) / units;
-    per_unit = per_unit < 1 ? 1 : (per_unit > nch ? nch : per_unit);
-    const dim3 grid(per_unit, units);
+    const ScanPlan pl = scan_plan(units, a.d.T_max, a.nchunks);
+    const bool small = pl.ch != kChunk;
+    const dim3 grid(pl.per_unit, units);
     switch (a.d.D) {
         case 64: return small ? launch_scan_ch<64, KB, 256>(a, agg_max, grid, st) : launch_scan_ch<64, KB, kChunk>(a, agg_max, grid, st);
         case 128: return small ? launch_scan_ch<128, KB, 256>(a, agg_max, grid, st) : launch_scan_ch<128, KB, kChunk>(a, agg_max, grid, st);
