@@ -9,6 +9,9 @@
 namespace prism {
 
 // ---- tiling constants --------------------------------------------------------------------
+#ifndef PRISM_HIST_WGS
+#define PRISM_HIST_WGS 256             // scan workgroups per copy of a unit's key histogram
+#endif
 #ifndef PRISM_SCAN_WGS
 #define PRISM_SCAN_WGS 1024            // target scan workgroups over all units
 #endif
@@ -58,7 +61,7 @@ inline ScanPlan scan_plan(int units, int64_t T_max, int nchunks) {
     const int nch = int((T_max + p.ch - 1) / p.ch);
     int per_unit = (kScanWgs + units - 1) / units;
     p.per_unit = per_unit < 1 ? 1 : (per_unit > nch ? nch : per_unit);
-    p.rep = (p.per_unit + 255) / 256;
+    p.rep = (p.per_unit + PRISM_HIST_WGS - 1) / PRISM_HIST_WGS;
     p.rep = p.rep < 1 ? 1 : (p.rep > kHistRep ? kHistRep : p.rep);
     return p;
 }
