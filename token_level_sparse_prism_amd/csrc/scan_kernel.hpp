@@ -99,8 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     static_assert(ROUNDS % U == 0, "chunk must hold whole unrolled rounds");
 
     __shared__ uint32_t s_hist[kHistBins];
-    __shared__ uint32_t s_key[CH];
-    __shared__ float s_scale[CH];
+    __shared__ uint32_t s_key[CH];  // the chunk's aggregated int32 dot products, then nothing
     __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
     __shared__ float s_red[kThreads / 64];
     __shared__ int32_t s_pg[kPaged ? CH : 1];  // paged: the physical pages of the chunk's tokens
@@ -114,17 +113,14 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     const int64_t Tb = seq_len_of(d, b);
     const int nch = int((d.T_max + CH - 1) / CH);  // work items of CH tokens per unit
 
-    if (ui.x == 0) {  // per-call state of the later kernels
-        uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
-        for (int i = tid; i < kHistBins; i += kThreads) h2[i] = 0u;
-        if (tid < kCandLists) a.cand_cnt[(int64_t(unit) * kCandLists + tid) * kCtrStride] = 0u;
-    }
     const int sub = lane % LPT;
     const int tok_lane = wave * TPW + lane / LPT;
 
     // ---- query quantization: one absmax over the group's G*D values (s_hist holds q meanwhile).
     // Loads complete in issue order, so the small query and scale loads go out before the first
-    // chunk's key rows, which then stream in while the codes are computed.
+    // chunk's key rows, which then stream in while the codes are computed.  The scales stay in
+    // registers until the chunk's keys are formed after the streaming loop, so the prologue
+    // waits for the query alone.
     float* s_qf = reinterpret_cast<float*>(s_hist);
     const int64_t qoff = (int64_t(b) * d.Hq + int64_t(g) * G) * D;
     const int qe = a.q_bf16 ? 8 : 4;  // values per 16-byte piece
@@ -164,16 +160,18 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         fill_pages(c0, nvalid);
         __syncthreads();
     }
-    float scl_pre[CH / kThreads];
-    {
-        const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
+    // scl[i]: the scale of token c0 + tid + i * kThreads of the current chunk
+    float scl[CH / kThreads];
+    auto load_scales = [&]() {
+        const float* sc = a.scales + int64_t(unit) * d.T_max + c0;
 #pragma unroll
         for (int i = 0; i < CH / kThreads; ++i) {
             const int t = tid + i * kThreads;
-            if constexpr (paged) scl_pre[i] = t < nvalid ? sc_head[paged_slot(c0 + t)] : 0.0f;
-            else scl_pre[i] = t < nvalid ? scl[t] : 0.0f;
+            if constexpr (paged) scl[i] = t < nvalid ? sc_head[paged_slot(c0 + t)] : 0.0f;
+            else scl[i] = t < nvalid ? sc[t] : 0.0f;
         }
-    }
+    };
+    load_scales();
     // rolling buffer of U rows per lane: a register is refilled with the row U rounds ahead as
     // soon as it has been used, so about U loads stay in flight through the whole chunk
     typename SR::R kv[U];
@@ -192,6 +190,11 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     };
 #pragma unroll
     for (int u = 0; u < U; ++u) kv[u] = load_row(u);
+    if (ui.x == 0) {  // per-call state of the later kernels
+        uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
+        for (int i = tid; i < kHistBins; i += kThreads) h2[i] = 0u;
+        if (tid < kCandLists) a.cand_cnt[(int64_t(unit) * kCandLists + tid) * kCtrStride] = 0u;
+    }
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
@@ -246,8 +249,6 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         c3[n] = -3 * qs;
     }
     for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;  // q is in registers now
-#pragma unroll
-    for (int i = 0; i < CH / kThreads; ++i) s_scale[tid + i * kThreads] = scl_pre[i];
     __syncthreads();
 
     bool first = true;
@@ -263,13 +264,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
                 fill_pages(c0, nvalid);
                 __syncthreads();
             }
-            const float* scl = a.scales + int64_t(unit) * d.T_max + c0;
-#pragma unroll 4
-            for (int i = tid; i < nvalid; i += kThreads) {
-                if constexpr (paged) s_scale[i] = sc_head[paged_slot(c0 + i)];
-                else s_scale[i] = scl[i];
-            }
-            __syncthreads();
+            load_scales();
         }
 
         // ---- streaming int8 scan ----
@@ -296,24 +291,26 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
                     if constexpr (NQ == 2) acc0 = acc0 * 16 + lane_dot<KB>(qv[1], kv[u], c3[1]);
                     A = group_sum_i<LPT>(acc0);
                 }
-                if (sub == 0 && tok < nvalid) {
-                    const float score = float(A) * s_scale[tok];  // one fp32 product
-                    s_key[tok] = order_key(score);
-                }
+                if (sub == 0 && tok < nvalid) s_key[tok] = uint32_t(A);
                 if (r0 + U < ROUNDS) kv[u] = load_row(r0 + U + u);
             }
         }
         first = false;
         __syncthreads();
 
-        // ---- keys out (coalesced), top-digit histogram ----
+        // ---- scores and keys out (coalesced), top-digit histogram ----
         uint32_t* kout = a.keys + int64_t(unit) * a.kstride + c0;
         float* sout = a.scores ? a.scores + int64_t(unit) * d.T_max + c0 : nullptr;
-        for (int i = tid; i < nvalid; i += kThreads) {
-            const uint32_t k = s_key[i];
-            atomicAdd(&s_hist[k >> kKeyShift], 1u);
-            kout[i] = k;
-            if (sout) sout[i] = key_to_float(k);
+#pragma unroll
+        for (int i = 0; i < CH / kThreads; ++i) {
+            const int t = tid + i * kThreads;
+            if (t < nvalid) {
+                const float score = float(int(s_key[t])) * scl[i];  // one fp32 product
+                const uint32_t k = order_key(score);
+                atomicAdd(&s_hist[k >> kKeyShift], 1u);
+                kout[t] = k;
+                if (sout) sout[t] = key_to_float(k);
+            }
         }
         __syncthreads();
     }
