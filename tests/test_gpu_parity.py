@@ -310,6 +310,56 @@ def test_paged_matches_contiguous(case, key_bits):
     assert_pool_equal(pool_p.cpu().numpy(), oracle.propose(q, lv, osc, kp, seq_lens=lens, agg=agg))
 
 
+# ------------------------------------------------------------------ proposal on CU-filling grids
+# Shapes whose 4096-token work items give at least 256 scan workgroups (one per CU), where the
+# scan runs one 1024-thread workgroup per CU with batches claimed by its waves: ragged tails,
+# MAX aggregation, two work items per workgroup, INT2 keys, fp32 queries and paged caches (pages
+# of 4 tokens are smaller than a wave-load and take the 256-thread scan at the same grid size).
+WIDE_CASES = [
+    # D, G, Hkv, agg, dtype, T, kp, lens, key bits, page size (0: contiguous)
+    (128, 4, 8, PB.AGG_SUM, "bf16", 65536, 4096, [65536, 50001], 8, 0),
+    (128, 3, 8, PB.AGG_MAX, "bf16", 65536, 2048, None, 8, 0),
+    (64, 1, 8, PB.AGG_SUM, "f32", 131072, 1000, [131072, 77777], 8, 0),
+    (256, 2, 8, PB.AGG_SUM, "bf16", 65536, 3000, [4095, 65536], 2, 0),
+    (128, 4, 8, PB.AGG_MAX, "bf16", 65536, 1500, [65000, 65536], 2, 0),
+    (128, 4, 8, PB.AGG_SUM, "bf16", 65536, 4096, [65536, 40000], 8, 16),
+    (128, 4, 8, PB.AGG_SUM, "bf16", 65536, 2048, [65536, 33333], 2, 64),
+    (128, 4, 8, PB.AGG_SUM, "bf16", 65536, 2048, [65536, 30001], 8, 4),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"D{c[0]}G{c[1]}a{c[3]}{c[4]}T{c[5]}kb{c[8]}P{c[9]}")
+def test_propose_cu_filling_grid(case):
+    D, G, Hkv, agg, dtype, T, kp, lens, key_bits, P = case
+    Bn = len(lens) if lens else 2
+    rng = np.random.default_rng(seed_of(D, G, T, kp, key_bits, P))
+    q = rnd(rng, (Bn, G * Hkv, D), dtype)
+    K = rnd(rng, (Bn, Hkv, T, D), dtype)
+    lens = np.full(Bn, T, np.int32) if lens is None else np.asarray(lens, np.int32)
+    for b in range(Bn):
+        K[b, :, lens[b]:] = 0.0
+    ld = torch.from_numpy(lens).cuda()
+    quant = PB.quantize_keys_int2 if key_bits == 2 else PB.quantize_keys
+    qd = dev(q, dtype)
+    scores = torch.zeros((Bn, Hkv, T), dtype=torch.float32, device="cuda")
+    if P:
+        Kp, table = to_pages(K, P, rng)
+        Kq_p, sc_p = quant(dev(Kp, dtype)[None])
+        pool = PB.propose_paged(qd, Kq_p[0], sc_p[0], torch.from_numpy(table).cuda(), P, kp, agg,
+                                key_bits=key_bits, T_max=T, seq_lens=ld, scores=scores)
+    else:
+        Kq, sc = quant(dev(K, dtype), seq_lens=ld)
+        prop = PB.propose_int2 if key_bits == 2 else PB.propose
+        pool = prop(qd, Kq, sc, kp, agg, seq_lens=ld, scores=scores)
+    torch.cuda.synchronize()
+    lv, osc = (oracle.quantize_rows_int2 if key_bits == 2 else oracle.quantize_rows)(K)
+    opool, oscores = oracle.propose(q, lv, osc, kp, seq_lens=lens, agg=agg, want_scores=True)
+    gs = scores.cpu().numpy()
+    for b in range(Bn):
+        assert np.array_equal(f32_bits(gs[b, :, :lens[b]]), f32_bits(oscores[b, :, :lens[b]])), "scores differ"
+    assert_pool_equal(pool.cpu().numpy(), opool)
+
+
 # ------------------------------------------------------------------------------------- whole steps
 def run_step_gpu(w, kp, kappa, agg=PB.AGG_SUM, key_bits=8):
     from token_level_sparse_prism_amd.step import LayerInputs, PrismStep

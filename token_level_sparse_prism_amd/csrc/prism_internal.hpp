@@ -12,6 +12,9 @@ namespace prism {
 #ifndef PRISM_HIST_WGS
 #define PRISM_HIST_WGS 256             // scan workgroups per copy of a unit's key histogram
 #endif
+#ifndef PRISM_SCAN_WIDE
+#define PRISM_SCAN_WIDE 1              // one 1024-thread scan workgroup per CU on large grids
+#endif
 #ifndef PRISM_SCAN_WGS
 #define PRISM_SCAN_WGS 1024            // target scan workgroups over all units
 #endif

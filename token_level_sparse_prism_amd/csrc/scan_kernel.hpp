@@ -322,6 +322,267 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// k_scan_w: the same scan for grids that give every CU a workgroup, one 1024-thread workgroup per
+// CU.  A work item of CHW tokens is cut into batches of U wave-loads (U * TPW consecutive tokens);
+// wave w starts on batch w and then takes the next unclaimed batch from an LDS counter.  The
+// waves that a CU serves first take more batches, so its waves finish together instead of the
+// CU's last-dispatched waves setting the end.  Paging needs pages of at least TPW tokens (a
+// wave-load then lies in one page, whose base is a scalar).
+constexpr int kScanWideThreads = 1024;
+constexpr int kScanWideChunk = 4096;
+
+template <int D, int NQ, bool kMax, int KB, int kPg, int CHW>
+__global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
+    constexpr int NT = kScanWideThreads;
+    constexpr int NW = NT / 64;
+    constexpr bool paged = kPg != 0;
+    static_assert(kPg != 1, "pages smaller than a wave-load use k_scan");
+    constexpr int DPL = (KB == 2 && NQ <= 2) ? 64 : 16;
+    using SR = ScanRow<KB, DPL>;
+    constexpr int QW = DPL / 4;
+    constexpr int LPT = D / DPL;
+    constexpr int TPW = 64 / LPT;          // tokens per wave-load
+    constexpr int U = KB == 8 ? SR::kLoads : (NQ <= 2 ? SR::kLoads : (NQ <= 8 ? SR::kLoads / 2 : SR::kLoads / 4));
+    constexpr int BT = U * TPW;            // tokens per batch
+    static_assert(CHW % BT == 0 && CHW / BT >= NW, "every wave starts on a batch of its own");
+    constexpr int RB = D * KB / 8;
+
+    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ uint32_t s_key[CHW];  // the work item's aggregated int32 dot products
+    __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
+    __shared__ float s_red[NW];
+    __shared__ int32_t s_pg[paged ? CHW / TPW + 2 : 1];
+    __shared__ uint32_t s_next;
+
+    const Dims& d = a.d;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
+    const int b = unit / d.Hkv, g = unit % d.Hkv;
+    const int G = d.G;
+    const int64_t Tb = seq_len_of(d, b);
+    const int nch = int((d.T_max + CHW - 1) / CHW);
+    const int sub = lane % LPT;
+    const int tl = lane / LPT;             // the lane's token inside a wave-load
+
+    // Every global load below is unconditional, at a clamped in-bounds address, and loads past
+    // the work item's tokens are simply not used: a load under a branch makes the compiler merge
+    // its wait counts with the path that skips it, and the merged counts wait for loads that are
+    // still streaming.  For the same reason the per-call zeroing goes before the first load.
+    if (ui.x == 0) {  // per-call state of the later kernels
+        uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
+        for (int i = tid; i < kHistBins; i += NT) h2[i] = 0u;
+        if (tid < kCandLists) a.cand_cnt[(int64_t(unit) * kCandLists + tid) * kCtrStride] = 0u;
+    }
+    float* s_qf = reinterpret_cast<float*>(s_hist);
+    const int64_t qoff = (int64_t(b) * d.Hq + int64_t(g) * G) * D;
+    const int qe = a.q_bf16 ? 8 : 4;
+    constexpr int QP = (kMaxG * 256 / 4 + NT - 1) / NT;
+    uint4 qraw[QP];
+    const int npieces = G * D / qe;
+#pragma unroll
+    for (int i = 0; i < QP; ++i) {
+        const int p = min(tid + i * NT, npieces - 1);
+        qraw[i] = load16(static_cast<const uint8_t*>(a.q) + (qoff * (a.q_bf16 ? 2 : 4)) + p * 16);
+    }
+    int chunk = ui.x;  // < nch: the grid has at most nch workgroups per unit
+    int64_t c0 = int64_t(chunk) * CHW;
+    int nvalid = scan_chunk_tokens<CHW>(Tb, c0);
+    int last = nvalid > 0 ? nvalid - 1 : 0;  // clamp for loads (token c0 + 0 exists: c0 < T_max)
+    const int lp = d.pg.log2p;
+    const int64_t npool = d.pg.slots >> lp;
+    auto fill_pages = [&]() {  // the work item's pages, clamped into the pool (page 0 if none)
+        const int64_t p0 = c0 >> lp;
+        const int npg = int(((c0 + last) >> lp) - p0 + 1);
+        for (int i = tid; i < npg; i += NT) {
+            int64_t pg = nvalid > 0 ? d.pg.table[int64_t(b) * d.pg.max_pages + p0 + i] : 0;
+            s_pg[i] = int32_t(pg < 0 ? 0 : (pg >= npool ? npool - 1 : pg));
+        }
+    };
+    const int8_t* kq_head = a.Kq + int64_t(g) * d.pg.slots * RB;
+    const float* sc_head = a.scales + int64_t(g) * d.pg.slots;
+    const uint32_t lane_off = uint32_t(tl * RB + sub * (RB / LPT));
+    if constexpr (paged) {
+        fill_pages();
+        __syncthreads();
+    }
+    float scl[CHW / NT];
+    auto load_scales = [&]() {
+        const float* sc = a.scales + int64_t(unit) * d.T_max + c0;
+#pragma unroll
+        for (int i = 0; i < CHW / NT; ++i) {
+            const int t = min(tid + i * NT, last);
+            if constexpr (paged) {
+                const int64_t tt = c0 + t;
+                scl[i] = sc_head[(int64_t(s_pg[(tt >> lp) - (c0 >> lp)]) << lp) + (tt & ((int64_t(1) << lp) - 1))];
+            } else {
+                scl[i] = sc[t];
+            }
+        }
+    };
+    // wave-load `it` of the work item: tokens c0 + it * TPW + [0, TPW), clamped to the last token
+    // (paged: to the last token's wave-load, which lies in one page)
+    auto load_item = [&](int it) -> typename SR::R {
+        if constexpr (paged) {
+            const int i0 = min(it * TPW, last & ~(TPW - 1));
+            const int64_t t0 = c0 + i0;
+            const int64_t pg = __builtin_amdgcn_readfirstlane(s_pg[(t0 >> lp) - (c0 >> lp)]);
+            return SR::load(kq_head + ((pg << lp) + (t0 & ((int64_t(1) << lp) - 1))) * RB + lane_off);
+        } else {
+            const int tok = min(it * TPW + tl, last);
+            return SR::load(a.Kq + (int64_t(unit) * d.T_max + c0 + tok) * RB + sub * (RB / LPT));
+        }
+    };
+    load_scales();
+    int nb = (nvalid + BT - 1) / BT;  // batches holding tokens
+    int bcur = wave;                  // wave w starts on batch w
+    typename SR::R kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kv[u] = load_item(bcur * U + u);
+    if (tid == 0) s_next = NW;
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QP; ++i) {
+        const int p = tid + i * NT;
+        float x[8];
+        if (a.q_bf16) unpack16<uint16_t>(qraw[i], x);
+        else unpack16<float>(qraw[i], x);
+        if (p < npieces) {
+            for (int e = 0; e < qe; ++e) {
+                s_qf[p * qe + e] = x[e];
+                amax = fmaxf(amax, fabsf(x[e]));
+            }
+        }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) s_red[wave] = amax;
+    __syncthreads();
+    amax = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) amax = fmaxf(amax, s_red[w]);
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    auto code = [&](float x) -> int {
+        float r = __builtin_rintf(x * inv);
+        return int(fminf(fmaxf(r, -127.0f), 127.0f));
+    };
+    for (int dd = tid; dd < D; dd += NT) {
+        if constexpr (kMax) {
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) s_q[h][dd] = int8_t(h < G ? code(s_qf[h * D + dd]) : 0);
+        } else if constexpr (NQ == 1) {
+            s_q[0][dd] = int8_t(code(s_qf[dd]));
+        } else {
+            int qs = 0;
+            for (int h = 0; h < G; ++h) qs += code(s_qf[h * D + dd]);
+            const int lo = ((qs + 8) & 15) - 8;
+            const int hi = (qs - lo) >> 4;
+            s_q[0][dd] = int8_t(hi);
+            s_q[1][dd] = int8_t(lo);
+        }
+    }
+    __syncthreads();
+    int qv[NQ][QW];
+    int c3[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        int qs = 0;
+#pragma unroll
+        for (int m = 0; m < QW / 4; ++m) {
+            const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * DPL + 16 * m]);
+            qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
+        }
+#pragma unroll
+        for (int i = 0; i < QW; ++i) qs = __builtin_amdgcn_sdot4(qv[n][i], 0x01010101, qs, false);
+        c3[n] = -3 * qs;
+    }
+    for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+    __syncthreads();
+
+    auto claim = [&]() -> int {
+        uint32_t v = 0u;
+        if (lane == 0) v = atomicAdd(&s_next, 1u);
+        return __builtin_amdgcn_readfirstlane(int(v));
+    };
+    // the wave's rows of batch bcur are in kv: aggregate them into s_key
+    auto consume = [&](int u) {
+        const int tok = (bcur * U + u) * TPW + tl;
+        int A;
+        if constexpr (kMax) {
+            int best = 0;
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) {
+                const int acc = group_sum_i<LPT>(lane_dot<KB>(qv[h], kv[u], c3[h]));
+                if (h < G) best = (h == 0 || acc > best) ? acc : best;
+            }
+            A = best;
+        } else {
+            int acc0 = lane_dot<KB>(qv[0], kv[u], c3[0]);
+            if constexpr (NQ == 2) acc0 = acc0 * 16 + lane_dot<KB>(qv[1], kv[u], c3[1]);
+            A = group_sum_i<LPT>(acc0);
+        }
+        if (sub == 0 && tok < nvalid) s_key[tok] = uint32_t(A);
+    };
+    for (;;) {  // work items of this workgroup; the rows of its first batch per wave are in flight
+        if (nvalid == 0) break;  // later work items are past T_b too
+        nb = __builtin_amdgcn_readfirstlane(nb);
+        int bnext = claim();
+        while (bnext < nb) {
+            const int bfut = claim();  // the batch after, claimed one batch ahead
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                consume(u);
+                kv[u] = load_item(bnext * U + u);
+            }
+            bcur = bnext;
+            bnext = bfut;
+        }
+        if (bcur < nb) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) consume(u);
+        }
+        __syncthreads();
+
+        uint32_t* kout = a.keys + int64_t(unit) * a.kstride + c0;
+        float* sout = a.scores ? a.scores + int64_t(unit) * d.T_max + c0 : nullptr;
+#pragma unroll
+        for (int i = 0; i < CHW / NT; ++i) {
+            const int t = tid + i * NT;
+            if (t < nvalid) {
+                const float score = float(int(s_key[t])) * scl[i];  // one fp32 product
+                const uint32_t k = order_key(score);
+                atomicAdd(&s_hist[k >> kKeyShift], 1u);
+                kout[t] = k;
+                if (sout) sout[t] = key_to_float(k);
+            }
+        }
+        if (tid == 0) s_next = NW;  // the next work item's claims start after the barrier
+        __syncthreads();
+
+        chunk += gridDim.x;
+        if (chunk >= nch) break;
+        c0 = int64_t(chunk) * CHW;
+        nvalid = scan_chunk_tokens<CHW>(Tb, c0);
+        if (nvalid == 0) break;
+        last = nvalid - 1;
+        if constexpr (paged) {
+            fill_pages();
+            __syncthreads();
+        }
+        load_scales();
+        nb = (nvalid + BT - 1) / BT;
+        bcur = wave;
+#pragma unroll
+        for (int u = 0; u < U; ++u) kv[u] = load_item(bcur * U + u);
+    }
+    uint32_t* gh = a.hist1 + (int64_t(unit) * a.hist_rep + ui.x % a.hist_rep) * kHistBins;
+    for (int i = tid; i < kHistBins; i += NT) {
+        const uint32_t c = s_hist[i];
+        if (c) atomicAdd(&gh[i], c);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 template <int D, int KB, int P, int CH>
 static hipError_t launch_scan_p(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
     const int G = a.d.G;
@@ -351,9 +612,62 @@ static hipError_t launch_scan_ch(const ProposeArgs& a, int agg_max, dim3 grid, h
     return launch_scan_p<D, KB, 1, CH>(a, agg_max, grid, st);
 }
 
-// The scan's launch for the grid of scan_plan (the caller sets a.hist_rep from the same plan).
+template <int D, int KB, int P>
+static hipError_t launch_scan_w_p(const ProposeArgs& a, int agg_max, dim3 grid, hipStream_t st) {
+    constexpr int C = kScanWideChunk;
+    const dim3 blk(kScanWideThreads);
+    const int G = a.d.G;
+    if (!agg_max) {
+        if (G == 1) launch_k("k_scan", (k_scan_w<D, 1, false, KB, P, C>), grid, blk, st, a);
+        else launch_k("k_scan", (k_scan_w<D, 2, false, KB, P, C>), grid, blk, st, a);
+    } else {
+        switch (padded_g(G)) {
+            case 1: launch_k("k_scan", (k_scan_w<D, 1, true, KB, P, C>), grid, blk, st, a); break;
+            case 2: launch_k("k_scan", (k_scan_w<D, 2, true, KB, P, C>), grid, blk, st, a); break;
+            case 4: launch_k("k_scan", (k_scan_w<D, 4, true, KB, P, C>), grid, blk, st, a); break;
+            default: return hipErrorInvalidValue;  // launch_scan_wide leaves G > 4 to k_scan
+        }
+    }
+    return hipGetLastError();
+}
+
+// The wide scan when its work items give at least one workgroup per CU (kScanWgs / 4 of them)
+// and any pages hold a whole wave-load; returns false when the caller should use k_scan.
+template <int KB>
+static bool launch_scan_wide(const ProposeArgs& a, int agg_max, hipStream_t st, hipError_t* err) {
+#if PRISM_SCAN_WIDE
+    const int units = a.d.B * a.d.Hkv;
+    const int64_t nchw = (a.d.T_max + kScanWideChunk - 1) / kScanWideChunk;
+    constexpr int wgs = kScanWgs / 4;
+    if (int64_t(units) * nchw < wgs) return false;
+    const int nq = agg_max ? padded_g(a.d.G) : (a.d.G == 1 ? 1 : 2);
+    if (nq > 4) return false;  // more query vectors than 128 registers per lane hold
+    const int dpl = (KB == 2 && nq <= 2) ? 64 : 16;
+    const int tpw = 64 * dpl / a.d.D;  // tokens per wave-load
+    if (a.d.pg.table && (1 << a.d.pg.log2p) < tpw) return false;
+    int per_unit = (wgs + units - 1) / units;
+    per_unit = per_unit < 1 ? 1 : (per_unit > nchw ? int(nchw) : per_unit);
+    const dim3 grid(per_unit, units);
+    const bool pg = a.d.pg.table != nullptr;
+    switch (a.d.D) {
+        case 64: *err = pg ? launch_scan_w_p<64, KB, 2>(a, agg_max, grid, st) : launch_scan_w_p<64, KB, 0>(a, agg_max, grid, st); break;
+        case 128: *err = pg ? launch_scan_w_p<128, KB, 2>(a, agg_max, grid, st) : launch_scan_w_p<128, KB, 0>(a, agg_max, grid, st); break;
+        case 256: *err = pg ? launch_scan_w_p<256, KB, 2>(a, agg_max, grid, st) : launch_scan_w_p<256, KB, 0>(a, agg_max, grid, st); break;
+        default: *err = hipErrorInvalidValue;
+    }
+    return true;
+#else
+    (void)a; (void)agg_max; (void)st; (void)err;
+    return false;
+#endif
+}
+
+// The scan's launch: the wide scan where it applies, else k_scan on the grid of scan_plan (the
+// caller sets a.hist_rep from the same plan; a smaller grid only leaves copies unused).
 template <int KB>
 hipError_t launch_scan_kb(const ProposeArgs& a, int agg_max, hipStream_t st) {
+    hipError_t err = hipSuccess;
+    if (launch_scan_wide<KB>(a, agg_max, st, &err)) return err;
     const int units = a.d.B * a.d.Hkv;
     const ScanPlan pl = scan_plan(units, a.d.T_max, a.nchunks);
     const bool small = pl.ch != kChunk;
