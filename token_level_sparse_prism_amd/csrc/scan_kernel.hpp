@@ -84,7 +84,7 @@ __device__ __forceinline__ int lane_dot(const int* qw, uint32_t w, int c3) {
 // CH: tokens per workgroup work item (1024, or 256 for small grids; see launch_scan_kb).
 template <int D, int NQ, bool kMax, int KB, int kPg, int CH>
 __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
-    constexpr bool kPaged = kPg != 0;
+    constexpr bool paged = kPg != 0;       // rows through the page table (d.pg.table != nullptr)
     constexpr int DPL = (KB == 2 && NQ <= 2) ? 64 : 16;  // dims per lane
     using SR = ScanRow<KB, DPL>;
     constexpr int QW = DPL / 4;            // q words per vector and lane
@@ -99,10 +99,10 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     static_assert(ROUNDS % U == 0, "chunk must hold whole unrolled rounds");
 
     __shared__ uint32_t s_hist[kHistBins];
-    __shared__ uint32_t s_key[CH];  // the chunk's aggregated int32 dot products, then nothing
+    __shared__ uint32_t s_key[CH];  // the chunk's aggregated int32 dot products
     __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
     __shared__ float s_red[kThreads / 64];
-    __shared__ int32_t s_pg[kPaged ? CH : 1];  // paged: the physical pages of the chunk's tokens
+    __shared__ int32_t s_pg[paged ? CH : 1];  // paged: the physical pages of the chunk's tokens
 
     const Dims& d = a.d;
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -112,9 +112,18 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     const int G = d.G;
     const int64_t Tb = seq_len_of(d, b);
     const int nch = int((d.T_max + CH - 1) / CH);  // work items of CH tokens per unit
-
     const int sub = lane % LPT;
     const int tok_lane = wave * TPW + lane / LPT;
+
+    // Every global load below is unconditional, at a clamped in-bounds address, and loads past
+    // the chunk's tokens are simply not used: a load under a branch makes the compiler merge its
+    // wait counts with the path that skips it, and the merged counts wait for loads that are still
+    // streaming.  For the same reason the per-call zeroing goes before the first load.
+    if (ui.x == 0) {  // per-call state of the later kernels
+        uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
+        for (int i = tid; i < kHistBins; i += kThreads) h2[i] = 0u;
+        if (tid < kCandLists) a.cand_cnt[(int64_t(unit) * kCandLists + tid) * kCtrStride] = 0u;
+    }
 
     // ---- query quantization: one absmax over the group's G*D values (s_hist holds q meanwhile).
     // Loads complete in issue order, so the small query and scale loads go out before the first
@@ -129,23 +138,22 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     const int npieces = G * D / qe;
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
-        const int p = tid + i * kThreads;
-        qraw[i] = p < npieces ? load16(static_cast<const uint8_t*>(a.q) + (qoff * (a.q_bf16 ? 2 : 4)) + p * 16)
-                              : make_uint4(0, 0, 0, 0);
+        const int p = min(tid + i * kThreads, npieces - 1);
+        qraw[i] = load16(static_cast<const uint8_t*>(a.q) + (qoff * (a.q_bf16 ? 2 : 4)) + p * 16);
     }
-    int chunk = ui.x;
+    int chunk = ui.x;  // < nch: the grid has at most nch workgroups per unit
     int64_t c0 = int64_t(chunk) * CH;
-    int nvalid = chunk < nch ? scan_chunk_tokens<CH>(Tb, c0) : 0;
-    constexpr bool paged = kPaged;  // rows through the page table (d.pg.table != nullptr)
-    // paged: the chunk's page ids go to LDS once (clamped into the pool), and a row of the chunk is
-    // found there; pg0 = the chunk's first page, lp = log2 of the page size
+    int nvalid = scan_chunk_tokens<CH>(Tb, c0);
+    int last = nvalid > 0 ? nvalid - 1 : 0;  // clamp for loads (token c0 + 0 exists: c0 < T_max)
+    // paged: the chunk's page ids go to LDS once (clamped into the pool; page 0 for an empty
+    // chunk), and a row of the chunk is found there; lp = log2 of the page size
     const int lp = d.pg.log2p;
     const int64_t npool = d.pg.slots >> lp;
-    auto fill_pages = [&](int64_t cc0, int nv) {
-        const int64_t p0 = cc0 >> lp;
-        const int npg = nv > 0 ? int(((cc0 + nv - 1) >> lp) - p0 + 1) : 0;
+    auto fill_pages = [&]() {
+        const int64_t p0 = c0 >> lp;
+        const int npg = int(((c0 + last) >> lp) - p0 + 1);
         for (int i = tid; i < npg; i += kThreads) {
-            int64_t pg = d.pg.table[int64_t(b) * d.pg.max_pages + p0 + i];
+            int64_t pg = nvalid > 0 ? d.pg.table[int64_t(b) * d.pg.max_pages + p0 + i] : 0;
             s_pg[i] = int32_t(pg < 0 ? 0 : (pg >= npool ? npool - 1 : pg));
         }
     };
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     const uint32_t lane_off = uint32_t(tok_lane * RB + sub * (RB / LPT));  // kPg == 2: a lane's offset in a round
     const float* sc_head = a.scales + int64_t(g) * d.pg.slots;
     if constexpr (paged) {
-        fill_pages(c0, nvalid);
+        fill_pages();
         __syncthreads();
     }
     // scl[i]: the scale of token c0 + tid + i * kThreads of the current chunk
@@ -166,43 +174,42 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
         const float* sc = a.scales + int64_t(unit) * d.T_max + c0;
 #pragma unroll
         for (int i = 0; i < CH / kThreads; ++i) {
-            const int t = tid + i * kThreads;
-            if constexpr (paged) scl[i] = t < nvalid ? sc_head[paged_slot(c0 + t)] : 0.0f;
-            else scl[i] = t < nvalid ? sc[t] : 0.0f;
+            const int t = min(tid + i * kThreads, last);
+            if constexpr (paged) scl[i] = sc_head[paged_slot(c0 + t)];
+            else scl[i] = sc[t];
+        }
+    };
+    // round r of the chunk: tokens c0 + r * TPR + [0, TPR), clamped to the last token (kPg == 2:
+    // to the last token's round, which lies in one page)
+    auto load_row = [&](int r) -> typename SR::R {
+        if constexpr (kPg == 2) {
+            const int i0 = min(r * TPR, last & ~(TPR - 1));
+            const int64_t t0 = c0 + i0;
+            const int64_t pg = __builtin_amdgcn_readfirstlane(s_pg[(t0 >> lp) - (c0 >> lp)]);
+            return SR::load(kq_head + ((pg << lp) + (t0 & ((int64_t(1) << lp) - 1))) * RB + lane_off);
+        } else if constexpr (paged) {
+            const int tok = min(r * TPR + tok_lane, last);
+            return SR::load(kq_head + paged_slot(c0 + tok) * uint32_t(RB) + uint32_t(sub * (RB / LPT)));
+        } else {
+            const int tok = min(r * TPR + tok_lane, last);
+            return SR::load(a.Kq + (int64_t(unit) * d.T_max + c0 + tok) * RB + sub * (RB / LPT));
         }
     };
     load_scales();
     // rolling buffer of U rows per lane: a register is refilled with the row U rounds ahead as
     // soon as it has been used, so about U loads stay in flight through the whole chunk
     typename SR::R kv[U];
-    const int8_t* krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * RB + sub * (RB / LPT);  // this lane's first row
-    auto load_row = [&](int r) -> typename SR::R {
-        if (r * TPR + tok_lane >= nvalid) return SR::zero();
-        if constexpr (kPg == 2) {
-            const int64_t t0 = c0 + int64_t(r) * TPR;  // the round's first token, page-aligned run
-            const int64_t pg = __builtin_amdgcn_readfirstlane(s_pg[(t0 >> lp) - (c0 >> lp)]);
-            return SR::load(kq_head + ((pg << lp) + (t0 & ((int64_t(1) << lp) - 1))) * RB + lane_off);
-        } else if constexpr (paged) {
-            return SR::load(kq_head + paged_slot(c0 + r * TPR + tok_lane) * uint32_t(RB) + uint32_t(sub * (RB / LPT)));
-        } else {
-            return SR::load(krow + r * (TPR * RB));
-        }
-    };
 #pragma unroll
     for (int u = 0; u < U; ++u) kv[u] = load_row(u);
-    if (ui.x == 0) {  // per-call state of the later kernels
-        uint32_t* h2 = a.hist2 + int64_t(unit) * kHistBins;
-        for (int i = tid; i < kHistBins; i += kThreads) h2[i] = 0u;
-        if (tid < kCandLists) a.cand_cnt[(int64_t(unit) * kCandLists + tid) * kCtrStride] = 0u;
-    }
+
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
         const int p = tid + i * kThreads;
+        float x[8];
+        if (a.q_bf16) unpack16<uint16_t>(qraw[i], x);
+        else unpack16<float>(qraw[i], x);
         if (p < npieces) {
-            float x[8];
-            if (a.q_bf16) unpack16<uint16_t>(qraw[i], x);
-            else unpack16<float>(qraw[i], x);
             for (int e = 0; e < qe; ++e) {
                 s_qf[p * qe + e] = x[e];
                 amax = fmaxf(amax, fabsf(x[e]));
@@ -251,51 +258,37 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
     for (int i = tid; i < kHistBins; i += kThreads) s_hist[i] = 0u;  // q is in registers now
     __syncthreads();
 
-    bool first = true;
-    for (; chunk < nch; chunk += gridDim.x) {
-        if (!first) {
-            c0 = int64_t(chunk) * CH;
-            nvalid = scan_chunk_tokens<CH>(Tb, c0);
-            krow = a.Kq + (int64_t(unit) * d.T_max + c0 + tok_lane) * RB + sub * (RB / LPT);
-        }
-        if (nvalid == 0) break;  // later chunks of this workgroup are past T_b too
-        if (!first) {
-            if constexpr (paged) {
-                fill_pages(c0, nvalid);
-                __syncthreads();
-            }
-            load_scales();
-        }
-
-        // ---- streaming int8 scan ----
-        if (!first) {
+    // round r's row is in kv[u]: aggregate it into s_key
+    auto consume = [&](int r, int u) {
+        const int tok = r * TPR + tok_lane;
+        int A;
+        if constexpr (kMax) {
+            int best = 0;
 #pragma unroll
-            for (int u = 0; u < U; ++u) kv[u] = load_row(u);
+            for (int h = 0; h < NQ; ++h) {
+                const int acc = group_sum_i<LPT>(lane_dot<KB>(qv[h], kv[u], c3[h]));
+                if (h < G) best = (h == 0 || acc > best) ? acc : best;
+            }
+            A = best;
+        } else {
+            int acc0 = lane_dot<KB>(qv[0], kv[u], c3[0]);
+            if constexpr (NQ == 2) acc0 = acc0 * 16 + lane_dot<KB>(qv[1], kv[u], c3[1]);
+            A = group_sum_i<LPT>(acc0);
         }
+        if (sub == 0 && tok < nvalid) s_key[tok] = uint32_t(A);
+    };
+    for (;;) {  // chunks of this workgroup; the current chunk's first U rounds are in flight
+        if (nvalid == 0) break;  // later chunks of this workgroup are past T_b too
 #pragma unroll 1
-        for (int r0 = 0; r0 < ROUNDS; r0 += U) {
+        for (int r0 = 0; r0 < ROUNDS - U; r0 += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int tok = (r0 + u) * TPR + tok_lane;
-                int A;
-                if constexpr (kMax) {
-                    int best = 0;
-#pragma unroll
-                    for (int h = 0; h < NQ; ++h) {
-                        const int acc = group_sum_i<LPT>(lane_dot<KB>(qv[h], kv[u], c3[h]));
-                        if (h < G) best = (h == 0 || acc > best) ? acc : best;
-                    }
-                    A = best;
-                } else {
-                    int acc0 = lane_dot<KB>(qv[0], kv[u], c3[0]);
-                    if constexpr (NQ == 2) acc0 = acc0 * 16 + lane_dot<KB>(qv[1], kv[u], c3[1]);
-                    A = group_sum_i<LPT>(acc0);
-                }
-                if (sub == 0 && tok < nvalid) s_key[tok] = uint32_t(A);
-                if (r0 + U < ROUNDS) kv[u] = load_row(r0 + U + u);
+                consume(r0 + u, u);
+                kv[u] = load_row(r0 + U + u);
             }
         }
-        first = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) consume(ROUNDS - U + u, u);
         __syncthreads();
 
         // ---- scores and keys out (coalesced), top-digit histogram ----
@@ -313,6 +306,20 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
             }
         }
         __syncthreads();
+
+        chunk += gridDim.x;
+        if (chunk >= nch) break;
+        c0 = int64_t(chunk) * CH;
+        nvalid = scan_chunk_tokens<CH>(Tb, c0);
+        if (nvalid == 0) break;
+        last = nvalid - 1;
+        if constexpr (paged) {
+            fill_pages();
+            __syncthreads();
+        }
+        load_scales();
+#pragma unroll
+        for (int u = 0; u < U; ++u) kv[u] = load_row(u);
     }
     uint32_t* gh = a.hist1 + (int64_t(unit) * a.hist_rep + ui.x % a.hist_rep) * kHistBins;
     for (int i = tid; i < kHistBins; i += kThreads) {
