@@ -28,6 +28,20 @@ __device__ __forceinline__ int chunk_tokens(int64_t Tb, int64_t c0) {
     return int(Tb - c0 < 0 ? 0 : (Tb - c0 > kChunk ? kChunk : Tb - c0));
 }
 
+// The chunk's keys, 4 consecutive tokens per thread (0 past nvalid).  One unconditional 16-byte
+// load at a clamped offset inside the unit's kstride (c0 + 4 <= kstride, both multiples of 4):
+// a load under a branch would make the compiler wait for it before the loads after it.
+__device__ __forceinline__ void chunk_keys(const ProposeArgs& a, int unit, int64_t c0, int nvalid, uint32_t* k) {
+    const int tid = threadIdx.x;
+    const int64_t lim = a.kstride - c0 - 4;
+    const int64_t off = int64_t(tid) * 4 < lim ? int64_t(tid) * 4 : lim;
+    const uint4 v = *reinterpret_cast<const uint4*>(a.keys + int64_t(unit) * a.kstride + c0 + off);
+    k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (tid * 4 + i >= nvalid) k[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------------------------
 // k_cand: grid (chunks, units).
 __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
@@ -48,15 +62,8 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
     const int nvalid = chunk_tokens(Tb, c0);
 
     // keys of the chunk (4 consecutive tokens per thread) and the unit's top-digit histogram
-    const uint32_t* keys = a.keys + int64_t(unit) * a.kstride + c0;
     uint32_t k[4];
-    if (tid * 4 + 3 < nvalid) {
-        const uint4 v = *reinterpret_cast<const uint4*>(keys + tid * 4);
-        k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) k[i] = tid * 4 + i < nvalid ? keys[tid * 4 + i] : 0u;
-    }
+    chunk_keys(a, unit, c0, nvalid, k);
     uint32_t h[16];
     load_hist_desc(a.hist1 + int64_t(unit) * a.hist_rep * kHistBins, h);
     for (int r = 1; r < a.hist_rep; ++r) {  // the scan spread the histogram over hist_rep copies
@@ -157,19 +164,12 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
     cn = cn < uint64_t(a.cand_cap) ? cn : uint32_t(a.cand_cap);
     uint32_t h[16];
     load_hist_desc(a.hist2 + int64_t(unit) * kHistBins, h);
-    uint32_t gt_before = 0;
     const uint32_t* cg = a.cnt_gt + int64_t(unit) * a.nchunks;
-#pragma unroll 4
-    for (int i = tid; i < chunk; i += kThreads) gt_before += cg[i];
-    const uint32_t* keys = a.keys + int64_t(unit) * a.kstride + c0;
+    const uint32_t g0 = cg[tid < chunk ? tid : 0];  // unconditional (see chunk_keys)
+    uint32_t gt_before = tid < chunk ? g0 : 0u;
+    for (int i = tid + kThreads; i < chunk; i += kThreads) gt_before += cg[i];
     uint32_t k[4];
-    if (tid * 4 + 3 < nvalid) {
-        const uint4 v = *reinterpret_cast<const uint4*>(keys + tid * 4);
-        k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) k[i] = tid * 4 + i < nvalid ? keys[tid * 4 + i] : 0u;
-    }
+    chunk_keys(a, unit, c0, nvalid, k);
 
     // digit A (bits 19..8) of the threshold
     const uint32_t need_bin = uint32_t(kp_eff) - above;

@@ -119,20 +119,28 @@ __global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
     const int n = lane & 15, kg = lane >> 4;
     const int64_t j = int64_t(ui.x) * SLOTS + wave * 16 + n;
 
-    const int32_t t = j < kp ? a.pool[int64_t(unit) * kp + j] : -1;
-    const bool valid = t >= 0 && t < Tb;
-    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (int64_t(b) * d.Hq + int64_t(g) * G + n) * D + 8 * kg;
-    bf16x8 qa[STEPS];
+    // The slot, the query pieces and then the whole K row are each loaded unconditionally (clamped
+    // addresses) and fenced from the matrix products: otherwise the compiler waits for the slot
+    // together with the queries and issues the row's pieces between the products, one memory
+    // round trip each.
+    int32_t t = a.pool[int64_t(unit) * kp + (j < kp ? j : kp - 1)];
+    const int nq = n < G ? n : G - 1;
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (int64_t(b) * d.Hq + int64_t(g) * G + nq) * D + 8 * kg;
+    uint4 qraw[STEPS];
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        const uint4 v = n < G ? load16(qh + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
-        qa[s] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int s = 0; s < STEPS; ++s) qraw[s] = load16(qh + 32 * s);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j >= kp) t = -1;
+    const bool valid = t >= 0 && t < Tb;
     const int64_t krow = valid ? cache_row(d, b, g, t) : cache_row0(d, b, g);
     const uint16_t* kr = static_cast<const uint16_t*>(a.K) + krow * D + 8 * kg;
     uint4 kb[STEPS];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) kb[s] = load16(kr + 32 * s);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 qa[STEPS];  // rows of heads >= G are zero
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) qa[s] = __builtin_bit_cast(bf16x8, n < G ? qraw[s] : make_uint4(0u, 0u, 0u, 0u));
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
