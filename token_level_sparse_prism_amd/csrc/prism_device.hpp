@@ -289,18 +289,6 @@ __device__ __forceinline__ void load_hist_desc(const uint32_t* __restrict__ h, u
     }
 }
 
-// ---- streaming stores of scratch that the next kernel reads once -------------------------
-__device__ __forceinline__ void st_stream(float4* p, float4 v) {
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const f4 x = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(x, reinterpret_cast<f4*>(p));
-}
-__device__ __forceinline__ void st_stream(uint2* p, uint2 v) {
-    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-    const u2 x = {v.x, v.y};
-    __builtin_nontemporal_store(x, reinterpret_cast<u2*>(p));
-}
-
 // ---- device-scope data hand-off inside one kernel ----------------------------------------
 // Values another workgroup reads in the same kernel are written through to device scope and read
 // at device scope; the handshake waits for this workgroup's stores to complete and counts

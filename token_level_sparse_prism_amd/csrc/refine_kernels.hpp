@@ -6,7 +6,7 @@
 //   k_rscore  grid (pool slices of 64 slots) x units.  Gathers the pool's K rows, computes the G
 //             heads' logits (fp32) and the group score S, and stores the logits and {order key
 //             of S, id} per slot (key 0 for an empty slot; id = the token, or with paged caches
-//             its row in the KV head's pool).
+//             its row in the KV head's pool).  Plain (cached) stores: k_attend reads them next.
 //   k_attend  grid (128 or 256 selected ranks) x units, 1024 threads.  Every workgroup derives the
 //             exact top-kappa of its unit from the keys, ranks the selected
 //             slots in slot order (ties to the lower slot), writes idx for its ranks, gathers
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
             if (sub == 0 && j < kp && (r0 + u) * RPR + rl < kScoreSlice) {
                 const uint32_t key = valid ? order_key(S) : 0u;
                 const uint32_t id = d.pg.table ? uint32_t(cache_row(d, b, g, t[u]) - cache_row0(d, b, g)) : uint32_t(t[u]);
-                st_stream(&skey[j], make_uint2(key, valid ? id : 0xFFFFFFFFu));
+                skey[j] = make_uint2(key, valid ? id : 0xFFFFFFFFu);
 #pragma unroll
                 for (int h4 = 0; h4 < LS; h4 += 4) {
                     float4 v;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
                     v.y = h4 + 1 < GP ? l[h4 + 1] : 0.0f;
                     v.z = h4 + 2 < GP ? l[h4 + 2] : 0.0f;
                     v.w = h4 + 3 < GP ? l[h4 + 3] : 0.0f;
-                    st_stream(reinterpret_cast<float4*>(&logits[j * LS + h4]), v);
+                    *reinterpret_cast<float4*>(&logits[j * LS + h4]) = v;
                 }
             }
         }
@@ -168,12 +168,12 @@ __global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
             v.y = 4 * kg + 1 < GP ? l4[1] : 0.0f;
             v.z = 4 * kg + 2 < GP ? l4[2] : 0.0f;
             v.w = 4 * kg + 3 < GP ? l4[3] : 0.0f;
-            st_stream(reinterpret_cast<float4*>(a.logits + (int64_t(unit) * kp + j) * LS + 4 * kg), v);
+            *reinterpret_cast<float4*>(a.logits + (int64_t(unit) * kp + j) * LS + 4 * kg) = v;
         }
         if (kg == 0) {
             const uint32_t key = valid ? order_key(S) : 0u;
             const uint32_t id = d.pg.table ? uint32_t(krow - cache_row0(d, b, g)) : uint32_t(t);
-            st_stream(a.skey + int64_t(unit) * a.kstride + j, make_uint2(key, valid ? id : 0xFFFFFFFFu));
+            a.skey[int64_t(unit) * a.kstride + j] = make_uint2(key, valid ? id : 0xFFFFFFFFu);
         }
     }
 }
