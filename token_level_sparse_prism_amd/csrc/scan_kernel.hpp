@@ -351,11 +351,12 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
     constexpr int TPW = 64 / LPT;          // tokens per wave-load
     constexpr int U = KB == 8 ? SR::kLoads : (NQ <= 2 ? SR::kLoads : (NQ <= 8 ? SR::kLoads / 2 : SR::kLoads / 4));
     constexpr int BT = U * TPW;            // tokens per batch
+    constexpr int SPL = (BT + 63) / 64;    // a batch's scales (and keys) per lane
     static_assert(CHW % BT == 0 && CHW / BT >= NW, "every wave starts on a batch of its own");
     constexpr int RB = D * KB / 8;
 
     __shared__ uint32_t s_hist[kHistBins];
-    __shared__ uint32_t s_key[CHW];  // the work item's aggregated int32 dot products
+    __shared__ uint32_t s_key[CHW];  // aggregated int32 dot products, each batch's by its wave
     __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
     __shared__ float s_red[NW];
     __shared__ int32_t s_pg[paged ? CHW / TPW + 2 : 1];
@@ -413,17 +414,16 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
         fill_pages();
         __syncthreads();
     }
-    float scl[CHW / NT];
-    auto load_scales = [&]() {
-        const float* sc = a.scales + int64_t(unit) * d.T_max + c0;
+    // scales of batch b: lane l holds those of its tokens b * BT + l + 64 i (clamped to the last)
+    auto load_scales = [&](int bb, float* sc) {
 #pragma unroll
-        for (int i = 0; i < CHW / NT; ++i) {
-            const int t = min(tid + i * NT, last);
+        for (int i = 0; i < SPL; ++i) {
+            const int t = min(bb * BT + lane + 64 * i, last);
             if constexpr (paged) {
                 const int64_t tt = c0 + t;
-                scl[i] = sc_head[(int64_t(s_pg[(tt >> lp) - (c0 >> lp)]) << lp) + (tt & ((int64_t(1) << lp) - 1))];
+                sc[i] = sc_head[(int64_t(s_pg[(tt >> lp) - (c0 >> lp)]) << lp) + (tt & ((int64_t(1) << lp) - 1))];
             } else {
-                scl[i] = sc[t];
+                sc[i] = a.scales[int64_t(unit) * d.T_max + c0 + t];
             }
         }
     };
@@ -440,10 +440,11 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
             return SR::load(a.Kq + (int64_t(unit) * d.T_max + c0 + tok) * RB + sub * (RB / LPT));
         }
     };
-    load_scales();
     int nb = (nvalid + BT - 1) / BT;  // batches holding tokens
     int bcur = wave;                  // wave w starts on batch w
+    float sc_cur[SPL], sc_nxt[SPL];   // scales of batch bcur and of the batch being loaded
     typename SR::R kv[U];
+    load_scales(bcur, sc_cur);        // before the rows: loads complete in issue order
 #pragma unroll
     for (int u = 0; u < U; ++u) kv[u] = load_item(bcur * U + u);
     if (tid == 0) s_next = NW;
@@ -530,41 +531,47 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
         }
         if (sub == 0 && tok < nvalid) s_key[tok] = uint32_t(A);
     };
+    // the wave's products of batch bb are in s_key (written by this wave, so in order): scores,
+    // keys out (coalesced) and the top-digit histogram
+    uint32_t* kout = a.keys + int64_t(unit) * a.kstride;
+    float* sout = a.scores ? a.scores + int64_t(unit) * d.T_max : nullptr;
+    auto keys_out = [&](int bb, const float* sc) {
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+            const int t = bb * BT + lane + 64 * i;
+            if ((BT % 64 == 0 || lane + 64 * i < BT) && t < nvalid) {
+                const float score = float(int(s_key[t])) * sc[i];  // one fp32 product
+                const uint32_t k = order_key(score);
+                atomicAdd(&s_hist[k >> kKeyShift], 1u);
+                kout[c0 + t] = k;
+                if (sout) sout[c0 + t] = key_to_float(k);
+            }
+        }
+    };
     for (;;) {  // work items of this workgroup; the rows of its first batch per wave are in flight
         if (nvalid == 0) break;  // later work items are past T_b too
         nb = __builtin_amdgcn_readfirstlane(nb);
         int bnext = claim();
         while (bnext < nb) {
             const int bfut = claim();  // the batch after, claimed one batch ahead
+            load_scales(bnext, sc_nxt);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 consume(u);
                 kv[u] = load_item(bnext * U + u);
             }
+            keys_out(bcur, sc_cur);
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) sc_cur[i] = sc_nxt[i];
             bcur = bnext;
             bnext = bfut;
         }
         if (bcur < nb) {
 #pragma unroll
             for (int u = 0; u < U; ++u) consume(u);
+            keys_out(bcur, sc_cur);
         }
-        __syncthreads();
-
-        uint32_t* kout = a.keys + int64_t(unit) * a.kstride + c0;
-        float* sout = a.scores ? a.scores + int64_t(unit) * d.T_max + c0 : nullptr;
-#pragma unroll
-        for (int i = 0; i < CHW / NT; ++i) {
-            const int t = tid + i * NT;
-            if (t < nvalid) {
-                const float score = float(int(s_key[t])) * scl[i];  // one fp32 product
-                const uint32_t k = order_key(score);
-                atomicAdd(&s_hist[k >> kKeyShift], 1u);
-                kout[t] = k;
-                if (sout) sout[t] = key_to_float(k);
-            }
-        }
-        if (tid == 0) s_next = NW;  // the next work item's claims start after the barrier
-        __syncthreads();
+        __syncthreads();  // every wave is done claiming from s_next and adding to s_hist
 
         chunk += gridDim.x;
         if (chunk >= nch) break;
@@ -572,13 +579,12 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
         nvalid = scan_chunk_tokens<CHW>(Tb, c0);
         if (nvalid == 0) break;
         last = nvalid - 1;
-        if constexpr (paged) {
-            fill_pages();
-            __syncthreads();
-        }
-        load_scales();
+        if (tid == 0) s_next = NW;
+        if constexpr (paged) fill_pages();
+        __syncthreads();  // the reset counter (and the pages) before the work item's claims
         nb = (nvalid + BT - 1) / BT;
         bcur = wave;
+        load_scales(bcur, sc_cur);
 #pragma unroll
         for (int u = 0; u < U; ++u) kv[u] = load_item(bcur * U + u);
     }
