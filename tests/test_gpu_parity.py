@@ -313,8 +313,10 @@ def test_paged_matches_contiguous(case, key_bits):
 # ------------------------------------------------------------------ proposal on CU-filling grids
 # Shapes whose 4096-token work items give at least 256 scan workgroups (one per CU), where the
 # scan runs one 1024-thread workgroup per CU with batches claimed by its waves: ragged tails,
-# MAX aggregation, two work items per workgroup, INT2 keys, fp32 queries and paged caches (pages
-# of 4 tokens are smaller than a wave-load and take the 256-thread scan at the same grid size).
+# MAX aggregation, two work items per workgroup, INT2 keys, fp32 queries, paged caches (pages of
+# 4 tokens are smaller than a wave-load and take the 256-thread scan at the same grid size) and a
+# T_max that is no multiple of the work item (the last work item is partial and is a workgroup's
+# second one).
 WIDE_CASES = [
     # D, G, Hkv, agg, dtype, T, kp, lens, key bits, page size (0: contiguous)
     (128, 4, 8, PB.AGG_SUM, "bf16", 65536, 4096, [65536, 50001], 8, 0),
@@ -325,6 +327,8 @@ WIDE_CASES = [
     (128, 4, 8, PB.AGG_SUM, "bf16", 65536, 4096, [65536, 40000], 8, 16),
     (128, 4, 8, PB.AGG_SUM, "bf16", 65536, 2048, [65536, 33333], 2, 64),
     (128, 4, 8, PB.AGG_SUM, "bf16", 65536, 2048, [65536, 30001], 8, 4),
+    (128, 4, 8, PB.AGG_SUM, "bf16", 65541, 2048, [65541, 61234], 8, 0),  # T_max not a multiple of 4
+    (128, 4, 8, PB.AGG_SUM, "bf16", 65541, 2048, [65541, 4097], 2, 0),
 ]
 
 

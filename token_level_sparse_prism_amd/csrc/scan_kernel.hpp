@@ -1,8 +1,10 @@
 // scan_kernel.hpp -- the proposal layer's full-context scan on gfx950 (Prism Attention page,
-// Sec. 4.2: the anchor layer scores every token with the compressed key cache).  k_scan streams
+// Sec. 4.2: the anchor layer scores every token with the compressed key cache).  The scan streams
 // the int8 or 2-bit keys once, writes a 32-bit order key per token and adds each workgroup's
-// histogram of the keys' top 12 bits into the unit's histogram.  k_scan8.hip and k_scan2.hip
-// instantiate it, one key format per translation unit.
+// histogram of the keys' top 12 bits into the unit's histogram.  Two kernels share that work:
+// k_scan_w (one 1024-thread workgroup per CU, waves claiming batches) where the grid fills the
+// chip, k_scan (256-thread workgroups, fixed chunks) elsewhere.  k_scan8.hip and k_scan2.hip
+// instantiate them, one key format per translation unit.
 #pragma once
 
 #include "prism_device.hpp"
@@ -333,8 +335,9 @@ __global__ __launch_bounds__(kThreads) void k_scan(ProposeArgs a) {
 // CU.  A work item of CHW tokens is cut into batches of U wave-loads (U * TPW consecutive tokens);
 // wave w starts on batch w and then takes the next unclaimed batch from an LDS counter.  The
 // waves that a CU serves first take more batches, so its waves finish together instead of the
-// CU's last-dispatched waves setting the end.  Paging needs pages of at least TPW tokens (a
-// wave-load then lies in one page, whose base is a scalar).
+// CU's last-dispatched waves setting the end.  A wave turns each batch it has used into keys at
+// once.  Paging needs pages of at least TPW tokens (a wave-load then lies in one page, whose base
+// is a scalar).
 constexpr int kScanWideThreads = 1024;
 constexpr int kScanWideChunk = 4096;
 
