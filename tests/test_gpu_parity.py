@@ -186,6 +186,11 @@ REFINE_CASES = [
     (128, 4, 1, PB.AGG_SUM, "bf16", 6000, 5000, 1000, None),     # one tile, clustered bin above 2048 keys
     (64, 4, 1, PB.AGG_MAX, "f32", 2000, 450, 100, None),         # clustered bin of 450 keys
     (128, 2, 1, PB.AGG_SUM, "bf16", 1000, 200, 50, None),        # clustered bin of 200 keys
+    (128, 4, 2, PB.AGG_SUM, "bf16", 1200, 1024, 300, [1200, 0]), # head-dim split: empty sequence
+    (256, 2, 1, PB.AGG_SUM, "bf16", 3000, 1200, 500, None),      # head-dim split: 32 pieces of D
+    (128, 4, 1, PB.AGG_MAX, "bf16", 6000, 4096, 1024, None),     # head-dim split: most rows
+    (64, 1, 1, PB.AGG_SUM, "f32", 3000, 800, 700, None),         # head-dim split: 4 values per lane
+    (64, 8, 2, PB.AGG_SUM, "bf16", 1200, 1024, 300, [1200, 0]),  # rank split: empty sequence
 ]
 
 

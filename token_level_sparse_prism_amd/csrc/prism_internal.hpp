@@ -18,6 +18,9 @@ namespace prism {
 #ifndef PRISM_SCAN_WGS
 #define PRISM_SCAN_WGS 1024            // target scan workgroups over all units
 #endif
+#ifndef PRISM_ATTEND_DSPLIT
+#define PRISM_ATTEND_DSPLIT 1          // head-dimension split of the refined attention (no merge)
+#endif
 #ifndef PRISM_SCORE_SLICE
 #define PRISM_SCORE_SLICE 64
 #endif
@@ -28,6 +31,7 @@ constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in p
 constexpr int kAttendRanks = 128;      // selected rows per workgroup in sparse attention
 constexpr int kHistRep = 8;            // most copies of a unit's key histogram (see ScanPlan)
 constexpr int kMergeGroup = 16;        // partials merged by one workgroup (two levels above it)
+constexpr int kAttendDRanks = 1024;    // most selected rows of the head-dimension split attention
 constexpr int kAttendThreads = 1024;   // 16 waves: the selection's latency is shared by 4 waves per SIMD
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
 constexpr int kCtrStride = 16;         // counters sit 64 bytes apart (no shared cache line)

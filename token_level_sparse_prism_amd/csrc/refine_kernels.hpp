@@ -12,6 +12,9 @@
 //             slots in slot order (ties to the lower slot), writes idx for its ranks, gathers
 //             their V rows and forms a softmax(.)V partial from the stored logits.  The unit's
 //             last workgroup merges the partials (log-sum-exp) into out and lse.
+//   k_attend_d  in place of k_attend for kappa <= 1024, G <= 4 and small grids: grid (16-byte
+//             pieces of a V row) x units.  Every workgroup takes the whole selection and writes
+//             its columns of out directly (no partials, no merge).
 // The kernels and their launch templates; k_refine.hip (bf16) and k_refine_f32.hip (fp32)
 // instantiate them, one dtype per translation unit.
 #pragma once
@@ -257,6 +260,210 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     if (tid == 0) a.done_a[int64_t(unit) * kCtrStride] = 0u;
 }
 
+// `hi` on the lanes of the banks ((lane / 4) % 4) in BANKM, `lo` elsewhere: a DPP move with an
+// identity pattern and a write mask.
+template <int BANKM>
+__device__ __forceinline__ float bank_pick(float lo, float hi) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(lo), __float_as_int(hi), 0xE4, 0xF, BANKM, false));
+}
+
+// One step of recursive halving over lane bit B (5 to 2): afterwards v[i], i < HALF, holds on a
+// lane with bit B clear the sum over the lane pair (lane, lane ^ 2^B) of v[i], and on a lane with
+// the bit set that of v[i + HALF].  Bits 5 and 4 exchange halves with the gfx950 half-wave and
+// row swaps (the swap hands each lane its partner's copy of the half it keeps); bits 3 and 2
+// with row rotations under bank write masks (row_ror:n hands lane l the value of lane l - n mod 16).
+template <int B, int HALF, int NV>
+__device__ __forceinline__ void halve_step(float (&v)[NV]) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+        const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + HALF]);
+        if constexpr (B == 5 || B == 4) {
+            const auto r = B == 5 ? __builtin_amdgcn_permlane32_swap(lo, hi, false, false)
+                                  : __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+            v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        } else if constexpr (B == 3) {
+            int recv = __builtin_amdgcn_update_dpp(int(lo), int(lo), 0x128, 0xF, 0x3, false);  // banks 0, 1: lane + 8
+            recv = __builtin_amdgcn_update_dpp(recv, int(hi), 0x128, 0xF, 0xC, false);          // banks 2, 3: lane - 8
+            v[i] = bank_pick<0xC>(v[i], v[i + HALF]) + __int_as_float(recv);
+        } else {
+            int recv = __builtin_amdgcn_update_dpp(int(lo), int(lo), 0x12C, 0xF, 0x5, false);  // banks 0, 2: lane + 4
+            recv = __builtin_amdgcn_update_dpp(recv, int(hi), 0x124, 0xF, 0xA, false);          // banks 1, 3: lane - 4
+            v[i] = bank_pick<0xA>(v[i], v[i + HALF]) + __int_as_float(recv);
+        }
+    }
+}
+
+// Sum over the 64 lanes of a wave of NV values per lane (NV a power of two, 4 to 64): recursive
+// halving over lane bits 5..2 (S = min(log2 NV, 4) steps), then an all-reduce over aligned groups
+// of 64 >> S lanes.  Afterwards the first lane of each group holds the wave's sums of values
+// [(lane >> (6 - S)) * R, +R) in v[0, R), R = NV >> S.
+template <int NV>
+__device__ __forceinline__ void wave_reduce_scatter(float (&v)[NV]) {
+    static_assert(NV >= 4 && NV <= 64 && (NV & (NV - 1)) == 0, "power of two, 4 to 64");
+    constexpr int S = NV >= 16 ? 4 : NV == 8 ? 3 : 2;
+    constexpr int R = NV >> S;
+    halve_step<5, NV / 2>(v);
+    halve_step<4, NV / 4>(v);
+    if constexpr (S >= 3) halve_step<3, NV / 8>(v);
+    if constexpr (S >= 4) halve_step<2, NV / 16>(v);
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = group_sum<(64 >> S)>(v[j]);
+}
+
+// Refined attention split over the head dimension, for kappa <= kAttendDRanks and GP <= 4:
+// grid (D / DS column pieces) x units, 1024 threads, DS = 16 bytes of a V row.  Every workgroup
+// derives the unit's whole selection (the same exact top-kappa and slot-order ranks as k_attend)
+// and the softmax statistics over all selected rows, so it writes its DS columns of out and lse
+// directly: no partials and no merge.  When units is a multiple of 8 the unit's workgroups share
+// one XCD (unit_major), so a V row is fetched into that XCD's L2 once and each workgroup reads its
+// 16-byte piece from there.
+// Thread t takes rank t; the waves' sums are combined in LDS in wave order.
+template <typename T, int D, int GP>
+__global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
+    constexpr int NT = kAttendThreads;
+    constexpr int NW = NT / 64;
+    constexpr int DS = Elem<T>::kPerLane;
+    constexpr int NS = D / DS;
+    constexpr int KM = kAttendDRanks;
+    constexpr int RPT = KM / NT;
+    constexpr int NV = GP * DS;
+    constexpr int LS = 4;  // logit stride for GP <= 4
+    static_assert(GP <= 4 && NV <= 64 && KM % NT == 0 && NS >= 2, "head-dimension split shape");
+    static_assert(kHistPadded <= kRowsAccFloats && kSelHistWords <= kRowsAccFloats, "LDS buffer too small");
+    __shared__ __align__(16) uint32_t s_big[kRowsAccFloats];  // selection histograms
+    __shared__ __align__(16) uint32_t s_cand[kSelCandTotal];
+    __shared__ uint32_t s_ccount[NW];
+    __shared__ uint32_t s_tmp[sel_tmp_words<NT>()];
+    __shared__ uint32_t s_res[16];
+    __shared__ int32_t s_slot[KM];
+    __shared__ int32_t s_tok[KM];
+    __shared__ float s_max[NW * GP];
+    __shared__ float s_sum[NW * GP];
+    __shared__ float s_part[NW * NV];
+
+    const Dims& d = a.d;
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const UnitIdx ui = unit_major();
+    const int unit = ui.unit;
+    const int piece = ui.x;
+    const int b = unit / d.Hkv, g = unit % d.Hkv;
+    const int G = d.G;
+    const int64_t kp = a.kp;
+
+    const SelResult sr = select_ranks<NT>(a.skey + int64_t(unit) * a.kstride, kp, uint32_t(a.kappa), 0, KM, s_big,
+                                          s_tmp, s_res, s_cand, s_ccount, s_slot, s_tok);
+    const int n = sr.n;
+    const bool paged = d.pg.table != nullptr;
+
+    // idx: piece p writes ranks [p * per, (p + 1) * per); ranks at or beyond n hold -1
+    {
+        const int per = (a.kappa + NS - 1) / NS;
+        const int r = piece * per + tid;
+        if (tid < per && r < a.kappa) {
+            int32_t t = -1;
+            if (r < n) t = paged ? a.pool[int64_t(unit) * kp + s_slot[r]] : s_tok[r];
+            a.idx[int64_t(unit) * a.kappa + r] = t;
+        }
+    }
+    const int64_t hq0 = int64_t(b) * d.Hq + int64_t(g) * G;
+    T* out = static_cast<T*>(a.out) + hq0 * D + piece * DS;
+    float* lse = a.lse ? a.lse + hq0 : nullptr;
+    if (n == 0) {  // no valid slot: out = 0, lse = -inf
+        if (tid < G * DS) store_elem<T>(&out[(tid / DS) * D + tid % DS], 0.0f);
+        if (piece == 0 && lse && tid < G) lse[tid] = -INFINITY;
+        return;
+    }
+
+    // this thread's rows: logits of the GP heads and the piece of the V row (clamped, unconditional
+    // loads; rows at or beyond n carry weight 0)
+    const float* lg = a.logits + int64_t(unit) * kp * LS;
+    const T* Vb = static_cast<const T*>(a.V) + cache_row0(d, b, g) * D + piece * DS;
+    float4 lraw[RPT];
+    uint4 vraw[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = tid + i * NT;
+        const int rr = r < n ? r : 0;
+        lraw[i] = *reinterpret_cast<const float4*>(lg + int64_t(s_slot[rr]) * LS);
+        vraw[i] = *reinterpret_cast<const uint4*>(Vb + int64_t(uint32_t(s_tok[rr])) * D);
+    }
+    float y[RPT][GP];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const bool valid = tid + i * NT < n;
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+            const float c = h == 0 ? lraw[i].x : h == 1 ? lraw[i].y : h == 2 ? lraw[i].z : lraw[i].w;
+            y[i][h] = (valid && h < G) ? c * a.y_scale : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        float m = y[0][h];
+#pragma unroll
+        for (int i = 1; i < RPT; ++i) m = fmaxf(m, y[i][h]);
+        m = wave_max(m);
+        if (lane == 0) s_max[wave * GP + h] = m;
+    }
+    __syncthreads();
+    // the block maximum per head: lane l reads wave l % 16 of head l / 16, a row-wide DPP max
+    static_assert(NW == 16, "the wave maxima fill one DPP row per head");
+    float M[GP];
+    {
+        const int hq = lane >> 4;
+        const float m = group_max<16>(hq < G && hq < GP ? s_max[(lane & 15) * GP + hq] : -INFINITY);
+#pragma unroll
+        for (int h = 0; h < GP; ++h) M[h] = readlane_f32(m, 16 * h);
+    }
+    float acc[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+        float l = 0.0f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float p = (tid + i * NT < n && h < G) ? exp2_le0(y[i][h] - M[h]) : 0.0f;
+            l += p;
+            float x[DS];
+            unpack16<T>(vraw[i], x);
+#pragma unroll
+            for (int e = 0; e < DS; ++e) acc[h * DS + e] = fmaf(p, x[e], acc[h * DS + e]);
+        }
+        l = wave_sum(l);
+        if (lane == 0) s_sum[wave * GP + h] = l;
+    }
+    wave_reduce_scatter<NV>(acc);
+    {
+        constexpr int S = NV >= 16 ? 4 : NV == 8 ? 3 : 2;
+        constexpr int R = NV >> S;
+        if ((lane & ((64 >> S) - 1)) == 0) {
+#pragma unroll
+            for (int j = 0; j < R; ++j) s_part[wave * NV + (lane >> (6 - S)) * R + j] = acc[j];
+        }
+    }
+    __syncthreads();
+    if (tid < NV) {
+        const int h = tid / DS, e = tid % DS;
+        if (h < G) {
+            float sacc = s_part[tid], L = s_sum[h];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                sacc += s_part[w * NV + tid];
+                L += s_sum[w * GP + h];
+            }
+            store_elem<T>(&out[int64_t(h) * D + e], sacc / L);
+            if (e == 0 && piece == 0 && lse) {
+                constexpr float kLn2 = 0.6931471805599453f;
+                float Mh = M[0];
+#pragma unroll
+                for (int k = 1; k < GP; ++k) Mh = h == k ? M[k] : Mh;
+                lse[h] = (Mh + log2f(L)) * kLn2;
+            }
+        }
+    }
+}
+
 // Compute units of the current device (cached per device).
 static int device_cus() {
     static int cus[64] = {0};
@@ -289,10 +496,18 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    {
-        if (wide) launch_k("k_attend", (k_attend<T, D, GP, 2 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
-        else launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks>), ga, dim3(kAttendThreads), st, a);
+    if constexpr (PRISM_ATTEND_DSPLIT && GP <= 4) {
+        // head-dimension split while its grid (D / 16-byte pieces per unit) fits one workgroup per
+        // CU: every workgroup gathers all kappa rows, so on fuller grids, and for kappa above 1024
+        // with V rows coming from HBM, the rank split is faster
+        constexpr int ns = D / Elem<T>::kPerLane;
+        if (a.kappa <= kAttendDRanks && int64_t(units) * ns <= int64_t(device_cus())) {
+            launch_k("k_attend", (k_attend_d<T, D, GP>), dim3(ns, units), dim3(kAttendThreads), st, a);
+            return hipGetLastError();
+        }
     }
+    if (wide) launch_k("k_attend", (k_attend<T, D, GP, 2 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
+    else launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks>), ga, dim3(kAttendThreads), st, a);
     return hipGetLastError();
 }
 
