@@ -190,7 +190,7 @@ REFINE_CASES = [
     (256, 2, 1, PB.AGG_SUM, "bf16", 3000, 1200, 500, None),      # head-dim split: 32 pieces of D
     (128, 4, 1, PB.AGG_MAX, "bf16", 6000, 4096, 1024, None),     # head-dim split: most rows
     (64, 1, 1, PB.AGG_SUM, "f32", 3000, 800, 700, None),         # head-dim split: 4 values per lane
-    (64, 8, 2, PB.AGG_SUM, "bf16", 1200, 1024, 300, [1200, 0]),  # rank split: empty sequence
+    (64, 16, 2, PB.AGG_SUM, "bf16", 1200, 1024, 300, [1200, 0]), # rank split (G > 8): empty sequence
 ]
 
 

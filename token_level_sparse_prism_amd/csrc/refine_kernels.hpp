@@ -12,7 +12,7 @@
 //             slots in slot order (ties to the lower slot), writes idx for its ranks, gathers
 //             their V rows and forms a softmax(.)V partial from the stored logits.  The unit's
 //             last workgroup merges the partials (log-sum-exp) into out and lse.
-//   k_attend_d  in place of k_attend for kappa <= 1024, G <= 4 and small grids: grid (16-byte
+//   k_attend_d  in place of k_attend for kappa <= 1024, G <= 8 and small grids: grid (16-byte
 //             pieces of a V row) x units.  Every workgroup takes the whole selection and writes
 //             its columns of out directly (no partials, no merge).
 // The kernels and their launch templates; k_refine.hip (bf16) and k_refine_f32.hip (fp32)
@@ -310,7 +310,7 @@ __device__ __forceinline__ void wave_reduce_scatter(float (&v)[NV]) {
     for (int j = 0; j < R; ++j) v[j] = group_sum<(64 >> S)>(v[j]);
 }
 
-// Refined attention split over the head dimension, for kappa <= kAttendDRanks and GP <= 4:
+// Refined attention split over the head dimension, for kappa <= kAttendDRanks and GP <= 8:
 // grid (D / DS column pieces) x units, 1024 threads, DS = 16 bytes of a V row.  Every workgroup
 // derives the unit's whole selection (the same exact top-kappa and slot-order ranks as k_attend)
 // and the softmax statistics over all selected rows, so it writes its DS columns of out and lse
@@ -327,8 +327,9 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     constexpr int KM = kAttendDRanks;
     constexpr int RPT = KM / NT;
     constexpr int NV = GP * DS;
-    constexpr int LS = 4;  // logit stride for GP <= 4
-    static_assert(GP <= 4 && NV <= 64 && KM % NT == 0 && NS >= 2, "head-dimension split shape");
+    constexpr int LS = GP < 4 ? 4 : GP;  // logit stride
+    constexpr int L4 = LS / 4;           // 16-byte logit pieces per slot
+    static_assert(GP <= 8 && NV <= 64 && KM % NT == 0 && NS >= 2, "head-dimension split shape");
     static_assert(kHistPadded <= kRowsAccFloats && kSelHistWords <= kRowsAccFloats, "LDS buffer too small");
     __shared__ __align__(16) uint32_t s_big[kRowsAccFloats];  // selection histograms
     __shared__ __align__(16) uint32_t s_cand[kSelCandTotal];
@@ -378,13 +379,14 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     // loads; rows at or beyond n carry weight 0)
     const float* lg = a.logits + int64_t(unit) * kp * LS;
     const T* Vb = static_cast<const T*>(a.V) + cache_row0(d, b, g) * D + piece * DS;
-    float4 lraw[RPT];
+    float4 lraw[RPT][L4];
     uint4 vraw[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = tid + i * NT;
         const int rr = r < n ? r : 0;
-        lraw[i] = *reinterpret_cast<const float4*>(lg + int64_t(s_slot[rr]) * LS);
+#pragma unroll
+        for (int j = 0; j < L4; ++j) lraw[i][j] = reinterpret_cast<const float4*>(lg + int64_t(s_slot[rr]) * LS)[j];
         vraw[i] = *reinterpret_cast<const uint4*>(Vb + int64_t(uint32_t(s_tok[rr])) * D);
     }
     float y[RPT][GP];
@@ -393,7 +395,8 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
         const bool valid = tid + i * NT < n;
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
-            const float c = h == 0 ? lraw[i].x : h == 1 ? lraw[i].y : h == 2 ? lraw[i].z : lraw[i].w;
+            const float4 v = lraw[i][h / 4];
+            const float c = h % 4 == 0 ? v.x : h % 4 == 1 ? v.y : h % 4 == 2 ? v.z : v.w;
             y[i][h] = (valid && h < G) ? c * a.y_scale : -INFINITY;
         }
     }
@@ -409,11 +412,13 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     // the block maximum per head: lane l reads wave l % 16 of head l / 16, a row-wide DPP max
     static_assert(NW == 16, "the wave maxima fill one DPP row per head");
     float M[GP];
-    {
-        const int hq = lane >> 4;
+#pragma unroll
+    for (int hb = 0; hb < GP; hb += 4) {  // four heads per round
+        const int hq = hb + (lane >> 4);
         const float m = group_max<16>(hq < G && hq < GP ? s_max[(lane & 15) * GP + hq] : -INFINITY);
 #pragma unroll
-        for (int h = 0; h < GP; ++h) M[h] = readlane_f32(m, 16 * h);
+        for (int h4 = 0; h4 < 4; ++h4)
+            if (hb + h4 < GP) M[hb + h4] = readlane_f32(m, 16 * h4);
     }
     float acc[NV];
 #pragma unroll
@@ -496,7 +501,7 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if constexpr (PRISM_ATTEND_DSPLIT && GP <= 4) {
+    if constexpr (PRISM_ATTEND_DSPLIT && GP <= 8) {
         // head-dimension split while its grid (D / 16-byte pieces per unit) fits one workgroup per
         // CU: every workgroup gathers all kappa rows, so on fuller grids, and for kappa above 1024
         // with V rows coming from HBM, the rank split is faster
