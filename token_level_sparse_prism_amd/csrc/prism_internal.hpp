@@ -28,6 +28,10 @@ constexpr int kThreads = 256;          // every kernel runs 4 waves of 64 lanes
 constexpr int kChunk = 1024;           // tokens per chunk in the proposal kernels
 constexpr int kScanWgs = PRISM_SCAN_WGS;
 constexpr int kScoreSlice = PRISM_SCORE_SLICE;  // pool slots per workgroup in pool scoring
+#ifndef PRISM_RSCORE_THREADS
+#define PRISM_RSCORE_THREADS 256
+#endif
+constexpr int kRscoreThreads = PRISM_RSCORE_THREADS;  // matrix-core pool scoring: 16 slots per wave
 constexpr int kAttendRanks = 128;      // selected rows per workgroup in sparse attention
 constexpr int kHistRep = 8;            // most copies of a unit's key histogram (see ScanPlan)
 constexpr int kMergeGroup = 16;        // partials merged by one workgroup (two levels above it)

@@ -104,13 +104,12 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
 // operand is one 16-byte piece of a K row.  A wave scores 16 slots; lane group l / 16 ends with
 // heads 4 (l / 16) .. + 3 of slot l % 16.
 template <int D, int GP, bool kMax>
-__global__ __launch_bounds__(kThreads) void k_rscore_mfma(RefineArgs a) {
+__global__ __launch_bounds__(kRscoreThreads) void k_rscore_mfma(RefineArgs a) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int STEPS = D / 32;
     constexpr int LS = GP < 4 ? 4 : GP;
-    constexpr int SLOTS = 16 * (kThreads / 64);
-    static_assert(SLOTS == kScoreSlice, "one slice of slots per workgroup");
+    constexpr int SLOTS = 16 * (kRscoreThreads / 64);
     const Dims& d = a.d;
     const int lane = lane_id(), wave = wave_id();
     const UnitIdx ui = unit_major();
@@ -486,6 +485,7 @@ template <typename T, int D, int GP>
 static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t st) {
     const int units = a.d.B * a.d.Hkv;
     const dim3 gs((a.kp + kScoreSlice - 1) / kScoreSlice, units);
+    const dim3 gsm((a.kp + 16 * (kRscoreThreads / 64) - 1) / (16 * (kRscoreThreads / 64)), units);
     // one attention workgroup fits a CU: when 128 ranks per workgroup would need more workgroups
     // than there are CUs, take 256 ranks each (half the workgroups, twice the rows each)
     const int64_t n128 = int64_t(units) * ((a.kappa + kAttendRanks - 1) / kAttendRanks);
@@ -493,8 +493,8 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     const int nr = wide ? 2 * kAttendRanks : kAttendRanks;
     const dim3 ga((a.kappa + nr - 1) / nr, units);
     if constexpr (sizeof(T) == 2) {
-        if (agg_max) launch_k("k_rscore", (k_rscore_mfma<D, GP, true>), gs, dim3(kThreads), st, a);
-        else launch_k("k_rscore", (k_rscore_mfma<D, GP, false>), gs, dim3(kThreads), st, a);
+        if (agg_max) launch_k("k_rscore", (k_rscore_mfma<D, GP, true>), gsm, dim3(kRscoreThreads), st, a);
+        else launch_k("k_rscore", (k_rscore_mfma<D, GP, false>), gsm, dim3(kRscoreThreads), st, a);
     } else {
         if (agg_max) launch_k("k_rscore", (k_rscore<T, D, GP, true>), gs, dim3(kThreads), st, a);
         else launch_k("k_rscore", (k_rscore<T, D, GP, false>), gs, dim3(kThreads), st, a);
