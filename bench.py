@@ -338,6 +338,22 @@ def main():
                 "avg_launch_us": round(scan_us, 3) if scan_us else None,
                 "frac_of_read_ceiling": round(achieved / ceiling["GBps"], 4) if achieved else None}
 
+    # the refined layer's two kernels against the same HBM roof (algorithmic bytes per launch:
+    # pool ids, gathered K rows and the query for pool scoring; gathered V rows, output and index
+    # list for the attention).  Both are far below it: their time is gather latency and the
+    # per-workgroup selection, not bandwidth.
+    secondary = {}
+    for kname, per_unit in (("k_rscore", lambda T_b: 4 * cfg.kp + min(cfg.kp, T_b) * cfg.D * e + cfg.G * cfg.D * e),
+                            ("k_attend", lambda T_b: min(cfg.kappa, cfg.kp, T_b) * cfg.D * e + cfg.G * cfg.D * e
+                             + 4 * cfg.kappa)):
+        kb = sum(per_unit(int(w.seq_lens[b])) for b in range(cfg.B) for _ in range(cfg.Hkv))
+        kus = kernels.get(kname, {}).get("avg_us")
+        if kus:
+            ach = kb / (kus * 1e-6) / 1e9
+            secondary[kname] = {"bound": "hbm", "limited_by": "gather latency", "achieved": round(ach, 1),
+                                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+                                "algorithmic_bytes_per_launch": int(kb), "avg_launch_us": round(kus, 3)}
+
     # the same step with INT2 proposal keys (a second key format; the headline above is int8):
     # stream-launched, same buffer rotation and workspaces, plus how its pools compare with int8's
     int2 = None
@@ -513,6 +529,7 @@ def main():
         "hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(ab["step"]),
         "roofline": roofline,
+        "refine_rooflines": secondary,
         "launch": launch,
         "repeats": len(rep_ms), "ms_per_step_p10": round(ms_p10, 5), "ms_per_step_p90": round(ms_p90, 5),
         "tokens_per_s": round(cfg.B * steps_per_s, 2),
