@@ -15,6 +15,7 @@ import json
 import os
 import sys
 import time
+import types
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -194,23 +195,46 @@ def main():
 
     PB.load()  # fail loudly if the HIP library is missing
     cfg = W.CONFIGS[args.config]
-    t0 = time.time()
-    w = W.generate(cfg)
-    gen_s = time.time() - t0
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
     def dev(x):
         return torch.from_numpy(x).to(device="cuda", dtype=dt)
 
-    lens_d = torch.from_numpy(w.seq_lens).cuda()
-    K0 = dev(w.K[0])
-    Kq, sc = PB.quantize_keys(K0, seq_lens=lens_d)
-    del K0
-    base = {"q0": dev(w.q[0]), "Kq": Kq, "sc": sc,
-            "layers": [(dev(w.q[l]), dev(w.K[l]), dev(w.V[l])) for l in range(1, w.layers)]}
+    # Configs whose float32 host copy of every layer would not fit comfortably (cfg4: 69 GB) are
+    # generated one layer at a time, straight to the device; the legs that need the host copy
+    # (INT2 keys, paged caches, the oracle's CPU baseline) are then skipped.
+    host_bytes = 4.0 * cfg.B * cfg.Hkv * cfg.T * cfg.D * 2 * (cfg.n_refined + 1)
+    layerwise = host_bytes > 24e9
+    t0 = time.time()
+    if layerwise:
+        args.no_int2, args.page_size, args.no_cpu_baseline = True, 0, True
+        wl = W.generate(cfg, layers=[0])
+        lens_d = torch.from_numpy(wl.seq_lens).cuda()
+        K0 = dev(wl.K[0])
+        Kq, sc = PB.quantize_keys(K0, seq_lens=lens_d)
+        base = {"q0": dev(wl.q[0]), "Kq": Kq, "sc": sc, "layers": []}
+        w = types.SimpleNamespace(seq_lens=wl.seq_lens)
+        del K0, wl
+        for l in range(1, cfg.n_refined + 1):
+            wl = W.generate(cfg, layers=[l])
+            base["layers"].append((dev(wl.q[0]), dev(wl.K[0]), dev(wl.V[0])))
+            del wl
+            print(f"generated layer {l} of {cfg.n_refined} ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
+    else:
+        w = W.generate(cfg)
+        lens_d = torch.from_numpy(w.seq_lens).cuda()
+        K0 = dev(w.K[0])
+        Kq, sc = PB.quantize_keys(K0, seq_lens=lens_d)
+        del K0
+        base = {"q0": dev(w.q[0]), "Kq": Kq, "sc": sc,
+                "layers": [(dev(w.q[l]), dev(w.K[l]), dev(w.V[l])) for l in range(1, w.layers)]}
+    gen_s = time.time() - t0
     torch.cuda.synchronize()
 
-    R = max(1, args.rotate)
+    # buffer sets for the rotation, as many as fit in under half of the device memory
+    set_bytes = sum(t.numel() * t.element_size() for t in [base["q0"], base["Kq"], base["sc"]]
+                    + [t for L in base["layers"] for t in L])
+    R = max(1, min(args.rotate, int(0.45 * torch.cuda.get_device_properties(0).total_memory // set_bytes)))
     sets = [base]
     for _ in range(R - 1):
         sets.append({"q0": base["q0"].clone(), "Kq": base["Kq"].clone(), "sc": base["sc"].clone(),

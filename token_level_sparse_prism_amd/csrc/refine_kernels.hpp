@@ -487,10 +487,12 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     const dim3 gs((a.kp + kScoreSlice - 1) / kScoreSlice, units);
     const dim3 gsm((a.kp + 16 * (kRscoreThreads / 64) - 1) / (16 * (kRscoreThreads / 64)), units);
     // one attention workgroup fits a CU: when 128 ranks per workgroup would need more workgroups
-    // than there are CUs, take 256 ranks each (half the workgroups, twice the rows each)
+    // than there are CUs, take 256 ranks each (half the workgroups, twice the rows each), and
+    // 512 when 256 would still need more than one round
+    const int64_t cus = device_cus();
     const int64_t n128 = int64_t(units) * ((a.kappa + kAttendRanks - 1) / kAttendRanks);
-    const bool wide = n128 > device_cus();
-    const int nr = wide ? 2 * kAttendRanks : kAttendRanks;
+    const int64_t n256 = int64_t(units) * ((a.kappa + 2 * kAttendRanks - 1) / (2 * kAttendRanks));
+    const int nr = n128 <= cus ? kAttendRanks : (n256 <= cus ? 2 * kAttendRanks : 4 * kAttendRanks);
     const dim3 ga((a.kappa + nr - 1) / nr, units);
     if constexpr (sizeof(T) == 2) {
         if (agg_max) launch_k("k_rscore", (k_rscore_mfma<D, GP, true>), gsm, dim3(kRscoreThreads), st, a);
@@ -511,7 +513,8 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
             return hipGetLastError();
         }
     }
-    if (wide) launch_k("k_attend", (k_attend<T, D, GP, 2 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
+    if (nr == 4 * kAttendRanks) launch_k("k_attend", (k_attend<T, D, GP, 4 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
+    else if (nr == 2 * kAttendRanks) launch_k("k_attend", (k_attend<T, D, GP, 2 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
     else launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks>), ga, dim3(kAttendThreads), st, a);
     return hipGetLastError();
 }
