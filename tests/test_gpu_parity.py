@@ -113,6 +113,31 @@ def test_propose_bitexact(case, variant):
     assert_pool_equal(pool.cpu().numpy(), opool)
 
 
+# Grids of more than 1024 chunk workgroups: the selection kernels take 2, 4 or 8 chunks per
+# workgroup (the chunk count is no multiple of 4 or 8 in the last two, so the last group has
+# chunks past the key row; ragged and empty sequences put groups past T_b).
+GROUPED_CASES = [
+    # D, G, B, Hkv, T, kp, lens
+    (128, 4, 4, 16, 20000, 2000, [20000, 12345, 0, 7777]),             # 64 units x 20 chunks: 2
+    (64, 2, 4, 16, 41000, 4096, [41000, 40100, 1025, 41000]),          # 64 units x 41 chunks: 4
+    (64, 2, 8, 16, 33000, 3000, [33000, 1, 32768, 33000, 20000, 33000, 0, 9999]),  # 128 x 33: 8
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_CASES, ids=lambda c: f"U{c[2] * c[3]}T{c[4]}")
+@pytest.mark.parametrize("variant", ["random", "ties"])
+def test_propose_grouped_chunks_bitexact(case, variant):
+    D, G, Bn, Hkv, T, kp, lens = case
+    q, K, V, lens = make_inputs(seed_of(D, G, T, kp, variant), Bn, G * Hkv, Hkv, D, T, "bf16", lens,
+                                ties=variant == "ties")
+    Kq, sc, ld = gpu_quant(K, "bf16", lens)
+    pool = PB.propose(dev(q, "bf16"), Kq, sc, kp, PB.AGG_SUM, seq_lens=ld)
+    torch.cuda.synchronize()
+    oKq, osc = oracle.quantize_rows(K)
+    opool = oracle.propose(q, oKq, osc, kp, seq_lens=lens, agg=PB.AGG_SUM)
+    assert_pool_equal(pool.cpu().numpy(), opool)
+
+
 # ------------------------------------------------------------------------------- INT2 proposal
 @pytest.mark.parametrize("D,dtype,T,lens", [(128, "f32", 3000, None), (64, "bf16", 3000, [3000, 1777]),
                                             (256, "bf16", 2500, [0, 2500]), (128, "bf16", 5000, None)])
