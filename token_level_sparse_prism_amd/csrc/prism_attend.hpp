@@ -227,9 +227,10 @@ constexpr int kRowsAccFloats = 8192;  // LDS floats for the waves' V partials (o
 // so both arrive in one round trip.  One barrier exchanges the per-wave maxima; a row's weights
 // go through the wave's own rows of s_p (NR*GP floats, 16-byte aligned).  The waves' partials
 // are summed in LDS in wave order, HB heads per round.  Writes g_ml[h] = (max_r y,
-// sum_r 2^(y - max)) and g_acc[h][d] = sum_r 2^(y - max) V[r][d] for h < G at device scope.
+// sum_r 2^(y - max)) and g_acc[h * AS + d] = sum_r 2^(y - max) V[r][d] for h < G at device scope
+// (AS: the partial's row stride, D unless the rows are a column range of wider rows).
 // LDS: s_red 2*(NT/64)*GP floats, s_wacc kRowsAccFloats floats.
-template <typename T, int D, int GP, int NR, int NT, typename VRow>
+template <typename T, int D, int GP, int NR, int NT, typename VRow, int AS = D>
 __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restrict__ logits, int LS,
                                                float y_scale, const int32_t* s_slot, const int32_t* s_tok, int n,
                                                int G, float* s_p, float* s_red, float* s_wacc,
@@ -360,7 +361,7 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
             float sacc = s_wacc[h * D + dd];
 #pragma unroll
             for (int w = 1; w < NW; ++w) sacc += s_wacc[(w * HB + h) * D + dd];
-            st_dev(&g_acc[(hb + h) * D + dd], sacc);
+            st_dev(&g_acc[(hb + h) * AS + dd], sacc);
         }
     }
     if (wave == 0) {
@@ -377,12 +378,12 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
     }
 }
 
-// Log-sum-exp merge of `np` partials (partial s at g_ml + s*GP*2, g_acc + s*GP*D), read at
+// Log-sum-exp merge of `np` partials (partial s at g_ml + s*GP*2, g_acc + s*GP*AS; rows of AS), read at
 // device scope, sixteen partials per batch of independent loads: the batch's maximum first, then
 // every partial's weight on its own.  Writes out[h][d] (dtype T) and lse[h] (natural log) for
 // h < G; np == 0 gives out = 0, lse = -inf.  With kToPartial it writes instead one partial of the
 // same form (o_ml, o_acc, at device scope): the merge of the np partials, m = -inf for np == 0.
-template <typename T, int D, int GP, int NT = kThreads, bool kToPartial = false>
+template <typename T, int D, int GP, int NT = kThreads, bool kToPartial = false, int AS = D>
 __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, const float* __restrict__ g_acc, int np, int G,
                                T* __restrict__ out, float* __restrict__ lse, float* __restrict__ o_ml = nullptr,
                                float* __restrict__ o_acc = nullptr) {
@@ -399,7 +400,7 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, c
                 const bool ok = s < np;
                 m[u] = ok ? ld_dev(&g_ml[(s * GP + h) * 2]) : -INFINITY;
                 l[u] = ok ? ld_dev(&g_ml[(s * GP + h) * 2 + 1]) : 0.0f;
-                v[u] = ok ? ld_dev(&g_acc[(int64_t(s) * GP + h) * D + dd]) : 0.0f;
+                v[u] = ok ? ld_dev(&g_acc[(int64_t(s) * GP + h) * AS + dd]) : 0.0f;
             }
             float Mn = M;
 #pragma unroll
@@ -416,14 +417,14 @@ __device__ __forceinline__ void merge_partials(const float* __restrict__ g_ml, c
             M = Mn;
         }
         if constexpr (kToPartial) {
-            st_dev(&o_acc[h * D + dd], acc);
+            st_dev(&o_acc[h * AS + dd], acc);
             if (dd == 0) {
                 st_dev(&o_ml[2 * h], M);
                 st_dev(&o_ml[2 * h + 1], L);
             }
         } else {
             const bool empty = np == 0;
-            store_elem<T>(&out[int64_t(h) * D + dd], empty ? 0.0f : acc / L);
+            store_elem<T>(&out[int64_t(h) * AS + dd], empty ? 0.0f : acc / L);
             if (dd == 0 && lse) lse[h] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
         }
     }

@@ -23,6 +23,10 @@
 #include "prism_prof.hpp"
 #include "prism_select.hpp"
 
+#ifndef PRISM_ATTEND_COLSPLIT
+#define PRISM_ATTEND_COLSPLIT 1  // split the rank-split attention's columns in two on small grids
+#endif
+
 namespace prism {
 
 template <typename T, int D, int GP, bool kMax>
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(kRscoreThreads) void k_rscore_mfma(RefineArgs a) {
     }
 }
 
-template <typename T, int D, int GP, int NR>
+template <typename T, int D, int GP, int NR, int DS = 1>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     constexpr int NT = kAttendThreads;
     constexpr int NW = NT / 64;
@@ -201,7 +205,9 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     const int tid = threadIdx.x;
     const UnitIdx ui = unit_major();
     const int unit = ui.unit;
-    const int slice = ui.x;
+    const int slice = ui.x / DS;  // DS workgroups per slice of ranks, each for D / DS of the columns
+    const int half = ui.x % DS;
+    constexpr int DH = D / DS;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
     const int64_t kp = a.kp;
@@ -214,17 +220,17 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     // ---- the slice's softmax(.)V partial, then idx.  s_tok holds the selected slots' record ids:
     // token ids, or with paged caches the row inside the KV head's pool (pool scoring found it) ----
     const bool paged = d.pg.table != nullptr;
-    const int nsa = int(gridDim.x);
+    const int nsa = int(gridDim.x) / DS;
     float* part_ml = a.part_ml + int64_t(unit) * nsa * GP * 2;
     float* part_acc = a.part_acc + int64_t(unit) * nsa * GP * D;
-    if (n > 0) {
-        const T* Vb = static_cast<const T*>(a.V) + cache_row0(d, b, g) * D;
+    if (n > 0) {  // the DS workgroups of a slice write the same (m, l), each its columns of acc
+        const T* Vb = static_cast<const T*>(a.V) + cache_row0(d, b, g) * D + half * DH;
         auto vrow = [&](int32_t id) -> const T* { return Vb + int64_t(uint32_t(id)) * D; };
-        softmax_v_rows<T, D, GP, NR, NT>(vrow, a.logits + int64_t(unit) * kp * LS, LS, a.y_scale, s_slot, s_tok, n, G,
-                                         s_p, s_red, reinterpret_cast<float*>(s_big), part_acc + int64_t(slice) * GP * D,
-                                         part_ml + int64_t(slice) * GP * 2);
+        softmax_v_rows<T, DH, GP, NR, NT, decltype(vrow), D>(
+            vrow, a.logits + int64_t(unit) * kp * LS, LS, a.y_scale, s_slot, s_tok, n, G, s_p, s_red,
+            reinterpret_cast<float*>(s_big), part_acc + int64_t(slice) * GP * D + half * DH, part_ml + int64_t(slice) * GP * 2);
     }
-    if (tid < NR && r0 + tid < a.kappa) {
+    if (half == 0 && tid < NR && r0 + tid < a.kappa) {
         int32_t t = -1;
         if (tid < n) t = paged ? a.pool[int64_t(unit) * kp + s_slot[tid]] : s_tok[tid];
         a.idx[int64_t(unit) * a.kappa + r0 + tid] = t;
@@ -232,12 +238,13 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
 
     const int np = int((sr.kappa_eff + NR - 1) / NR);  // slices that wrote a partial
     const int64_t hq0 = int64_t(b) * d.Hq + int64_t(g) * G;
-    T* out = static_cast<T*>(a.out) + hq0 * D;
-    float* lse = a.lse ? a.lse + hq0 : nullptr;
+    T* out = static_cast<T*>(a.out) + hq0 * D + half * DH;
+    float* lse = a.lse && half == 0 ? a.lse + hq0 : nullptr;
+    uint32_t* done = &a.done_a[int64_t(unit) * kCtrStride + half];  // one counter per column range
     if (nsa <= kMergeGroup) {  // one level: the last slice merges every partial
-        if (!arrive_last(&a.done_a[int64_t(unit) * kCtrStride], nsa, &s_flag)) return;
-        merge_partials<T, D, GP, NT>(part_ml, part_acc, np, G, out, lse);
-        if (tid == 0) a.done_a[int64_t(unit) * kCtrStride] = 0u;
+        if (!arrive_last(done, nsa, &s_flag)) return;
+        merge_partials<T, DH, GP, NT, false, D>(part_ml, part_acc + half * DH, np, G, out, lse);
+        if (tid == 0) *done = 0u;
         return;
     }
     // two levels: the last slice of each group of kMergeGroup merges the group's partials into a
@@ -245,18 +252,18 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     const int ngrp = (nsa + kMergeGroup - 1) / kMergeGroup;
     const int grp = slice / kMergeGroup;
     const int gsz = nsa - grp * kMergeGroup < kMergeGroup ? nsa - grp * kMergeGroup : kMergeGroup;
-    uint32_t* cg = a.done_g + (int64_t(unit) * ngrp + grp) * kCtrStride;
+    uint32_t* cg = a.done_g + (int64_t(unit) * ngrp + grp) * kCtrStride + half;
     if (!arrive_last(cg, gsz, &s_flag)) return;
     const int gnp = np - grp * kMergeGroup <= 0 ? 0 : (np - grp * kMergeGroup < kMergeGroup ? np - grp * kMergeGroup : kMergeGroup);
     float* g2_ml = a.part2_ml + int64_t(unit) * ngrp * GP * 2;
     float* g2_acc = a.part2_acc + int64_t(unit) * ngrp * GP * D;
-    merge_partials<T, D, GP, NT, true>(part_ml + int64_t(grp) * kMergeGroup * GP * 2,
-                                       part_acc + int64_t(grp) * kMergeGroup * GP * D, gnp, G, nullptr, nullptr,
-                                       g2_ml + int64_t(grp) * GP * 2, g2_acc + int64_t(grp) * GP * D);
+    merge_partials<T, DH, GP, NT, true, D>(part_ml + int64_t(grp) * kMergeGroup * GP * 2,
+                                           part_acc + int64_t(grp) * kMergeGroup * GP * D + half * DH, gnp, G, nullptr,
+                                           nullptr, g2_ml + int64_t(grp) * GP * 2, g2_acc + int64_t(grp) * GP * D + half * DH);
     if (tid == 0) *cg = 0u;
-    if (!arrive_last(&a.done_a[int64_t(unit) * kCtrStride], ngrp, &s_flag)) return;
-    merge_partials<T, D, GP, NT>(g2_ml, g2_acc, (np + kMergeGroup - 1) / kMergeGroup, G, out, lse);
-    if (tid == 0) a.done_a[int64_t(unit) * kCtrStride] = 0u;
+    if (!arrive_last(done, ngrp, &s_flag)) return;
+    merge_partials<T, DH, GP, NT, false, D>(g2_ml, g2_acc + half * DH, (np + kMergeGroup - 1) / kMergeGroup, G, out, lse);
+    if (tid == 0) *done = 0u;
 }
 
 // `hi` on the lanes of the banks ((lane / 4) % 4) in BANKM, `lo` elsewhere: a DPP move with an
@@ -515,7 +522,18 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     }
     if (nr == 4 * kAttendRanks) launch_k("k_attend", (k_attend<T, D, GP, 4 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
     else if (nr == 2 * kAttendRanks) launch_k("k_attend", (k_attend<T, D, GP, 2 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
-    else launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks>), ga, dim3(kAttendThreads), st, a);
+    else {
+        // at most half the CUs busy at 128 ranks: two workgroups per slice, each for half the
+        // columns of V (half the rows' bytes each; the merges run per half)
+        if constexpr (PRISM_ATTEND_COLSPLIT && D / 2 >= 64) {
+            if (2 * n128 <= cus) {
+                launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks, 2>), dim3(2 * ga.x, ga.y), dim3(kAttendThreads), st,
+                         a);
+                return hipGetLastError();
+            }
+        }
+        launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks>), ga, dim3(kAttendThreads), st, a);
+    }
     return hipGetLastError();
 }
 
