@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     const UnitIdx ui = unit_major();
     const int unit = ui.unit;
     const int slice = ui.x / DS;  // DS workgroups per slice of ranks, each for D / DS of the columns
-    const int half = ui.x % DS;
+    const int half = ui.x % DS;   // this workgroup's column range
     constexpr int DH = D / DS;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
     const int G = d.G;
@@ -523,8 +523,16 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     if (nr == 4 * kAttendRanks) launch_k("k_attend", (k_attend<T, D, GP, 4 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
     else if (nr == 2 * kAttendRanks) launch_k("k_attend", (k_attend<T, D, GP, 2 * kAttendRanks>), ga, dim3(kAttendThreads), st, a);
     else {
-        // at most half the CUs busy at 128 ranks: two workgroups per slice, each for half the
-        // columns of V (half the rows' bytes each; the merges run per half)
+        // at most a quarter (a half) of the CUs busy at 128 ranks: four (two) workgroups per
+        // slice, each for that share of the columns of V (that share of the rows' bytes; the
+        // merges run per column range)
+        if constexpr (PRISM_ATTEND_COLSPLIT && D / 4 >= 64) {
+            if (4 * n128 <= cus) {
+                launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks, 4>), dim3(4 * ga.x, ga.y), dim3(kAttendThreads), st,
+                         a);
+                return hipGetLastError();
+            }
+        }
         if constexpr (PRISM_ATTEND_COLSPLIT && D / 2 >= 64) {
             if (2 * n128 <= cus) {
                 launch_k("k_attend", (k_attend<T, D, GP, kAttendRanks, 2>), dim3(2 * ga.x, ga.y), dim3(kAttendThreads), st,
