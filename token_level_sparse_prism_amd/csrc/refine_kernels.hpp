@@ -7,7 +7,8 @@
 //             heads' logits (fp32) and the group score S, and stores the logits and {order key
 //             of S, id} per slot (key 0 for an empty slot; id = the token, or with paged caches
 //             its row in the KV head's pool).  Plain (cached) stores: k_attend reads them next.
-//   k_attend  grid (128 or 256 selected ranks) x units, 1024 threads.  Every workgroup derives the
+//   k_attend  grid (slices of 128, 256 or 512 selected ranks; on small grids 2 or 4 workgroups
+//             per slice, each for a range of the V columns) x units, 1024 threads.  Every workgroup derives the
 //             exact top-kappa of its unit from the keys, ranks the selected
 //             slots in slot order (ties to the lower slot), writes idx for its ranks, gathers
 //             their V rows and forms a softmax(.)V partial from the stored logits.  The unit's
