@@ -331,7 +331,10 @@ hipError_t launch_propose(const ProposeArgs& args, int agg_max, hipStream_t st) 
     // chunks per selection workgroup: one while the grid has at most kSelWgs workgroups, then
     // enough (up to 8) to bring it back there; a group shares the histogram reads and the pass
     // over the candidate lists, which every workgroup repeats
-    constexpr int64_t kSelWgs = 1024;
+#ifndef PRISM_SEL_WGS
+#define PRISM_SEL_WGS 512
+#endif
+    constexpr int64_t kSelWgs = PRISM_SEL_WGS;
     int M = 1;
     while (M < 8 && int64_t(units) * a.nchunks > kSelWgs * M) M *= 2;
     const dim3 grid((a.nchunks + M - 1) / M, units);
