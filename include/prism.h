@@ -38,10 +38,18 @@
  *  - Errors: a call that fails validation writes nothing and launches
  *    nothing.
  *  - Workspace: query its size with prism_workspace_bytes.  It must be
- *    zero-filled before its first use (prism_workspace_init does that);
- *    every call that completes leaves its control words zero again, so a
- *    workspace is reused without re-initialisation.  Calls that run at the
- *    same time must use different workspaces.
+ *    zero-filled before its first use (prism_workspace_init does that).
+ *    The proposal calls need their histogram words zero on entry and leave
+ *    them zero on completion; refine calls zero their own arrival counters
+ *    (their first kernel does), and the refine and dense layouts keep their
+ *    data clear of the proposal's zero-on-entry words of the same B*Hkv and
+ *    T_max.  So one zero-filled workspace, large enough for each call, serves
+ *    any sequence of completed calls in which every proposal call has the
+ *    same B*Hkv and T_max; a proposal call with a different B*Hkv or T_max
+ *    than the previous one on that workspace needs prism_workspace_init
+ *    first (its histogram may then overlap words the previous call left
+ *    non-zero, which would give wrong pools without an error).  Calls that
+ *    run at the same time must use different workspaces.
  *  - Determinism: pools and index sets are bit-identical from run to run;
  *    attention outputs are too (fixed split and merge order).
  */
@@ -208,8 +216,11 @@ prism_status prism_refine_attend_paged(const void* q, const void* K_pool, const 
 /*
  * Dense decode attention over every t < T_b (the kappa = kp = T_b special
  * case of the refined layer): out[h] = softmax(q[h] . K[0..T_b) * sm_scale)
- * . V[0..T_b), lse as above.  A reference and a baseline, not part of the
- * sparse path.  Workspace: prism_workspace_bytes(PRISM_OP_DENSE, s, 0, 0).
+ * . V[0..T_b), lse as above.  This is the full attention that the Prism
+ * page's efficiency comparison (Sec. 5.3, end-to-end latency against
+ * FlashAttention at 16K-128K contexts) measures the sparse path against:
+ * here a reference and a baseline, not part of the sparse path.
+ * Workspace: prism_workspace_bytes(PRISM_OP_DENSE, s, 0, 0).
  */
 prism_status prism_dense_ref(const void* q, const void* K, const void* V, prism_dtype dt,
                              const prism_shape* s, float sm_scale, void* out, float* lse,

@@ -113,21 +113,36 @@ def test_propose_bitexact(case, variant):
     assert_pool_equal(pool.cpu().numpy(), opool)
 
 
-# Grids of more than 1024 chunk workgroups: the selection kernels take 2, 4 or 8 chunks per
-# workgroup (the chunk count is no multiple of 4 or 8 in the last two, so the last group has
-# chunks past the key row; ragged and empty sequences put groups past T_b).
+SEL_WGS = 512  # the proposal selection's workgroup target (the launcher's PRISM_SEL_WGS)
+
+
+def chunks_per_selection_wg(units, T):
+    """M of the launcher: 1 while units x chunks <= SEL_WGS, else doubled (up to 8) until the
+    grid of chunk groups is back at or below SEL_WGS * M."""
+    nchunks = -(-T // 1024)
+    m = 1
+    while m < 8 and units * nchunks > SEL_WGS * m:
+        m *= 2
+    return m
+
+
+# Grids of more than SEL_WGS chunk workgroups: the selection kernels take 2, 4 or 8 chunks per
+# workgroup.  Every chunk count below is odd or no multiple of M, so the last group holds chunks
+# past the key row; ragged and empty sequences put whole groups past T_b.
 GROUPED_CASES = [
-    # D, G, B, Hkv, T, kp, lens
-    (128, 4, 4, 16, 20000, 2000, [20000, 12345, 0, 7777]),             # 64 units x 20 chunks: 2
-    (64, 2, 4, 16, 41000, 4096, [41000, 40100, 1025, 41000]),          # 64 units x 41 chunks: 4
-    (64, 2, 8, 16, 33000, 3000, [33000, 1, 32768, 33000, 20000, 33000, 0, 9999]),  # 128 x 33: 8
+    # D, G, B, Hkv, T, kp, lens, expected M
+    (128, 4, 2, 8, 33000, 1500, [33000, 17000], 2),                      # 16 units x 33 chunks
+    (128, 4, 4, 16, 20000, 2000, [20000, 12345, 0, 7777], 4),            # 64 units x 20 chunks
+    (64, 2, 4, 16, 41000, 4096, [41000, 40100, 1025, 41000], 8),         # 64 units x 41 chunks
+    (64, 2, 8, 16, 33000, 3000, [33000, 1, 32768, 33000, 20000, 33000, 0, 9999], 8),  # 128 x 33
 ]
 
 
-@pytest.mark.parametrize("case", GROUPED_CASES, ids=lambda c: f"U{c[2] * c[3]}T{c[4]}")
+@pytest.mark.parametrize("case", GROUPED_CASES, ids=lambda c: f"U{c[2] * c[3]}T{c[4]}M{c[7]}")
 @pytest.mark.parametrize("variant", ["random", "ties"])
 def test_propose_grouped_chunks_bitexact(case, variant):
-    D, G, Bn, Hkv, T, kp, lens = case
+    D, G, Bn, Hkv, T, kp, lens, M = case
+    assert chunks_per_selection_wg(Bn * Hkv, T) == M
     q, K, V, lens = make_inputs(seed_of(D, G, T, kp, variant), Bn, G * Hkv, Hkv, D, T, "bf16", lens,
                                 ties=variant == "ties")
     Kq, sc, ld = gpu_quant(K, "bf16", lens)
@@ -344,7 +359,12 @@ def test_paged_matches_contiguous(case, key_bits):
     assert torch.equal(out_p, out_c)
     assert torch.equal(lse_p, lse_c)
     lv, osc = (oracle.quantize_rows_int2 if key_bits == 2 else oracle.quantize_rows)(K)
-    assert_pool_equal(pool_p.cpu().numpy(), oracle.propose(q, lv, osc, kp, seq_lens=lens, agg=agg))
+    opool = oracle.propose(q, lv, osc, kp, seq_lens=lens, agg=agg)
+    assert_pool_equal(pool_p.cpu().numpy(), opool)
+    # the paged refined layer against the oracle on the logical caches (not only against the
+    # contiguous GPU path)
+    check_refine_batch(idx_p.cpu().numpy(), host(out_p), lse_p.cpu().numpy(), q, K, V, lens, opool, kappa, agg,
+                       dtype)
 
 
 # ------------------------------------------------------------------ proposal on CU-filling grids
@@ -501,10 +521,9 @@ def test_graph_replay_int2():
             assert torch.equal(a, b), f"replay {i}"
 
 
-def test_full_size_128k_sampled_units():
+def test_full_size_128k_all_units():
     """The 128K-context workload at full size, in the launch configuration the benchmark times:
-    every unit's pool, two units' refined layers in full against the oracle, and index sets
-    inside the pools everywhere."""
+    every unit's pool bit for bit and every unit's refined layers in full against the oracle."""
     c = W.CONFIGS["cfg3"]
     w = W.generate(c)
     step, Kq, sc = run_step_gpu(w, c.kp, c.kappa)
@@ -519,7 +538,7 @@ def test_full_size_128k_sampled_units():
         for g in range(c.Hkv):
             assert set(gidx[0, g].tolist()) <= set(gpool[0, g].tolist())
         check_refine_batch(gidx, host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(), w.q[l], w.K[l], w.V[l],
-                           w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype, units={(0, 0), (0, 5)})
+                           w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype)
 
 
 @pytest.mark.parametrize("name", ["cfg5_D256_k8192_r8", "cfg5_D64_k2048_r4"])
@@ -539,9 +558,9 @@ def test_full_size_262k_single_unit(name):
                            w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype)
 
 
-def test_full_size_cfg2_sampled_units():
-    """The 32K-context batch-4 workload at full size: every unit's pool bit for bit, and three
-    units' refined layers in full."""
+def test_full_size_cfg2_all_units():
+    """The 32K-context batch-4 workload at full size: every unit's pool bit for bit, and every
+    unit's refined layers in full."""
     c = W.CONFIGS["cfg2"]
     w = W.generate(c)
     step, Kq, sc = run_step_gpu(w, c.kp, c.kappa)
@@ -550,14 +569,13 @@ def test_full_size_cfg2_sampled_units():
     assert_pool_equal(step.pool.cpu().numpy(), opool)
     for l in range(1, w.layers):
         check_refine_batch(step.idx[l - 1].cpu().numpy(), host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(),
-                           w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype,
-                           units={(0, 0), (1, 3), (3, 7)})
+                           w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype)
 
 
 def test_full_size_128k_int2():
     """The 128K-context workload with INT2 proposal keys: the packed codes and scales, every
-    unit's pool bit for bit, two units' refined layers in full, and the anchor's unshifted planted
-    tokens in every pool."""
+    unit's pool bit for bit, every unit's refined layers in full, and the anchor's unshifted
+    planted tokens in every pool."""
     c = W.CONFIGS["cfg3"]
     w = W.generate(c)
     step, Kq2, sc = run_step_gpu(w, c.kp, c.kappa, key_bits=2)
@@ -571,8 +589,7 @@ def test_full_size_128k_int2():
         assert np.isin(w.salient[(0, g)][0], gpool[0, g]).all()
     for l in range(1, w.layers):
         check_refine_batch(step.idx[l - 1].cpu().numpy(), host(step.out[l - 1]), step.lse[l - 1].cpu().numpy(),
-                           w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype,
-                           units={(0, 1), (0, 6)})
+                           w.q[l], w.K[l], w.V[l], w.seq_lens, opool, c.kappa, PB.AGG_SUM, c.dtype)
 
 
 def test_graph_replay_matches_eager():
@@ -592,3 +609,118 @@ def test_graph_replay_matches_eager():
         cur = [step.pool] + list(step.idx) + list(step.out)
         for a, b in zip(ref, cur):
             assert torch.equal(a, b), f"replay {i}"
+
+
+@pytest.mark.timeout(900)
+def test_full_shape_cfg4():
+    """The batched long-context workload at its real shape (8 sequences of 16K-128K tokens from
+    the seed-4 draw, 64 query / 8 KV heads, 7 refined layers), generated one layer at a time
+    straight to the device as the benchmark does: every unit's pool bit for bit (each unit's
+    anchor keys regenerated on the host), and the refined layers of 8 units against the oracle
+    (units spread over every sequence, the shortest and longest among them)."""
+    c = W.CONFIGS["cfg4"]
+    lens = c.lengths()
+    ld = torch.from_numpy(lens).cuda()
+    from token_level_sparse_prism_amd.step import LayerInputs, PrismStep
+    q_host, layers = [], []
+    sample = [(b, (3 * b + 1) % c.Hkv) for b in range(c.B)]
+    kept = {}
+    Kq = sc = q0 = None
+    for l in range(c.n_refined + 1):
+        wl = W.generate(c, layers=[l])
+        q_host.append(wl.q[0])
+        if l == 0:
+            K0 = dev(wl.K[0], c.dtype)
+            Kq, sc = PB.quantize_keys(K0, seq_lens=ld)
+            q0 = dev(wl.q[0], c.dtype)
+            del K0
+        else:
+            layers.append(LayerInputs(dev(wl.q[0], c.dtype), dev(wl.K[0], c.dtype), dev(wl.V[0], c.dtype)))
+            for (b, g) in sample:
+                kept[(l, b, g)] = (wl.K[0][b, g].copy(), wl.V[0][b, g].copy())
+        del wl
+        torch.cuda.synchronize()
+    step = PrismStep(q0, Kq, sc, layers, c.kp, c.kappa, seq_lens=ld)
+    step()
+    torch.cuda.synchronize()
+    gpool = step.pool.cpu().numpy()
+    gidx = [t.cpu().numpy() for t in step.idx]
+    gout = [host(t) for t in step.out]
+    glse = [t.cpu().numpy() for t in step.lse]
+    G = c.G
+    for b in range(c.B):
+        T_b = int(lens[b])
+        for g in range(c.Hkv):
+            K0, _ = W.unit_tensors(c, b, g, 0, q_host[0], T_b, want_v=False)
+            oKq, osc = oracle.quantize_rows(K0)
+            opool, _ = oracle.propose_unit(q_host[0][b, g * G:(g + 1) * G], oKq, osc, T_b, c.kp)
+            assert_pool_equal(gpool[b, g][None], opool[None])
+            if (b, g) not in sample:
+                continue
+            for l in range(1, c.n_refined + 1):
+                Kl, Vl = kept[(l, b, g)]
+                from tests.parity import check_refine_unit
+                check_refine_unit(gidx[l - 1][b, g], gout[l - 1][b, g * G:(g + 1) * G],
+                                  glse[l - 1][b, g * G:(g + 1) * G], q_host[l][b, g * G:(g + 1) * G], Kl, Vl, T_b,
+                                  opool, c.kappa, PB.AGG_SUM, c.dtype, where=f"layer {l} unit ({b},{g})")
+
+
+def test_shared_workspace_propose_refine():
+    """One zero-filled workspace, sized for the larger of the two ops, serves a proposal, the
+    refined layers, the next proposal and so on: the results equal those of separate workspaces
+    (the refine layout keeps its data clear of the proposal's zero-on-entry histogram, and pool
+    scoring zeroes the attention's arrival counters itself)."""
+    c = W.CONFIGS["cfg2"].with_(B=2, T=20000, seq_lens=(20000, 11111))
+    w = W.generate(c)
+    ld = torch.from_numpy(w.seq_lens).cuda()
+    Kq, sc = PB.quantize_keys(dev(w.K[0], c.dtype), seq_lens=ld)
+    q0 = dev(w.q[0], c.dtype)
+    layers = [(dev(w.q[l], c.dtype), dev(w.K[l], c.dtype), dev(w.V[l], c.dtype)) for l in range(1, w.layers)]
+    shp = PB.make_shape(q0, Kq, ld)
+    nbytes = max(PB.workspace_bytes(PB.OP_PROPOSE, shp, c.kp), PB.workspace_bytes(PB.OP_REFINE, shp, c.kp, c.kappa))
+    shared = PB.new_workspace_bytes(nbytes)
+    ref_pool = PB.propose(q0, Kq, sc, c.kp, seq_lens=ld)
+    ref = [PB.refine_attend(q, K, V, ref_pool, c.kappa, seq_lens=ld) for q, K, V in layers]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        pool = PB.propose(q0, Kq, sc, c.kp, seq_lens=ld, ws=shared)
+        outs = [PB.refine_attend(q, K, V, pool, c.kappa, seq_lens=ld, ws=shared) for q, K, V in layers]
+        torch.cuda.synchronize()
+        assert torch.equal(pool, ref_pool), f"pass {rep}: pool"
+        for (o, i, s_), (ro, ri, rs) in zip(outs, ref):
+            assert torch.equal(i, ri) and torch.equal(o, ro) and torch.equal(s_, rs), f"pass {rep}: refine"
+
+
+@pytest.mark.parametrize("name,overrides", [("cfg2", {"B": 2, "T": 32768}), ("cfg3", {"Hkv": 2, "Hq": 8})])
+def test_anchor_attention_step(name, overrides):
+    """The step variant in which the anchor layer also attends: refine_attend on layer 0's exact
+    K and V with the pool it proposed.  Its index set and outputs against the oracle's refine on
+    layer 0 with the oracle's pool, and the refined layers unchanged by it."""
+    from token_level_sparse_prism_amd.step import LayerInputs, PrismStep
+    c = W.CONFIGS[name].with_(anchor_v=True, **overrides)
+    w = W.generate(c)
+    ld = torch.from_numpy(w.seq_lens).cuda()
+    K0 = dev(w.K[0], c.dtype)
+    Kq, sc = PB.quantize_keys(K0, seq_lens=ld)
+    q0 = dev(w.q[0], c.dtype)
+    layers = [LayerInputs(dev(w.q[l], c.dtype), dev(w.K[l], c.dtype), dev(w.V[l], c.dtype))
+              for l in range(1, w.layers)]
+    step = PrismStep(q0, Kq, sc, layers, c.kp, c.kappa, seq_lens=ld,
+                     anchor=LayerInputs(q0, K0, dev(w.V[0], c.dtype)))
+    plain = PrismStep(q0, Kq, sc, layers, c.kp, c.kappa, seq_lens=ld)
+    step()
+    torch.cuda.synchronize()
+    anchor = (step.idx_anchor.cpu().numpy(), host(step.out_anchor), step.lse_anchor.cpu().numpy())
+    refined = [(t.clone(), o.clone()) for t, o in zip(step.idx, step.out)]
+    plain()
+    torch.cuda.synchronize()
+    oKq, osc = oracle.quantize_rows(w.K[0])
+    opool = oracle.propose(w.q[0], oKq, osc, c.kp, seq_lens=w.seq_lens)
+    assert_pool_equal(step.pool.cpu().numpy(), opool)
+    check_refine_batch(anchor[0], anchor[1], anchor[2], w.q[0], w.K[0], w.V[0], w.seq_lens, opool, c.kappa,
+                       PB.AGG_SUM, c.dtype)
+    for b in range(c.B):  # the anchor's own planted tokens are what its attention selects
+        for g in range(c.Hkv):
+            assert np.isin(w.salient[(b, g)][0], anchor[0][b, g]).all()
+    for (i, o), i2, o2 in zip(refined, plain.idx, plain.out):
+        assert torch.equal(i, i2) and torch.equal(o, o2)

@@ -241,6 +241,34 @@ def test_pool_equals_repeated_argmax(T, G, D):
             assert pool.tolist() == pad(argmax_select(scores.tolist(), kp), kp).tolist()
 
 
+def argmax_select_np(scores, k):
+    """Repeated argmax as above, vectorised for T in the thousands: np.argmax returns the first
+    (lowest-index) maximum, and a taken entry drops to -inf."""
+    s = np.asarray(scores, dtype=np.float64).copy()
+    chosen = []
+    for _ in range(min(k, s.size)):
+        t = int(np.argmax(s))
+        chosen.append(t)
+        s[t] = -np.inf
+    return sorted(chosen)
+
+
+@pytest.mark.parametrize("G,D", [(4, 128), (1, 64), (8, 256)])
+def test_pool_equals_repeated_argmax_4096(G, D):
+    """P1 at T = 4096 (one pool per kp in {1, T/4, T-1, T, T+5}), with duplicated rows among
+    Gaussian keys so that equal scores occur."""
+    T = 4096
+    rng = np.random.default_rng(4096 + G + D)
+    q = rng.standard_normal((G, D)).astype(np.float32)
+    K = rng.standard_normal((T, D)).astype(np.float32)
+    K[5::9] = K[4]
+    Kq, s = oracle.quantize_rows(K)
+    for kp in (1, T // 4, T - 1, T, T + 5):
+        for agg in (oracle.AGG_SUM, oracle.AGG_MAX):
+            pool, scores = oracle.propose_unit(q, Kq, s, T, kp, agg)
+            assert pool.tolist() == pad(argmax_select_np(scores, kp), kp).tolist()
+
+
 def test_all_equal_scores_take_lowest_indices():
     rng = np.random.default_rng(3)
     K = np.tile(rng.standard_normal((1, 64)).astype(np.float32), (100, 1))
@@ -298,6 +326,33 @@ def test_head_to_kv_head_mapping():
     assert pool[0, 0].tolist() == list(range(kp))
     single, _ = oracle.propose_unit(q[0, 5:6], Kq[0, 1], s[0, 1], T, kp)
     assert pool[0, 1].tolist() == single.tolist()
+
+
+def test_batched_dense_head_mapping():
+    """The batched dense wrapper maps query head h of sequence b to KV head h // G of that
+    sequence.  Only head 6 of sequence 1 is non-zero (6 // G = 1, while 6 mod Hkv = 0): its output
+    equals the one-unit dense attention over KV head 1 of sequence 1, and every zero head's output is the plain mean of its
+    own KV head's V rows (closed form: equal logits), with lse = log T_b."""
+    rng = np.random.default_rng(16)
+    B, Hq, Hkv, D, T = 2, 8, 2, 64, 50
+    lens = np.array([50, 37], np.int32)
+    q = np.zeros((B, Hq, D), np.float32)
+    q[1, 6] = rng.standard_normal(D)
+    K = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    out, lse = oracle.dense(q, K, V, seq_lens=lens)
+    G = Hq // Hkv
+    one_out, one_lse = oracle.dense_unit(q[1, 6:7], K[1, 1], V[1, 1], int(lens[1]))
+    np.testing.assert_allclose(out[1, 6], one_out[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[1, 6], one_lse[0], rtol=0, atol=1e-12)
+    for b in range(B):
+        for h in range(Hq):
+            if (b, h) == (1, 6):
+                continue
+            n = int(lens[b])
+            mean = V[b, h // G, :n].astype(np.float64).mean(0)
+            np.testing.assert_allclose(out[b, h], mean, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h], math.log(n), rtol=0, atol=1e-12)
 
 
 def test_ragged_lengths_and_short_sequences():

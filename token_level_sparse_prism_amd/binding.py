@@ -144,6 +144,12 @@ def new_workspace(op: int, shape: Shape, kp: int = 0, kappa: int = 0, device=Non
     n = workspace_bytes(op, shape, kp, kappa)
     if n == 0:
         raise PrismError("prism_workspace_bytes", 1)
+    return new_workspace_bytes(n, device=device, stream=stream)
+
+
+def new_workspace_bytes(n: int, device=None, stream=None) -> torch.Tensor:
+    """A zero-filled, 256-byte aligned workspace of n bytes (e.g. the larger of two ops' sizes,
+    for a workspace that the two share)."""
     ws = torch.empty(n + 256, dtype=torch.uint8, device=device or "cuda")
     off = (-ws.data_ptr()) % 256
     ws = ws[off:off + n]

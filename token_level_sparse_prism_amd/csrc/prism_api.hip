@@ -64,7 +64,7 @@ size_t prism_workspace_bytes(int op, const prism_shape* s, int32_t kp, int32_t k
             return propose_ws(units, s->T_max).total;
         case PRISM_OP_REFINE:
             if (kp < 1 || kappa < 1 || kappa > kp) return 0;
-            return refine_ws(units, kp, kappa, GP, s->D).total;
+            return refine_ws(units, s->T_max, kp, kappa, GP, s->D).total;
         case PRISM_OP_DENSE:
             return dense_ws(units, s->T_max, GP, s->D).total;
         default:
@@ -185,7 +185,7 @@ static prism_status refine_impl(const void* q, const void* K, const void* V, pri
         return PRISM_ERR_INVALID_ARG;
     const int64_t units = int64_t(s->B) * s->Hkv;
     const int GP = padded_g(s->Hq / s->Hkv);
-    const RefineWs L = refine_ws(units, kp, kappa, GP, s->D);
+    const RefineWs L = refine_ws(units, s->T_max, kp, kappa, GP, s->D);
     if (ws_bytes < L.total) return PRISM_ERR_WORKSPACE;
     if ((int64_t(kp) + kScoreSlice - 1) / kScoreSlice > 65535) return PRISM_ERR_UNSUPPORTED;
 
@@ -206,6 +206,8 @@ static prism_status refine_impl(const void* q, const void* K, const void* V, pri
     a.lse = lse;
     a.done_a = reinterpret_cast<uint32_t*>(carve(ws, L.done_a));
     a.done_g = reinterpret_cast<uint32_t*>(carve(ws, L.done_g));
+    a.ctrl = a.done_a;
+    a.ctrl_words = int(L.ctrl_bytes / 4);
     a.part2_ml = reinterpret_cast<float*>(carve(ws, L.part2_ml));
     a.part2_acc = reinterpret_cast<float*>(carve(ws, L.part2_acc));
     a.skey = reinterpret_cast<uint2*>(carve(ws, L.skey));

@@ -112,7 +112,10 @@ inline int padded_g(int G) {
 }
 inline int logit_stride(int GP) { return GP < 4 ? 4 : GP; }
 
-inline RefineWs refine_ws(int64_t units, int64_t kp, int64_t kappa, int GP, int D) {
+// The refine and dense layouts put their data after the proposal's zero-on-entry region of the
+// same (units, T_max), so a proposal, refine and dense calls of one shape can share a workspace:
+// none of them leaves anything but zeros in the others' control words.
+inline RefineWs refine_ws(int64_t units, int64_t T_max, int64_t kp, int64_t kappa, int GP, int D) {
     RefineWs w{};
     const int64_t nsa = (kappa + kAttendRanks - 1) / kAttendRanks;
     size_t o = 0;
@@ -120,6 +123,8 @@ inline RefineWs refine_ws(int64_t units, int64_t kp, int64_t kappa, int GP, int 
     w.done_a = o;   o = align256(o + size_t(units) * kCtrStride * 4);
     w.done_g = o;   o = align256(o + size_t(units) * ngrp * kCtrStride * 4);
     w.ctrl_bytes = o;
+    const size_t pc = propose_ws(units, T_max).ctrl_bytes;
+    o = o > pc ? o : pc;
     w.skey = o;     o = align256(o + size_t(units) * key_stride(kp) * 8);
     w.logits = o;   o = align256(o + size_t(units) * kp * logit_stride(GP) * 4);
     w.part_ml = o;  o = align256(o + size_t(units) * nsa * GP * 2 * 4);
@@ -140,6 +145,8 @@ inline DenseWs dense_ws(int64_t units, int64_t T_max, int GP, int D) {
     size_t o = 0;
     w.done = o;     o = align256(o + size_t(units) * kCtrStride * 4);
     w.ctrl_bytes = o;
+    const size_t pc = propose_ws(units, T_max).ctrl_bytes;
+    o = o > pc ? o : pc;
     w.part_ml = o;  o = align256(o + size_t(units) * nc * GP * 2 * 4);
     w.part_acc = o; o = align256(o + size_t(units) * nc * GP * D * 4);
     w.total = o;
@@ -201,6 +208,8 @@ struct RefineArgs {
     float* lse;
     uint32_t* done_a;       // [U][kCtrStride]
     uint32_t* done_g;       // [U][ngrp][kCtrStride]: per group of kMergeGroup slices (two-level merge)
+    uint32_t* ctrl;         // the arrival counters above, ctrl_words words from done_a: pool scoring
+    int ctrl_words;         // zeroes them, so a call needs no zeroed workspace
     uint2* skey;            // [U][kstride] {order key of S (0 = empty slot), id} per pool slot: id = the
                             // token, or with paged caches its row in the KV head's pool
     float* logits;          // [U][kp][LS]

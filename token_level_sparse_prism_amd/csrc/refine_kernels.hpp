@@ -30,6 +30,14 @@
 
 namespace prism {
 
+// The attention kernel's arrival counters are zeroed by the first pool-scoring workgroup (the
+// launch boundary orders these stores before every arrival), so a call never depends on what an
+// earlier call left in the workspace.
+__device__ __forceinline__ void zero_ctrl(const RefineArgs& a, int nthreads) {
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < a.ctrl_words; i += nthreads) a.ctrl[i] = 0u;
+}
+
 template <typename T, int D, int GP, bool kMax>
 __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
     constexpr int EPL = Elem<T>::kPerLane;
@@ -43,6 +51,7 @@ __global__ __launch_bounds__(kThreads) void k_rscore(RefineArgs a) {
 
     const Dims& d = a.d;
     const int lane = lane_id(), wave = wave_id();
+    zero_ctrl(a, kThreads);
     const UnitIdx ui = unit_major();
     const int unit = ui.unit;
     const int slice = ui.x;
@@ -117,6 +126,7 @@ __global__ __launch_bounds__(kRscoreThreads) void k_rscore_mfma(RefineArgs a) {
     constexpr int SLOTS = 16 * (kRscoreThreads / 64);
     const Dims& d = a.d;
     const int lane = lane_id(), wave = wave_id();
+    zero_ctrl(a, kRscoreThreads);
     const UnitIdx ui = unit_major();
     const int unit = ui.unit;
     const int b = unit / d.Hkv, g = unit % d.Hkv;
