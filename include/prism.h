@@ -206,6 +206,28 @@ prism_status prism_propose_paged(const void* q, prism_dtype qdt, const void* Kq_
                                  int32_t kp, prism_agg agg, int32_t* pool, float* scores, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/*
+ * prism_refine_attend without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same computation, arguments, outputs
+ * and errors as prism_refine_attend minus ws / ws_bytes.  Its scratch is a
+ * static device array of the library, 32 MiB (33554432 bytes) on each GPU
+ * it runs on, held until the process ends; the call allocates nothing.  It
+ * needs the refine layout's bytes for this shape, kp and kappa without the
+ * proposal-sharing gap: units * (8 * ceil4(kp) + 4 * kp * max(4, Gp))
+ * plus the split partials, about 24 MiB at B*Hkv = 64, kp = 8192,
+ * kappa = 2048, G = 8, D = 128; a call that needs more than 32 MiB returns
+ * PRISM_ERR_WORKSPACE before any device work.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (two streams,
+ * two host threads) race and give wrong results; calls ordered on one stream
+ * are safe (the call zeroes the counters it needs itself).  The first call
+ * on a device looks the array's address up once (hipGetSymbolAddress).
+ */
+prism_status prism_refine_attend_static(const void* q, const void* K, const void* V, prism_dtype dt,
+                                        const prism_shape* s, const int32_t* pool, int32_t kp,
+                                        int32_t kappa, prism_agg agg, float sm_scale, void* out,
+                                        int32_t* idx, float* lse, void* stream);
+
 /* prism_refine_attend over paged K and V pools (same outputs, workspace and
  * errors). */
 prism_status prism_refine_attend_paged(const void* q, const void* K_pool, const void* V_pool, prism_dtype dt,

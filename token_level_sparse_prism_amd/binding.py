@@ -21,7 +21,8 @@ STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_INVALID_ARG", 2: "PRISM_ERR_UNSUPPORTED",
 EXPORTS = ("prism_workspace_bytes", "prism_workspace_init", "prism_quantize_keys", "prism_propose",
            "prism_quantize_keys_int2", "prism_propose_int2", "prism_propose_paged", "prism_refine_attend_paged",
            "prism_refine_attend", "prism_dense_ref", "prism_profile_enable", "prism_profile_query",
-           "prism_profile_reset", "prism_last_hip_error", "prism_status_str", "prism_read_probe")
+           "prism_profile_reset", "prism_last_hip_error", "prism_status_str", "prism_read_probe",
+           "prism_refine_attend_static")
 KERNELS = ("k_quantize_keys", "k_quantize_keys_int2", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense",
            "k_read_probe")
 
@@ -72,11 +73,13 @@ def load():
                                               ctypes.c_size_t, _vp]
     lib.prism_refine_attend.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, _vp, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.prism_refine_attend_static.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, _vp, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp]
     lib.prism_dense_ref.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, ctypes.c_float, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp]
     for fn in ("prism_workspace_init", "prism_quantize_keys", "prism_propose", "prism_quantize_keys_int2",
                "prism_propose_int2", "prism_propose_paged", "prism_refine_attend_paged", "prism_refine_attend",
-               "prism_dense_ref", "prism_last_hip_error"):
+               "prism_dense_ref", "prism_last_hip_error", "prism_refine_attend_static"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.prism_profile_enable.argtypes = [ctypes.c_int]
     lib.prism_profile_enable.restype = ctypes.c_int
@@ -245,6 +248,30 @@ def refine_attend(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool: torch
     _check("prism_refine_attend", load().prism_refine_attend(
         _ptr(q), _ptr(K), _ptr(V), _dtype_code(q), ctypes.byref(shape), _ptr(pool), kp, kappa, agg,
         float(sm_scale), _ptr(out), _ptr(idx), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, idx, lse
+
+
+def refine_attend_static(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, pool: torch.Tensor, kappa: int,
+                         agg: int = AGG_SUM, sm_scale: float = 0.0, seq_lens: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
+    """Refined layer through the allocation-free entry point (the library's static scratch, no
+    workspace).  Pass out / idx / lse to keep this call free of allocations on the torch side too."""
+    for t, n in ((q, "q"), (K, "K"), (V, "V"), (pool, "pool")):
+        _need(t, n)
+    if not (q.dtype == K.dtype == V.dtype):
+        raise TypeError("q, K and V must share one dtype")
+    shape = make_shape(q, K, seq_lens)
+    kp = pool.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    if idx is None:
+        idx = torch.empty((shape.B, shape.Hkv, kappa), dtype=torch.int32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((shape.B, shape.Hq), dtype=torch.float32, device=q.device)
+    _check("prism_refine_attend_static", load().prism_refine_attend_static(
+        _ptr(q), _ptr(K), _ptr(V), _dtype_code(q), ctypes.byref(shape), _ptr(pool), kp, kappa, agg,
+        float(sm_scale), _ptr(out), _ptr(idx), _ptr(lse), _stream(stream)))
     return out, idx, lse
 
 

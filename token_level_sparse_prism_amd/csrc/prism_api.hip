@@ -3,12 +3,29 @@
 // work (and can be exercised on a host without a GPU).
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/prism.h"
 #include "prism_internal.hpp"
+#include "prism_prof.hpp"
 
 using namespace prism;
 
+// Scratch of prism_refine_attend_static: one copy per GPU, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device array: its device address is taken
+// once per device with hipGetSymbolAddress (static_scratch below) and only that address is used.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of the current device's copy of `scratch`, looked up on the first call on
+// that device (with the device current) and kept.
+prism_status static_scratch(void** out);
 
 thread_local int g_last_hip_error = 0;
 
@@ -49,6 +66,23 @@ prism_status hip_status(hipError_t e) {
 }
 
 uint8_t* carve(void* ws, size_t off) { return static_cast<uint8_t*>(ws) + off; }
+
+prism_status static_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return PRISM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return PRISM_ERR_HIP;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return PRISM_OK;
+}
 
 }  // namespace
 
@@ -174,24 +208,29 @@ prism_status prism_propose_paged(const void* q, prism_dtype qdt, const void* Kq_
 static prism_status refine_impl(const void* q, const void* K, const void* V, prism_dtype dt,
                                 const prism_shape* s, const prism_paging* paging, const int32_t* pool, int32_t kp,
                                 int32_t kappa, prism_agg agg, float sm_scale, void* out, int32_t* idx, float* lse,
-                                void* ws, size_t ws_bytes, void* stream) {
+                                void* ws, size_t ws_bytes, void* stream, bool use_static = false) {
     prism_status st = check_shape(s);
     if (st != PRISM_OK) return st;
     if (!valid_dtype(dt) || !valid_agg(agg)) return PRISM_ERR_INVALID_ARG;
     if (kp < 1 || kappa < 1 || kappa > kp || !(sm_scale >= 0.0f) || isinf(sm_scale)) return PRISM_ERR_INVALID_ARG;
-    if (!q || !K || !V || !pool || !out || !idx || !ws) return PRISM_ERR_INVALID_ARG;
+    if (!q || !K || !V || !pool || !out || !idx || (!ws && !use_static)) return PRISM_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16) || !aligned(pool, 4) ||
-        !aligned(idx, 4) || (lse && !aligned(lse, 4)) || !aligned(ws, 256))
+        !aligned(idx, 4) || (lse && !aligned(lse, 4)) || (!use_static && !aligned(ws, 256)))
         return PRISM_ERR_INVALID_ARG;
     const int64_t units = int64_t(s->B) * s->Hkv;
     const int GP = padded_g(s->Hq / s->Hkv);
-    const RefineWs L = refine_ws(units, s->T_max, kp, kappa, GP, s->D);
-    if (ws_bytes < L.total) return PRISM_ERR_WORKSPACE;
+    const RefineWs L = refine_ws(units, s->T_max, kp, kappa, GP, s->D, !use_static);
+    if (use_static) {
+        if (L.total > kStaticScratchBytes) return PRISM_ERR_WORKSPACE;
+    } else if (ws_bytes < L.total) {
+        return PRISM_ERR_WORKSPACE;
+    }
     if ((int64_t(kp) + kScoreSlice - 1) / kScoreSlice > 65535) return PRISM_ERR_UNSUPPORTED;
 
     RefineArgs a{};
     a.d = dims_of(s);
     if (paging && (st = paging_of(paging, s, &a.d.pg)) != PRISM_OK) return st;
+    if (use_static && (st = static_scratch(&ws)) != PRISM_OK) return st;
     a.q = q;
     a.K = K;
     a.V = V;
@@ -214,7 +253,10 @@ static prism_status refine_impl(const void* q, const void* K, const void* V, pri
     a.logits = reinterpret_cast<float*>(carve(ws, L.logits));
     a.part_ml = reinterpret_cast<float*>(carve(ws, L.part_ml));
     a.part_acc = reinterpret_cast<float*>(carve(ws, L.part_acc));
-    return hip_status(launch_refine(a, dt == PRISM_BF16, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream)));
+    if (use_static) prof_suppress(true);
+    const hipError_t e = launch_refine(a, dt == PRISM_BF16, agg == PRISM_AGG_MAX, static_cast<hipStream_t>(stream));
+    if (use_static) prof_suppress(false);
+    return hip_status(e);
 }
 
 prism_status prism_refine_attend(const void* q, const void* K, const void* V, prism_dtype dt,
@@ -222,6 +264,14 @@ prism_status prism_refine_attend(const void* q, const void* K, const void* V, pr
                                  prism_agg agg, float sm_scale, void* out, int32_t* idx, float* lse,
                                  void* ws, size_t ws_bytes, void* stream) {
     return refine_impl(q, K, V, dt, s, nullptr, pool, kp, kappa, agg, sm_scale, out, idx, lse, ws, ws_bytes, stream);
+}
+
+prism_status prism_refine_attend_static(const void* q, const void* K, const void* V, prism_dtype dt,
+                                        const prism_shape* s, const int32_t* pool, int32_t kp, int32_t kappa,
+                                        prism_agg agg, float sm_scale, void* out, int32_t* idx, float* lse,
+                                        void* stream) {
+    return refine_impl(q, K, V, dt, s, nullptr, pool, kp, kappa, agg, sm_scale, out, idx, lse, nullptr, 0, stream,
+                       true);
 }
 
 prism_status prism_refine_attend_paged(const void* q, const void* K_pool, const void* V_pool, prism_dtype dt,

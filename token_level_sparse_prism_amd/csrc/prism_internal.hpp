@@ -115,7 +115,8 @@ inline int logit_stride(int GP) { return GP < 4 ? 4 : GP; }
 // The refine and dense layouts put their data after the proposal's zero-on-entry region of the
 // same (units, T_max), so a proposal, refine and dense calls of one shape can share a workspace:
 // none of them leaves anything but zeros in the others' control words.
-inline RefineWs refine_ws(int64_t units, int64_t T_max, int64_t kp, int64_t kappa, int GP, int D) {
+inline RefineWs refine_ws(int64_t units, int64_t T_max, int64_t kp, int64_t kappa, int GP, int D,
+                          bool after_propose_ctrl = true) {
     RefineWs w{};
     const int64_t nsa = (kappa + kAttendRanks - 1) / kAttendRanks;
     size_t o = 0;
@@ -123,7 +124,7 @@ inline RefineWs refine_ws(int64_t units, int64_t T_max, int64_t kp, int64_t kapp
     w.done_a = o;   o = align256(o + size_t(units) * kCtrStride * 4);
     w.done_g = o;   o = align256(o + size_t(units) * ngrp * kCtrStride * 4);
     w.ctrl_bytes = o;
-    const size_t pc = propose_ws(units, T_max).ctrl_bytes;
+    const size_t pc = after_propose_ctrl ? propose_ws(units, T_max).ctrl_bytes : 0;
     o = o > pc ? o : pc;
     w.skey = o;     o = align256(o + size_t(units) * key_stride(kp) * 8);
     w.logits = o;   o = align256(o + size_t(units) * kp * logit_stride(GP) * 4);

@@ -34,7 +34,10 @@ hipEvent_t take_event() {
 
 }  // namespace
 
-bool prof_enabled() { return g_on.load(std::memory_order_relaxed); }
+thread_local bool t_suppress = false;
+
+bool prof_enabled() { return !t_suppress && g_on.load(std::memory_order_relaxed); }
+void prof_suppress(bool on) { t_suppress = on; }
 
 bool prof_pair(const char* name, hipEvent_t* begin, hipEvent_t* end) {
     std::lock_guard<std::mutex> lk(g_mu);

@@ -10,6 +10,9 @@
 namespace prism {
 
 bool prof_enabled();
+// Per-thread switch that keeps prof_enabled() false (event creation may allocate; the
+// allocation-free entry point turns timing off for its own launches).
+void prof_suppress(bool on);
 // Two timing events registered under `name`; false (and no events) when none can be created.
 bool prof_pair(const char* name, hipEvent_t* begin, hipEvent_t* end);
 
