@@ -50,6 +50,13 @@ def parse():
                         "the scan kernel's HBM traffic per launch to " + os.path.relpath(PMC_FILE, ROOT))
     p.add_argument("--pmc-command", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("", ""),
                    help="the two rocprofv3 command lines, recorded beside the ingested figures")
+    p.add_argument("--timeline", type=int, default=0, metavar="REPS",
+                   help="phase timeline instead of the benchmark: REPS passes of one proposal and one refined "
+                        "layer through the timeline build (lib/libprism_tl.so, built by "
+                        "`python -m token_level_sparse_prism_amd.build --timeline`); prints per-kernel spans, "
+                        "launch gaps and per-phase medians over the workgroups")
+    p.add_argument("--lib", default="", help="load this build of the library instead of lib/libprism.so "
+                                             "(or lib/libprism_tl.so with --timeline)")
     p.add_argument("--recall", action="store_true",
                    help="quality readout on the 262144-token stress workloads instead of the benchmark: "
                         "salient, attention-mass and exact top-kappa recall of Prism (kp = rho*kappa) "
@@ -175,6 +182,83 @@ def recall_readout():
     return 0
 
 
+TL_PHASE_NAMES = {
+    "k_scan": ["prologue", "stream", "flush"],
+    "k_cand": ["threshold bin", "candidates"],
+    "k_compact": ["digit A", "candidate pass", "last byte", "pool write"],
+    "k_rscore": ["score"],
+    "k_attend": ["selection", "rows + statistics", "accumulate + partial", "arrival", "merge"],
+    "k_select": ["keys + level-1 histogram", "crossing", "candidate lists", "exact threshold", "ranks"],
+    "k_rows": ["logits + V issue + wave max", "max barrier", "softmax + accumulate"],
+}
+
+
+def timeline_summary(recs, kernels):
+    """Medians over the passes of: each kernel's span (first workgroup start to last stamp), the
+    gap from one kernel's last stamp to the next one's first start, and per phase the median (and
+    the 90th percentile) over workgroups of the time between consecutive stamps (phases a
+    workgroup did not reach are left out).  Stamps tick at 100 MHz."""
+    import numpy as np
+    per = {k: {"span": [], "gap_before": [], "wgs": [], "phases": {}} for k in kernels}
+    for rec in recs:
+        prev_end = None
+        for k in kernels:
+            a = rec[k].astype(np.int64)
+            live = a[:, 0] > 0
+            if not live.any():
+                continue
+            a = a[live]
+            t0 = a[:, 0].min()
+            end = a.max()
+            per[k]["span"].append((end - t0) / 100.0)
+            per[k]["wgs"].append(int(live.sum()))
+            if prev_end is not None:
+                per[k]["gap_before"].append((t0 - prev_end) / 100.0)
+            prev_end = end
+            names = TL_PHASE_NAMES.get(k, [])
+            for p, name in enumerate(names):
+                ok = (a[:, p] > 0) & (a[:, p + 1] > 0)
+                if ok.any():
+                    d = (a[ok, p + 1] - a[ok, p]) / 100.0
+                    per[k]["phases"].setdefault(name, []).append((float(np.median(d)), float(np.percentile(d, 90)),
+                                                                  int(ok.sum())))
+    out = {}
+    for k in kernels:
+        v = per[k]
+        if not v["span"]:
+            continue
+        out[k] = {"workgroups": int(np.median(v["wgs"])), "span_us": round(float(np.median(v["span"])), 2),
+                  "gap_before_us": round(float(np.median(v["gap_before"])), 2) if v["gap_before"] else None,
+                  "phases_us": {n: {"median": round(float(np.median([x[0] for x in L])), 2),
+                                    "p90": round(float(np.median([x[1] for x in L])), 2),
+                                    "workgroups": int(np.median([x[2] for x in L]))}
+                                for n, L in v["phases"].items()}}
+    return out
+
+
+def timeline_readout(args, cfg, steps, R):
+    import torch
+    from token_level_sparse_prism_amd import binding as PB
+
+    kernels = list(PB.TL_KERNELS)
+    recs = []
+    for rep in range(args.timeline):
+        st = steps[rep % R]
+        PB.timeline_clear()
+        st.propose()
+        st.refine(0)
+        torch.cuda.synchronize()
+        recs.append({k: PB.timeline_read(k, 8192) for k in kernels})
+    summ = timeline_summary(recs, kernels)
+    print(json.dumps({"timeline": cfg.name, "passes": args.timeline, "kernels": summ}), flush=True)
+    for k, v in summ.items():
+        ph = ", ".join(f"{n} {x['median']:.2f} (p90 {x['p90']:.2f}, {x['workgroups']} wg)"
+                       for n, x in v["phases_us"].items())
+        gap = f"gap before {v['gap_before_us']:.2f} us, " if v["gap_before_us"] is not None else ""
+        print(f"{k:10s} {v['workgroups']:5d} wg  span {v['span_us']:6.2f} us  {gap}{ph}", flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.ingest_pmc:
@@ -193,7 +277,11 @@ def main():
     from token_level_sparse_prism_amd import workload as W
     from token_level_sparse_prism_amd.step import LayerInputs, PrismStep
 
-    PB.load()  # fail loudly if the HIP library is missing
+    if args.timeline:
+        from token_level_sparse_prism_amd import build as PBUILD
+        PB.load(args.lib or PBUILD.LIB_TL)  # the timeline build; fail loudly if it is missing
+    else:
+        PB.load(args.lib or None)  # fail loudly if the HIP library is missing
     cfg = W.CONFIGS[args.config]
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
@@ -258,6 +346,12 @@ def main():
         for b in range(cfg.B):
             for g in range(cfg.Hkv):
                 assert set(ii[b, g][ii[b, g] >= 0].tolist()) <= set(pool[b, g].tolist())
+
+    if args.timeline:
+        for i in range(args.warmup):
+            steps[i % R]()
+        torch.cuda.synchronize()
+        return timeline_readout(args, cfg, steps, R)
 
     if args.pmc_pass:
         for i in range(args.steps):

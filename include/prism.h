@@ -270,6 +270,20 @@ void prism_profile_reset(void);
  */
 prism_status prism_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Diagnostics: per-workgroup phase timeline, present only in the timeline build of the library
+ * (lib/libprism_tl.so, compiled with PRISM_TIMELINE=1; the normal build returns
+ * PRISM_ERR_UNSUPPORTED).  Thread 0 of every workgroup of the proposal and refine kernels
+ * stores the GPU's 100 MHz real-time counter at the kernel's phase points; each launch
+ * overwrites its workgroups' entries.  prism_timeline_read synchronises the device and copies
+ * kernel `kernel`'s (0 k_scan, 1 k_cand, 2 k_compact, 3 k_rscore, 4 k_attend; 5 and 6 are the
+ * selection and the rows phase inside k_attend) stamps of
+ * workgroups [0, max_wgs) (linear workgroup id, at most 8192) into out[max_wgs][8]; 0 marks a
+ * phase a workgroup did not reach.  prism_timeline_clear zeroes every stamp.
+ */
+prism_status prism_timeline_read(int kernel, unsigned long long* out, int64_t max_wgs);
+prism_status prism_timeline_clear(void);
+
 /* The hipError_t of the last failed HIP call on this thread (0 if none). */
 int prism_last_hip_error(void);
 

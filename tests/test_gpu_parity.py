@@ -28,7 +28,7 @@ def rnd(rng, shape, dtype):
     return W.bf16_round(x) if dtype == "bf16" else x
 
 
-def make_inputs(seed, Bn, Hq, Hkv, D, T, dtype, lens=None, ties=False, zero_q=False, clustered=False):
+def make_inputs(seed, Bn, Hq, Hkv, D, T, dtype, lens=None, ties=False, zero_q=False, clustered=False, dup=0):
     rng = np.random.default_rng(seed)
     q = rnd(rng, (Bn, Hq, D), dtype)
     K = rnd(rng, (Bn, Hkv, T, D), dtype)
@@ -36,6 +36,10 @@ def make_inputs(seed, Bn, Hq, Hkv, D, T, dtype, lens=None, ties=False, zero_q=Fa
     if ties:
         proto = rnd(rng, (7, D), dtype)
         K[:] = proto[rng.integers(0, 7, size=(Bn, Hkv, T))]
+    if dup:
+        # runs of `dup` equal rows: the threshold key is shared by up to `dup` pool slots, fewer
+        # than the lean selection's short list holds, so its tie path ranks them
+        K[:] = K[:, :, (np.arange(T) // dup) * dup]
     if clustered:
         # q.K = a + b / 256 per head with a in 1 + {0..15}/128 and b in 1 + {0..127}/128: 2048
         # distinct scores inside one octave's eighth (two for G = 3), exact in bf16 products and
@@ -242,7 +246,7 @@ REFINE_CASES = [
 
 
 @pytest.mark.parametrize("case", REFINE_CASES, ids=lambda c: f"D{c[0]}G{c[1]}a{c[3]}{c[4]}kp{c[6]}k{c[7]}")
-@pytest.mark.parametrize("variant", ["random", "zero_q", "ties", "clustered"])
+@pytest.mark.parametrize("variant", ["random", "zero_q", "ties", "clustered", "dup"])
 def test_refine_parity(case, variant):
     """'clustered' puts the whole pool in one or two top-12-bit score bins with exact scores, so
     the threshold is resolved from a long candidate list (direct counting up to 512 keys, the
@@ -250,7 +254,8 @@ def test_refine_parity(case, variant):
     D, G, Hkv, agg, dtype, T, kp, kappa, lens = case
     Bn = len(lens) if lens else 1
     q, K, V, lens = make_inputs(seed_of(D, G, T, kp, kappa, variant), Bn, G * Hkv, Hkv, D, T, dtype, lens,
-                                zero_q=variant == "zero_q", ties=variant == "ties", clustered=variant == "clustered")
+                                zero_q=variant == "zero_q", ties=variant == "ties", clustered=variant == "clustered",
+                                dup=37 if variant == "dup" else 0)
     rng = np.random.default_rng(kp + kappa)
     q0 = rnd(rng, q.shape, dtype)
     oKq, osc = oracle.quantize_rows(K)
@@ -260,7 +265,7 @@ def test_refine_parity(case, variant):
                                      kappa, agg, seq_lens=ld)
     torch.cuda.synchronize()
     check_refine_batch(idx.cpu().numpy(), host(out), lse.cpu().numpy(), q, K, V, lens, pool, kappa, agg, dtype,
-                       exact=variant == "clustered")
+                       exact=variant in ("clustered", "dup"))
     if variant == "zero_q":  # every score ties: the lowest pool slots win
         gi = idx.cpu().numpy()
         for b in range(Bn):

@@ -22,7 +22,7 @@ EXPORTS = ("prism_workspace_bytes", "prism_workspace_init", "prism_quantize_keys
            "prism_quantize_keys_int2", "prism_propose_int2", "prism_propose_paged", "prism_refine_attend_paged",
            "prism_refine_attend", "prism_dense_ref", "prism_profile_enable", "prism_profile_query",
            "prism_profile_reset", "prism_last_hip_error", "prism_status_str", "prism_read_probe",
-           "prism_refine_attend_static")
+           "prism_refine_attend_static", "prism_timeline_read", "prism_timeline_clear")
 KERNELS = ("k_quantize_keys", "k_quantize_keys_int2", "k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_dense",
            "k_read_probe")
 
@@ -47,14 +47,17 @@ _lib = None
 _vp = ctypes.c_void_p
 
 
-def load():
-    """Load libprism.so (built by token_level_sparse_prism_amd/build.py); raise if it is absent."""
+def load(path: Optional[str] = None):
+    """Load libprism.so (built by token_level_sparse_prism_amd/build.py), or the library at `path`
+    (the timeline build lib/libprism_tl.so for bench.py --timeline); raise if it is absent.  The
+    first load fixes the library for the process."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"HIP library {LIB_PATH} is not built; run token_level_sparse_prism_amd/build.py")
-    lib = ctypes.CDLL(LIB_PATH)
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run token_level_sparse_prism_amd/build.py")
+    lib = ctypes.CDLL(path)
     sp = ctypes.POINTER(Shape)
     lib.prism_workspace_bytes.argtypes = [ctypes.c_int, sp, ctypes.c_int32, ctypes.c_int32]
     lib.prism_workspace_bytes.restype = ctypes.c_size_t
@@ -75,6 +78,10 @@ def load():
                                         ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.prism_refine_attend_static.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, _vp, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp]
+    lib.prism_timeline_read.argtypes = [ctypes.c_int, _vp, ctypes.c_int64]
+    lib.prism_timeline_read.restype = ctypes.c_int
+    lib.prism_timeline_clear.argtypes = []
+    lib.prism_timeline_clear.restype = ctypes.c_int
     lib.prism_dense_ref.argtypes = [_vp, _vp, _vp, ctypes.c_int, sp, ctypes.c_float, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp]
     for fn in ("prism_workspace_init", "prism_quantize_keys", "prism_propose", "prism_quantize_keys_int2",
@@ -385,3 +392,21 @@ def profile_query(name: str) -> Tuple[int, float]:
     ms = ctypes.c_double(0.0)
     _check("prism_profile_query", load().prism_profile_query(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+TL_KERNELS = ("k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_select", "k_rows")
+TL_PHASES = 8
+
+
+def timeline_clear():
+    _check("prism_timeline_clear", load().prism_timeline_clear())
+
+
+def timeline_read(kernel: str, max_wgs: int):
+    """[max_wgs, 8] uint64 real-time stamps (100 MHz) of a kernel's last launch, 0 = not reached
+    (timeline build only)."""
+    import numpy as np
+    out = np.zeros((max_wgs, TL_PHASES), dtype=np.uint64)
+    _check("prism_timeline_read", load().prism_timeline_read(TL_KERNELS.index(kernel),
+                                                             out.ctypes.data_as(ctypes.c_void_p), max_wgs))
+    return out

@@ -4,6 +4,9 @@ Every .hip file under csrc/ is compiled with hipcc for gfx950 (in parallel), the
 one shared library exporting the C ABI of include/prism.h.
 
 Usage: python -m token_level_sparse_prism_amd.build   (or python token_level_sparse_prism_amd/build.py)
+       python -m token_level_sparse_prism_amd.build --timeline
+           also builds lib/libprism_tl.so: the same sources with PRISM_TIMELINE=1, whose kernels
+           record per-workgroup phase timestamps (a diagnostics build; bench.py --timeline loads it)
 """
 import concurrent.futures as cf
 import glob
@@ -23,33 +26,42 @@ FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-u
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+LIB_TL = os.path.join(LIBDIR, "libprism_tl.so")
+BUILD_TL = os.path.join(PKG, "_build_tl")
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 0, timeline: bool = False) -> str:
+    build_dir, lib = (BUILD_TL, LIB_TL) if timeline else (BUILD, LIB)
+    extra = ("-DPRISM_TIMELINE=1",) if timeline else ()
+    os.makedirs(build_dir, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), srcs))
+    LIBX = lib
+    tmp = LIBX + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, LIBX)
     if verbose:
-        print(f"built {LIB}", flush=True)
-    return LIB
+        print(f"built {LIBX}", flush=True)
+    return LIBX
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    if "--timeline" in sys.argv[1:]:
+        build(verbose=True, timeline=True)
     sys.exit(0)

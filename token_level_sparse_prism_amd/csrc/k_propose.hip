@@ -70,6 +70,7 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
 
     const Dims& d = a.d;
     const int tid = threadIdx.x;
+    PRISM_TL(kTlCand, 0);
     const UnitIdx ui = unit_major();
     const int unit = ui.unit;
     const int cfirst = ui.x * M;
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
         for (int j = 0; j < 16; ++j) h[j] += hr[j];
     }
     find_crossing_regs<16>(h, kHistBins, uint32_t(kp_eff), s_tmp, s_res);
+    PRISM_TL(kTlCand, 1);
     const uint32_t bin = s_res[0];
     if (cfirst == 0 && tid == 0) {
         uint32_t* st = a.state + int64_t(unit) * 8;
@@ -150,6 +152,7 @@ __global__ __launch_bounds__(kThreads) void k_cand(ProposeArgs a) {
             }
         }
     }
+    PRISM_TL(kTlCand, 2);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -167,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
 
     const Dims& d = a.d;
     const int tid = threadIdx.x;
+    PRISM_TL(kTlCompact, 0);
     const UnitIdx ui = unit_major();
     const int unit = ui.unit;
     const int cfirst = ui.x * M;
@@ -222,6 +226,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
     // digit A (bits 19..8) of the threshold
     const uint32_t need_bin = uint32_t(kp_eff) - above;
     find_crossing_regs<16>(h, kHistBins, need_bin, s_tmp, s_res);
+    PRISM_TL(kTlCompact, 1);
     const uint32_t da = s_res[0], above_a = s_res[1];
     const uint32_t pre = (bin << 12) | da;
     // one pass over the candidates: the candidates of chunks before the group above pre (all of
@@ -253,7 +258,9 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
         }
     }
     __syncthreads();
+    PRISM_TL(kTlCompact, 2);
     find_crossing<256>(s_hist, need_bin - above_a, s_tmp, s_res);
+    PRISM_TL(kTlCompact, 3);
     const uint32_t tau = (pre << 8) | s_res[0];
     const uint32_t need = need_bin - above_a - s_res[1];  // keys equal to tau to take, >= 1
 
@@ -317,6 +324,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(ProposeArgs a) {
         gt_run += t[3 + m] & 0xFFFFu;
         eq_run += t[3 + m] >> 16;
     }
+    PRISM_TL(kTlCompact, 4);
 }
 
 hipError_t launch_scan8(const ProposeArgs& a, int agg_max, hipStream_t st);

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "prism_device.hpp"
+#include "prism_prof.hpp"
 
 namespace prism {
 
@@ -249,6 +250,7 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
     const int row0 = wave * RPW;
     float* s_max = s_red;
     float* s_sum = s_red + NW * GP;
+    PRISM_TL(kTlRows, 0);
 
     // this lane's row: its logits (the lane's load is issued first)
     const bool my_valid = lane < RPW && row0 + lane < n;
@@ -267,7 +269,9 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
         raw[u] = LR::load(vrow(s_tok[r < n ? r : 0]) + lane * NE);
     }
 
-    // statistics
+    // statistics, per wave: the wave's own maximum per head (-inf for a wave without rows), so
+    // no barrier stands between a wave's logits and its V accumulation; the cross-wave sum below
+    // rescales each wave's partial to the workgroup maximum
     float y[GP];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
@@ -275,36 +279,25 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
         const float c = (h % 4 == 0) ? v.x : (h % 4 == 1) ? v.y : (h % 4 == 2) ? v.z : v.w;
         y[h] = (my_valid && h < G) ? c * y_scale : -INFINITY;
     }
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-        if (h >= G) break;
-        const float m = wave_max(y[h]);
-        if (lane == 0) s_max[wave * GP + h] = m;
-    }
-    __syncthreads();
-    // every wave's maximum (waves without rows hold -inf), per head: lane l reads wave l % 16 of
-    // head l / 16 of a group of four heads and a row-wide DPP max reduces them
     static_assert(NW == 16, "the wave maxima fill one DPP row per head");
     float p[GP];
 #pragma unroll
-    for (int hb = 0; hb < GP; hb += 4) {
-        const int hq = hb + (lane >> 4);
-        const float m = group_max<16>(hq < G ? s_max[(lane & 15) * GP + hq] : -INFINITY);
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) {
-            const int h = hb + h4;
-            if (h < GP) {
-                const float M = readlane_f32(m, 16 * h4);
-                p[h] = (my_valid && h < G) ? exp2_le0(y[h] - M) : 0.0f;
-            }
+    for (int h = 0; h < GP; ++h) {
+        if (h >= G) {
+            p[h] = 0.0f;
+            continue;
+        }
+        const float m = wave_max(y[h]);
+        p[h] = my_valid ? exp2_le0(y[h] - m) : 0.0f;  // m is finite where a lane holds a row
+        const float l = wave_sum(p[h]);
+        if (lane == 0) {
+            s_max[wave * GP + h] = m;
+            s_sum[wave * GP + h] = l;
         }
     }
-#pragma unroll
-    for (int h = 0; h < GP; ++h) {
-        if (h >= G) break;
-        const float l = wave_sum(p[h]);
-        if (lane == 0) s_sum[wave * GP + h] = l;
-    }
+    PRISM_TL(kTlRows, 1);
+    PRISM_TL(kTlRows, 2);
+    PRISM_TL(kTlAttend, 2);
     if (lane < RPW) {  // the wave's rows' weights; read back below by the same wave only
 #pragma unroll
         for (int h = 0; h < GP; ++h) s_p[(row0 + lane) * GP + h] = p[h];
@@ -341,8 +334,10 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
         }
     }
 
-    // sum of the waves' partials in wave order, HB heads per round; partials are read by another
-    // workgroup of the same kernel, so they are written through to device scope
+    PRISM_TL(kTlRows, 3);
+    // sum of the waves' partials in wave order, each scaled by 2^(wave max - workgroup max), HB
+    // heads per round; partials are read by another workgroup of the same kernel, so they are
+    // written through to device scope
 #pragma unroll
     for (int hb = 0; hb < GP; hb += HB) {
         if (hb >= G) break;
@@ -358,9 +353,13 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
         const int nb = (G - hb < HB ? G - hb : HB) * D;
         for (int i = tid; i < nb; i += NT) {
             const int h = i / D, dd = i % D;
-            float sacc = s_wacc[h * D + dd];
+            float M = -INFINITY;
 #pragma unroll
-            for (int w = 1; w < NW; ++w) sacc += s_wacc[(w * HB + h) * D + dd];
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, s_max[w * GP + hb + h]);  // finite: n >= 1
+            float sacc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                sacc = fmaf(s_wacc[(w * HB + h) * D + dd], exp2_le0(s_max[w * GP + hb + h] - M), sacc);
             st_dev(&g_acc[(hb + h) * AS + dd], sacc);
         }
     }
@@ -368,10 +367,11 @@ __device__ __forceinline__ void softmax_v_rows(VRow vrow, const float* __restric
 #pragma unroll
         for (int hb = 0; hb < GP; hb += 4) {
             const int hq = hb + (lane >> 4);
-            const float m = group_max<16>(hq < G ? s_max[(lane & 15) * GP + hq] : -INFINITY);
-            const float l = group_sum<16>(hq < G ? s_sum[(lane & 15) * GP + hq] : 0.0f);
+            const float mw = hq < G ? s_max[(lane & 15) * GP + hq] : -INFINITY;
+            const float M = group_max<16>(mw);
+            const float l = group_sum<16>(hq < G ? s_sum[(lane & 15) * GP + hq] * exp2_le0(mw - M) : 0.0f);
             if ((lane & 15) == 0 && hq < G) {
-                st_dev(&g_ml[2 * hq], m);
+                st_dev(&g_ml[2 * hq], M);
                 st_dev(&g_ml[2 * hq + 1], l);
             }
         }

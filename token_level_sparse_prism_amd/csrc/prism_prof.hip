@@ -54,9 +54,59 @@ bool prof_pair(const char* name, hipEvent_t* begin, hipEvent_t* end) {
     return true;
 }
 
+#if PRISM_TIMELINE
+namespace {
+struct TlTu {
+    hipError_t (*copy)(unsigned long long*, size_t);
+    hipError_t (*clear)();
+};
+std::vector<TlTu>& tl_tus() {
+    static std::vector<TlTu> v;
+    return v;
+}
+}  // namespace
+void tl_register(hipError_t (*copy)(unsigned long long*, size_t), hipError_t (*clear)()) {
+    tl_tus().push_back({copy, clear});
+}
+#endif
+
 }  // namespace prism
 
 extern "C" {
+
+prism_status prism_timeline_read(int kernel, unsigned long long* out, int64_t max_wgs) {
+#if PRISM_TIMELINE
+    if (kernel < 0 || kernel >= prism::kTlKernels || !out || max_wgs < 1) return PRISM_ERR_INVALID_ARG;
+    const size_t n = size_t(prism::kTlKernels) * prism::kTlWgs * prism::kTlPhases;
+    std::vector<unsigned long long> buf(n);
+    const int64_t wgs = max_wgs < prism::kTlWgs ? max_wgs : prism::kTlWgs;
+    const size_t off = size_t(kernel) * prism::kTlWgs * prism::kTlPhases;
+    for (size_t i = 0; i < size_t(wgs) * prism::kTlPhases; ++i) out[i] = 0ull;
+    if (hipDeviceSynchronize() != hipSuccess) return PRISM_ERR_HIP;
+    for (const auto& tu : prism::tl_tus()) {
+        if (tu.copy(buf.data(), n) != hipSuccess) return PRISM_ERR_HIP;
+        for (size_t i = 0; i < size_t(wgs) * prism::kTlPhases; ++i)
+            if (buf[off + i] > out[i]) out[i] = buf[off + i];
+    }
+    return PRISM_OK;
+#else
+    (void)kernel;
+    (void)out;
+    (void)max_wgs;
+    return PRISM_ERR_UNSUPPORTED;
+#endif
+}
+
+prism_status prism_timeline_clear(void) {
+#if PRISM_TIMELINE
+    if (hipDeviceSynchronize() != hipSuccess) return PRISM_ERR_HIP;
+    for (const auto& tu : prism::tl_tus())
+        if (tu.clear() != hipSuccess) return PRISM_ERR_HIP;
+    return PRISM_OK;
+#else
+    return PRISM_ERR_UNSUPPORTED;
+#endif
+}
 
 prism_status prism_profile_enable(int on) {
     prism::g_on.store(on != 0);

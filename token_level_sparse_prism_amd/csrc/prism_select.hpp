@@ -12,9 +12,17 @@
 //   4. Selected slots are ranked in slot order, ties at tau going to the lower slot, with
 //      workgroup scans; ranks [r0, r0 + n) land in LDS with their token ids.
 // Keys are read in tiles of 8192 slots, two slots per thread and row (one 16-byte load).
+// Pools of one tile take select_ranks_lean (below), which builds the level-2 histogram straight
+// from the registers and ranks with one packed scan; the general path above serves larger pools
+// and thresholds with heavy ties.
 #pragma once
 
 #include "prism_device.hpp"
+#include "prism_prof.hpp"
+
+#ifndef PRISM_SELECT_LEAN
+#define PRISM_SELECT_LEAN 1  // single-tile pools take the lean selection path
+#endif
 
 namespace prism {
 
@@ -116,9 +124,223 @@ __device__ __forceinline__ void sel_digit_hist(const uint2* __restrict__ gk, int
     }
 }
 
+// Exclusive prefix sum over the workgroup in thread order with one barrier: s_w (NT/64 words)
+// must not be touched by other code between the caller's previous barrier and its next one.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan1(uint32_t v, uint32_t* s_w, uint32_t* total) {
+    const uint32_t x = wave_incl_scan(v);
+    if (lane_id() == 63) s_w[wave_id()] = x;
+    __syncthreads();
+    uint32_t before, tot;
+    wave_totals_prefix<NT / 64>(s_w, &before, &tot);
+    *total = tot;
+    return before + x - v;
+}
+
+constexpr int kLeanShort = 256;  // keys sharing the threshold's top 20 bits that the lean path ranks directly
+
+// N exclusive prefix sums over the workgroup in thread order with one barrier (s_w: N * NT/64
+// words, not touched by other code between the caller's previous barrier and its next one).
+template <int N, int NT>
+__device__ __forceinline__ void block_excl_scan1_n(const uint32_t* v, uint32_t* pre, uint32_t* tot, uint32_t* s_w) {
+    constexpr int NW = NT / 64;
+    uint32_t x[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = wave_incl_scan(v[i]);
+    if (lane_id() == 63) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) s_w[i * NW + wave_id()] = x[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        uint32_t before;
+        wave_totals_prefix<NW>(s_w + i * NW, &before, &tot[i]);
+        pre[i] = before + x[i] - v[i];
+    }
+}
+
+// Single-tile selection (kp <= kSelTile, NT * 8 == kSelTile).  Thread t holds slots
+// 2 NT r + 2 t + e (rows r < 4, e < 2) in registers for the whole selection, loaded as one
+// coalesced 16-byte {key, id} pair per row.
+//   1. level-1 histogram of the keys' top 12 bits (LDS atomics), a one-barrier workgroup scan in
+//      descending bin order: the bin of the kappa-th largest key;
+//   2. level-2 histogram of bits 19..12 over that bin's keys, straight from the registers, and
+//      one wave's crossing over its 256 bins;
+//   3. the keys sharing those top 20 bits (typically a few) go to a short LDS list, where each
+//      finds its rank among them by direct counting: the exact threshold tau, how many keys equal
+//      to tau are taken and how many there are;
+//   4. one workgroup scan of the per-row counts (keys taken, and keys equal to tau when only some
+//      are taken), packed two rows to a word, gives every selected slot its rank in slot order,
+//      ties at tau to the lower slot.
+// Returns false, after a barrier and with nothing written but LDS scratch, when more than
+// kLeanShort keys share the threshold's top 20 bits (heavy ties); select_ranks then takes its
+// general path.
+template <int NT>
+__device__ __forceinline__ bool select_ranks_lean(const uint2* __restrict__ gk, int64_t kp, uint32_t kappa, int r0,
+                                                  int nmax, uint32_t* s_hist, uint32_t* s_tmp, uint32_t* s_res,
+                                                  uint32_t* s_short, int32_t* s_slot, int32_t* s_tok,
+                                                  SelResult* out) {
+    constexpr int ROWS = sel_rows<NT>();
+    static_assert(ROWS == 4 && NT * 4 == kHistBins, "4 rows of 2 slots and 4 level-1 bins per thread");
+    static_assert(4 * (NT / 64) <= sel_tmp_words<NT>(), "the rank scan's words fit s_tmp");
+    const int tid = threadIdx.x, wave = wave_id();
+    PRISM_TL(kTlSelect, 0);
+    uint4 kv[ROWS];
+    sel_load_tile<NT>(gk, kp, 0, kv);
+    for (int i = tid; i < kSelHistWords / 4; i += NT) reinterpret_cast<uint4*>(s_hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        if (kv[r].x) atomicAdd(&s_hist[kv[r].x >> kKeyShift], 1u);
+        if (kv[r].z) atomicAdd(&s_hist[kv[r].z >> kKeyShift], 1u);
+    }
+    __syncthreads();
+    PRISM_TL(kTlSelect, 1);
+
+    // level-1 crossing: thread t holds bins 4095 - 4t - k (k < 4)
+    uint32_t kap;
+    {
+        const uint4 x = *reinterpret_cast<const uint4*>(s_hist + (kHistBins - 4 * (tid + 1)));
+        const uint32_t c[4] = {x.w, x.z, x.y, x.x};
+        const uint32_t sum = (c[0] + c[1]) + (c[2] + c[3]);
+        uint32_t total;
+        uint32_t acc = block_excl_scan1<NT>(sum, s_tmp, &total);
+        kap = kappa < total ? kappa : total;
+        if (tid == 0) {
+            s_res[kResValid] = total;
+            s_res[kResC2] = 0u;
+        }
+        if (kap > 0u && kap < total && acc < kap && kap <= acc + sum) {  // exactly one thread
+            bool f = false;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool hit = !f && acc + c[k] >= kap;
+                if (hit) {
+                    s_res[kResBin] = uint32_t(kHistBins - 1 - 4 * tid - k);
+                    s_res[kResAbove] = acc;
+                }
+                f = f || hit;
+                acc += f ? 0u : c[k];
+            }
+        }
+    }
+    __syncthreads();
+    PRISM_TL(kTlSelect, 2);
+    const uint32_t n_valid = s_res[kResValid];
+    out->kappa_eff = kap;
+    out->n = 0;
+    if (kap == 0) return true;
+
+    uint32_t tau = 1u, need = 0xFFFFFFFFu, eq_total = 0u;  // default: every valid key is taken
+    if (kap < n_valid) {
+        const uint32_t bin = s_res[kResBin];
+        const uint32_t R = kap - s_res[kResAbove];  // rank of tau inside the bin: 1 <= R <= its count
+        uint32_t* s_h2 = s_hist + kHist1Words;      // zeroed with the level-1 histogram
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            if (kv[r].x && (kv[r].x >> kKeyShift) == bin) atomicAdd(&s_h2[(kv[r].x >> 12) & 0xFFu], 1u);
+            if (kv[r].z && (kv[r].z >> kKeyShift) == bin) atomicAdd(&s_h2[(kv[r].z >> 12) & 0xFFu], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) sel_sub_crossing(s_h2, R, s_res);
+        __syncthreads();
+        PRISM_TL(kTlSelect, 3);
+        const uint32_t bin2 = s_res[kResBin2];
+        const uint32_t c2 = s_h2[bin2];
+        if (c2 > uint32_t(kLeanShort)) {  // the same for every thread
+            __syncthreads();              // every thread has read the LDS above before it is reused
+            return false;
+        }
+        const uint32_t pre = (bin << 8) | bin2;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            if (kv[r].x && (kv[r].x >> 12) == pre) s_short[atomicAdd(&s_res[kResC2], 1u)] = kv[r].x;
+            if (kv[r].z && (kv[r].z >> 12) == pre) s_short[atomicAdd(&s_res[kResC2], 1u)] = kv[r].z;
+        }
+        __syncthreads();
+        const uint32_t R2 = R - s_res[kResAbove2];
+        if (uint32_t(tid) < c2) {
+            const uint32_t k = s_short[tid];
+            uint32_t gt = 0, ge = 0;
+            for (uint32_t j = 0; j < c2; ++j) {
+                const uint32_t x = s_short[j];
+                gt += x > k ? 1u : 0u;
+                ge += x >= k ? 1u : 0u;
+            }
+            if (gt < R2 && R2 <= ge) {  // every holder of tau writes the same three words
+                s_res[kResTau] = k;
+                s_res[kResNeed] = R2 - gt;
+                s_res[kResEq] = ge - gt;
+            }
+        }
+        __syncthreads();
+        tau = s_res[kResTau];
+        need = s_res[kResNeed];
+        eq_total = s_res[kResEq];
+    }
+    PRISM_TL(kTlSelect, 4);
+
+    // ranks in slot order (row-major over the tile): per thread and row the keys taken (above
+    // tau, or at least tau when every key equal to tau is taken) and, when only some ties are
+    // taken, the keys equal to tau; two rows per 16-bit-packed word, one workgroup scan
+    const bool take_all_eq = need >= eq_total;
+    uint32_t v[4], pre[4], tot[4];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        uint32_t sel = 0, eq = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 k = kv[2 * p + h];
+            const uint32_t gt = (k.x > tau ? 1u : 0u) + (k.z > tau ? 1u : 0u);
+            const uint32_t e = (k.x == tau ? 1u : 0u) + (k.z == tau ? 1u : 0u);
+            sel += (take_all_eq ? gt + e : gt) << (16 * h);
+            eq += e << (16 * h);
+        }
+        v[p] = sel;
+        v[2 + p] = eq;
+    }
+    // s_tmp's words from the crossing scan were last read before the barriers above
+    if (take_all_eq) {
+        block_excl_scan1_n<2, NT>(v, pre, tot, s_tmp);
+    } else {
+        block_excl_scan1_n<4, NT>(v, pre, tot, s_tmp);
+    }
+    const int n = int(kap) - r0 <= 0 ? 0 : (int(kap) - r0 > nmax ? nmax : int(kap) - r0);
+    uint32_t rows_sel = 0, rows_eq = 0;  // taken keys and ties of the rows before
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const int p = r / 2, sh = 16 * (r % 2);
+        const uint32_t sel_before = rows_sel + ((pre[p] >> sh) & 0xFFFFu);
+        uint32_t eqi = take_all_eq ? 0u : rows_eq + ((pre[2 + p] >> sh) & 0xFFFFu);
+        uint32_t rank = sel_before + (take_all_eq ? 0u : (eqi < need ? eqi : need));
+        const uint32_t k2[2] = {kv[r].x, kv[r].z};
+        const int32_t t2[2] = {int32_t(kv[r].y), int32_t(kv[r].w)};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const bool eqk = k2[e] == tau;
+            const bool take = k2[e] > tau || (eqk && (take_all_eq || eqi < need));
+            eqi += eqk ? 1u : 0u;
+            const uint32_t off = rank - uint32_t(r0);  // wraps for ranks below r0
+            if (take && off < uint32_t(n)) {
+                s_slot[off] = r * 2 * NT + tid * 2 + e;
+                s_tok[off] = t2[e];
+            }
+            rank += take ? 1u : 0u;
+        }
+        rows_sel += (tot[p] >> sh) & 0xFFFFu;
+        if (!take_all_eq) rows_eq += (tot[2 + p] >> sh) & 0xFFFFu;
+    }
+    __syncthreads();
+    PRISM_TL(kTlSelect, 5);
+    out->n = n;
+    return true;
+}
+
 // gk: the unit's [kp] {key, id} slots (16-byte aligned); ids pass through to s_tok.
 // LDS: s_hist kSelHistWords words, 16-byte aligned; s_tmp sel_tmp_words<NT>() words; s_res 16 words;
 // s_cand kSelCandTotal words (16-byte aligned), s_ccount NT/64 words, s_slot / s_tok nmax each.
+// A pool of at most kSelTile slots takes select_ranks_lean unless its threshold has heavy ties.
 template <int NT>
 __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, int64_t kp, uint32_t kappa, int r0, int nmax, uint32_t* s_hist,
                                                   uint32_t* s_tmp, uint32_t* s_res, uint32_t* s_cand,
@@ -128,9 +350,17 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
     constexpr int CPW = sel_cand_per_wave<NT>();
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int ntiles = int((kp + kSelTile - 1) / kSelTile);
+    if constexpr (NT * 8 == kSelTile && PRISM_SELECT_LEAN) {
+        if (kp <= kSelTile) {
+            SelResult r;
+            if (select_ranks_lean<NT>(gk, kp, kappa, r0, nmax, s_hist, s_tmp, s_res, s_cand, s_slot, s_tok, &r))
+                return r;
+        }
+    }
     uint4 kv[ROWS];
 
     // ---- level-1 histogram (the LDS is cleared while the first keys are in flight) ----
+    PRISM_TL(kTlSelect, 0);
     sel_load_tile<NT>(gk, kp, 0, kv);
     for (int i = tid; i < kSelHistWords / 4; i += NT) reinterpret_cast<uint4*>(s_hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
@@ -143,6 +373,7 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
         }
     }
     __syncthreads();
+    PRISM_TL(kTlSelect, 1);
     // ---- crossing: thread t holds bins 4095 - 4t - k (k < 4), one 16-byte LDS read ----
     {
         static_assert(NT * 4 == kHistBins, "four bins per thread");
@@ -175,6 +406,7 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
     }
     if (ntiles > 1) sel_load_tile<NT>(gk, kp, 0, kv);
     __syncthreads();
+    PRISM_TL(kTlSelect, 2);
     const uint32_t n_valid = s_res[kResValid];
     const uint32_t kappa_eff = s_res[kResKappa];
     SelResult res{kappa_eff, 0};
@@ -203,6 +435,7 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
         if (lane == 0) s_ccount[wave] = cnt;
         if (lane == 0 && cnt > uint32_t(CPW)) s_res[kResOvf] = 1u;
         __syncthreads();
+        PRISM_TL(kTlSelect, 3);
         const bool overflow = s_res[kResOvf] != 0u;
         const uint32_t R = kappa_eff - above;  // rank of tau inside the bin, 1 <= R <= count of the bin
         if (!overflow) {
@@ -270,6 +503,7 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
             }
             __syncthreads();
         }
+        PRISM_TL(kTlSelect, 4);
         tau = s_res[kResTau];
         need = s_res[kResNeed];
         eq_total = s_res[kResEq];
@@ -327,6 +561,7 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
             }
             __syncthreads();  // s_tmp is rewritten by the next tile
         }
+        PRISM_TL(kTlSelect, 5);
         return res;
     }
     // per-row counts of one thread are at most 2, two rows share a 32-bit word (16 bits each)

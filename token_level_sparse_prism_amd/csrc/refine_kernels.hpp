@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kRscoreThreads) void k_rscore_mfma(RefineArgs a) {
     constexpr int SLOTS = 16 * (kRscoreThreads / 64);
     const Dims& d = a.d;
     const int lane = lane_id(), wave = wave_id();
+    PRISM_TL(kTlRscore, 0);
     zero_ctrl(a, kRscoreThreads);
     const UnitIdx ui = unit_major();
     const int unit = ui.unit;
@@ -193,6 +194,7 @@ __global__ __launch_bounds__(kRscoreThreads) void k_rscore_mfma(RefineArgs a) {
             a.skey[int64_t(unit) * a.kstride + j] = make_uint2(key, valid ? id : 0xFFFFFFFFu);
         }
     }
+    PRISM_TL(kTlRscore, 1);
 }
 
 template <typename T, int D, int GP, int NR, int DS = 1>
@@ -223,10 +225,12 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     const int G = d.G;
     const int64_t kp = a.kp;
     const int r0 = slice * NR;
+    PRISM_TL(kTlAttend, 0);
 
     const SelResult sr = select_ranks<NT>(a.skey + int64_t(unit) * a.kstride, kp, uint32_t(a.kappa), r0, NR, s_big,
                                           s_tmp, s_res, s_cand, s_ccount, s_slot, s_tok);
     const int n = sr.n;
+    PRISM_TL(kTlAttend, 1);
 
     // ---- the slice's softmax(.)V partial, then idx.  s_tok holds the selected slots' record ids:
     // token ids, or with paged caches the row inside the KV head's pool (pool scoring found it) ----
@@ -246,6 +250,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
         if (tid < n) t = paged ? a.pool[int64_t(unit) * kp + s_slot[tid]] : s_tok[tid];
         a.idx[int64_t(unit) * a.kappa + r0 + tid] = t;
     }
+    PRISM_TL(kTlAttend, 3);
 
     const int np = int((sr.kappa_eff + NR - 1) / NR);  // slices that wrote a partial
     const int64_t hq0 = int64_t(b) * d.Hq + int64_t(g) * G;
@@ -254,8 +259,10 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(RefineArgs a) {
     uint32_t* done = &a.done_a[int64_t(unit) * kCtrStride + half];  // one counter per column range
     if (nsa <= kMergeGroup) {  // one level: the last slice merges every partial
         if (!arrive_last(done, nsa, &s_flag)) return;
+        PRISM_TL(kTlAttend, 4);
         merge_partials<T, DH, GP, NT, false, D>(part_ml, part_acc + half * DH, np, G, out, lse);
         if (tid == 0) *done = 0u;
+        PRISM_TL(kTlAttend, 5);
         return;
     }
     // two levels: the last slice of each group of kMergeGroup merges the group's partials into a
@@ -368,10 +375,12 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     const int G = d.G;
     const int64_t kp = a.kp;
 
+    PRISM_TL(kTlAttend, 0);
     const SelResult sr = select_ranks<NT>(a.skey + int64_t(unit) * a.kstride, kp, uint32_t(a.kappa), 0, KM, s_big,
                                           s_tmp, s_res, s_cand, s_ccount, s_slot, s_tok);
     const int n = sr.n;
     const bool paged = d.pg.table != nullptr;
+    PRISM_TL(kTlAttend, 1);
 
     // idx: piece p writes ranks [p * per, (p + 1) * per); ranks at or beyond n hold -1
     {
@@ -425,7 +434,9 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
         m = wave_max(m);
         if (lane == 0) s_max[wave * GP + h] = m;
     }
+    PRISM_TL(kTlAttend, 2);
     __syncthreads();
+    PRISM_TL(kTlAttend, 3);
     // the block maximum per head: lane l reads wave l % 16 of head l / 16, a row-wide DPP max
     static_assert(NW == 16, "the wave maxima fill one DPP row per head");
     float M[GP];
@@ -455,6 +466,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
         l = wave_sum(l);
         if (lane == 0) s_sum[wave * GP + h] = l;
     }
+    PRISM_TL(kTlAttend, 4);
     wave_reduce_scatter<NV>(acc);
     {
         constexpr int S = NV >= 16 ? 4 : NV == 8 ? 3 : 2;
@@ -484,6 +496,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
             }
         }
     }
+    PRISM_TL(kTlAttend, 5);
 }
 
 // Compute units of the current device (cached per device).

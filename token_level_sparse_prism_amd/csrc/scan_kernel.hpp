@@ -375,6 +375,7 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
     const int nch = int((d.T_max + CHW - 1) / CHW);
     const int sub = lane % LPT;
     const int tl = lane / LPT;             // the lane's token inside a wave-load
+    PRISM_TL(kTlScan, 0);
 
     // Every global load below is unconditional, at a clamped in-bounds address, and loads past
     // the work item's tokens are simply not used: a load under a branch makes the compiler merge
@@ -551,6 +552,7 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
             }
         }
     };
+    PRISM_TL(kTlScan, 1);
     for (;;) {  // work items of this workgroup; the rows of its first batch per wave are in flight
         if (nvalid == 0) break;  // later work items are past T_b too
         nb = __builtin_amdgcn_readfirstlane(nb);
@@ -591,11 +593,13 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) kv[u] = load_item(bcur * U + u);
     }
+    PRISM_TL(kTlScan, 2);
     uint32_t* gh = a.hist1 + (int64_t(unit) * a.hist_rep + ui.x % a.hist_rep) * kHistBins;
     for (int i = tid; i < kHistBins; i += NT) {
         const uint32_t c = s_hist[i];
         if (c) atomicAdd(&gh[i], c);
     }
+    PRISM_TL(kTlScan, 3);
 }
 
 // ---------------------------------------------------------------------------------------------
