@@ -57,6 +57,10 @@ def parse():
                         "launch gaps and per-phase medians over the workgroups")
     p.add_argument("--lib", default="", help="load this build of the library instead of lib/libprism.so "
                                              "(or lib/libprism_tl.so with --timeline)")
+    p.add_argument("--figures", action="store_true",
+                   help="cross-layer study on the 262144-token stress shapes with 1 + 7 layers instead of the "
+                        "benchmark: index overlap against layer offset (Figure 1 analog) and each refined layer's "
+                        "top-128 bucketed by its rank at the anchor (Figure 2 analog); one JSON line per D")
     p.add_argument("--recall", action="store_true",
                    help="quality readout on the 262144-token stress workloads instead of the benchmark: "
                         "salient, attention-mass and exact top-kappa recall of Prism (kp = rho*kappa) "
@@ -259,12 +263,104 @@ def timeline_readout(args, cfg, steps, R):
     return 0
 
 
+def figures_readout():
+    """Cross-layer study on controlled data (the Prism page's Figure 1 and Figure 2 measurements,
+    re-made on the synthetic generator).  Shape: one KV head with 8 query heads, T = 262144, the
+    anchor (layer 0) and 7 refined layers, 16 planted tokens per layer, 20% of them shifted by up
+    to +-64 positions in each refined layer and given anchor keys at the normal-quantile score of
+    ranks in [128, 384); N(0,1) keys (where that placement is exact) and the stress shape's
+    Student-t keys (heavier tails push those targets to lower ranks), D = 64 and 256.  Every top-k below is the library's exact selection over the whole context
+    (refine_attend with the full context as the pool, SUM of the 8 heads' logits as the score),
+    and every softmax mass comes from its lse against dense_ref's full-context lse.
+      Figure 1 analog, per offset d = 1..7, averaged over the layer pairs (l, l + d):
+        overlap      |top128(l) & top128(l+d)| / 128           (static reuse of layer l's indices)
+        cover_rho2   |top256(l) & top128(l+d)| / 128           (layer l's pool expanded 2x)
+        cover_rho4   |top512(l) & top128(l+d)| / 128           (expanded 4x)
+        and the same three for the planted tokens of layer l + d that its top-128 holds.
+      Figure 2 analog, per refined layer l = 1..7 (reference: the anchor's exact ranks), the share
+      of layer l's top-128 indices, and of the softmax mass they carry, whose anchor rank is
+        < 128, in [128, 512), or >= 512."""
+    import numpy as np
+    import torch
+
+    from token_level_sparse_prism_amd import binding as PB
+    from token_level_sparse_prism_amd import workload as W
+
+    PB.load()
+    k = 128
+    for key_dist, D in (("normal", 64), ("normal", 256), ("student_t3", 64), ("student_t3", 256)):
+        cfg = W.CONFIGS[f"cfg5_D{D}_k512_r1"].with_(name=f"cross-layer D={D} keys={key_dist}", n_refined=7, kappa=k,
+                                                    kp=k, n_salient=16, anchor_v=True, key_dist=key_dist)
+        w = W.generate(cfg)
+        dev = lambda x: torch.from_numpy(x).to(device="cuda", dtype=torch.bfloat16)
+        lens = torch.from_numpy(w.seq_lens).cuda()
+        L = w.layers
+        layers = [(dev(w.q[l]), dev(w.K[l]), dev(w.V[l])) for l in range(L)]
+        full = torch.arange(cfg.T, dtype=torch.int32, device="cuda").view(1, 1, cfg.T)
+        lse_full = [PB.dense_ref(q, K, V, seq_lens=lens)[1] for q, K, V in layers]
+
+        def top(l, n):
+            q, K, V = layers[l]
+            idx = PB.refine_attend(q, K, V, full, n, seq_lens=lens)[1]
+            return set(idx.cpu().numpy().ravel().tolist()) - {-1}
+
+        def mass(l, toks):
+            """Softmax mass of layer l (mean over its 8 heads) on a token set."""
+            if not toks:
+                return 0.0
+            q, K, V = layers[l]
+            pool = torch.tensor(sorted(toks), dtype=torch.int32, device="cuda").view(1, 1, -1)
+            lse = PB.refine_attend(q, K, V, pool, len(toks), seq_lens=lens)[2]
+            return float(torch.exp(lse - lse_full[l]).mean())
+
+        t128 = [top(l, k) for l in range(L)]
+        t256 = [top(l, 2 * k) for l in range(L)]
+        t512 = [top(l, 4 * k) for l in range(L)]
+        sal = [set(w.salient[(0, 0)][0].tolist())] + [set(x.tolist()) for x in w.salient[(0, 0)][1]]
+        fig1 = []
+        for d in range(1, L):
+            rows = []
+            for l in range(0, L - d):
+                tgt = t128[l + d]
+                st = tgt & sal[l + d]
+                rows.append([len(t128[l] & tgt) / k, len(t256[l] & tgt) / k, len(t512[l] & tgt) / k,
+                             len(t128[l] & st) / max(1, len(st)), len(t256[l] & st) / max(1, len(st)),
+                             len(t512[l] & st) / max(1, len(st))])
+            m = np.mean(rows, axis=0)
+            fig1.append({"offset": d, "pairs": len(rows), "overlap": round(float(m[0]), 4),
+                         "cover_rho2": round(float(m[1]), 4), "cover_rho4": round(float(m[2]), 4),
+                         "planted_overlap": round(float(m[3]), 4), "planted_cover_rho2": round(float(m[4]), 4),
+                         "planted_cover_rho4": round(float(m[5]), 4)})
+        fig2 = []
+        a128, a512 = t128[0], t512[0]
+        for l in range(1, L):
+            tgt = t128[l]
+            b = [tgt & a128, (tgt & a512) - a128, tgt - a512]
+            ms = [mass(l, x) for x in b]
+            mt = mass(l, tgt)
+            fig2.append({"layer": l, "index_share": [round(len(x) / k, 4) for x in b],
+                         "mass_share": [round(x / mt, 4) if mt > 0 else 0.0 for x in ms],
+                         "top128_mass": round(mt, 4)})
+        idx_mean = np.mean([r["index_share"] for r in fig2], axis=0)
+        mass_mean = np.mean([r["mass_share"] for r in fig2], axis=0)
+        print(json.dumps({"study": cfg.name, "T": cfg.T, "D": D, "keys": key_dist, "G": cfg.G, "layers": L, "k": k,
+                          "figure1_overlap_vs_offset": fig1, "figure2_anchor_rank_buckets": fig2,
+                          "figure2_mean": {"buckets": ["<128", "128-511", ">=512"],
+                                           "index_share": [round(float(x), 4) for x in idx_mean],
+                                           "mass_share": [round(float(x), 4) for x in mass_mean]}}), flush=True)
+        del layers, w
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main():
     args = parse()
     if args.ingest_pmc:
         return ingest_pmc(args)
     if args.recall:
         return recall_readout()
+    if args.figures:
+        return figures_readout()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the hot path needs no exchange between GPUs "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
