@@ -22,7 +22,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attn steps/s + achieved HBM GB/s at 128K ctx, proposal+3 refined layers"
 PEAK_HBM_GBPS = 8000.0
-PMC_FILE = os.path.join(ROOT, "profiles", "k_scan_128k_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "prism_step_128k_pmc.json")
 CALIB_BYTES = 1 << 30  # the copy read and written by the counter pass's calibration kernel
 
 
@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="time stream launches only (no HIP graph replay)")
+    p.add_argument("--no-anchor", action="store_true",
+                   help="skip the step variant with the anchor layer's own attention")
     p.add_argument("--no-int2", action="store_true",
                    help="skip the second measurement of the same step with INT2 proposal keys")
     p.add_argument("--page-size", type=int, default=64,
@@ -55,6 +57,8 @@ def parse():
                         "layer through the timeline build (lib/libprism_tl.so, built by "
                         "`python -m token_level_sparse_prism_amd.build --timeline`); prints per-kernel spans, "
                         "launch gaps and per-phase medians over the workgroups")
+    p.add_argument("--key-bits", type=int, default=8, choices=(8, 2),
+                   help="proposal key format of the --timeline passes (8: int8 codes, 2: INT2 codes)")
     p.add_argument("--lib", default="", help="load this build of the library instead of lib/libprism.so "
                                              "(or lib/libprism_tl.so with --timeline)")
     p.add_argument("--figures", action="store_true",
@@ -68,12 +72,21 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash():
+def kernel_source_hash(names=("scan_kernel.hpp", "k_scan8.hip", "prism_device.hpp", "prism_internal.hpp")):
     h = hashlib.sha256()
-    for name in ("scan_kernel.hpp", "k_scan8.hip", "prism_device.hpp", "prism_internal.hpp"):
+    for name in names:
         with open(os.path.join(ROOT, "token_level_sparse_prism_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def all_sources_hash():
+    """Hash of every kernel source: the per-step counter bytes are void after any change."""
+    d = os.path.join(ROOT, "token_level_sparse_prism_amd", "csrc")
+    return kernel_source_hash(tuple(sorted(f for f in os.listdir(d) if f.endswith((".hip", ".hpp")))))
+
+
+STEP_KERNELS = ("k_scan", "k_cand", "k_compact", "k_rscore", "k_attend")
 
 
 def _counter_rows(d):
@@ -102,25 +115,54 @@ def _per_dispatch(rows, counter):
     return out
 
 
+_KERNEL_ALIASES = {"k_scan": "k_scan", "k_scan_w": "k_scan", "k_cand": "k_cand", "k_compact": "k_compact",
+                   "k_rscore": "k_rscore", "k_rscore_mfma": "k_rscore", "k_attend": "k_attend",
+                   "k_attend_d": "k_attend"}
+
+
+def _kernel_of(name):
+    """The step kernel a dispatch belongs to (by its function name, e.g. "void prism::k_scan_w<...>(...)"),
+    or None."""
+    import re
+    m = re.search(r"(?:^|[^A-Za-z0-9_])(k_[a-z_0-9]+)\s*[<(]", name)
+    return _KERNEL_ALIASES.get(m.group(1)) if m else None
+
+
 def ingest_pmc(args):
-    """HBM traffic of the scan kernel per launch, from FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
-    scaled by what the same counters read for the calibration copy of CALIB_BYTES."""
-    res = {"workload": args.config, "source_hash": kernel_source_hash(), "calib_bytes": CALIB_BYTES,
-           "commands": {"FETCH_SIZE": args.pmc_command[0], "WRITE_SIZE": args.pmc_command[1]}}
+    """HBM traffic per launch of every kernel of the step, from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by what the same counters read for the calibration copy of CALIB_BYTES; the
+    scan kernel's figure is the bench line's roofline.traffic, the per-step sum (scan, candidates,
+    compaction, and per refined layer pool scoring and attention) its step_roofline.traffic."""
+    from token_level_sparse_prism_amd import workload as W
+    cfg = W.CONFIGS[args.config]
+    res = {"workload": args.config, "source_hash": kernel_source_hash(), "all_sources_hash": all_sources_hash(),
+           "calib_bytes": CALIB_BYTES, "commands": {"FETCH_SIZE": args.pmc_command[0], "WRITE_SIZE": args.pmc_command[1]},
+           "kernels": {}}
     total = 0.0
+    per_kernel = {k: 0.0 for k in STEP_KERNELS}
     for counter, d in (("FETCH_SIZE", args.ingest_pmc[0]), ("WRITE_SIZE", args.ingest_pmc[1])):
         disp = _per_dispatch(_counter_rows(d), counter)
-        scan = [v for n, v in disp.values() if "k_scan" in n]
         calib = [v for n, v in disp.values() if "neg_kernel" in n]
-        if not scan or len(calib) != 1:
-            raise SystemExit(f"{counter}: {len(scan)} scan dispatches, {len(calib)} calibration dispatches")
-        kib = sum(scan) / len(scan)
+        if len(calib) != 1:
+            raise SystemExit(f"{counter}: {len(calib)} calibration dispatches")
         factor = CALIB_BYTES / (calib[0] * 1024.0)
-        bytes_ = kib * 1024.0 * factor
-        res[counter] = {"kib_per_launch": round(kib, 1), "launches": len(scan),
-                        "calib_kib": round(calib[0], 1), "scale": round(factor, 5),
-                        "bytes_per_launch": int(bytes_)}
-        total += bytes_
+        for k in STEP_KERNELS:
+            vals = [v for n, v in disp.values() if _kernel_of(n) == k]
+            if not vals:
+                raise SystemExit(f"{counter}: no {k} dispatches")
+            kib = sum(vals) / len(vals)
+            entry = res["kernels"].setdefault(k, {})
+            entry[counter] = {"kib_per_launch": round(kib, 1), "launches": len(vals),
+                              "bytes_per_launch": int(kib * 1024.0 * factor)}
+            per_kernel[k] += kib * 1024.0 * factor
+        res[counter] = {"calib_kib": round(calib[0], 1), "scale": round(factor, 5),
+                        "bytes_per_launch": res["kernels"]["k_scan"][counter]["bytes_per_launch"]}
+        total += res["kernels"]["k_scan"][counter]["bytes_per_launch"]
+    for k in STEP_KERNELS:
+        res["kernels"][k]["traffic_bytes_per_launch"] = int(per_kernel[k])
+    per_step = {"k_scan": 1, "k_cand": 1, "k_compact": 1, "k_rscore": cfg.n_refined, "k_attend": cfg.n_refined}
+    res["launches_per_step"] = per_step
+    res["traffic_bytes_per_step"] = int(sum(per_kernel[k] * per_step[k] for k in STEP_KERNELS))
     res["traffic_bytes_per_launch"] = int(total)
     with open(PMC_FILE, "w") as f:
         json.dump(res, f, indent=1)
@@ -187,7 +229,7 @@ def recall_readout():
 
 
 TL_PHASE_NAMES = {
-    "k_scan": ["prologue", "stream", "flush"],
+    "k_scan": ["query load", "barrier", "codes", "stream", "flush"],
     "k_cand": ["threshold bin", "candidates"],
     "k_compact": ["digit A", "candidate pass", "last byte", "pool write"],
     "k_rscore": ["score"],
@@ -254,7 +296,8 @@ def timeline_readout(args, cfg, steps, R):
         torch.cuda.synchronize()
         recs.append({k: PB.timeline_read(k, 8192) for k in kernels})
     summ = timeline_summary(recs, kernels)
-    print(json.dumps({"timeline": cfg.name, "passes": args.timeline, "kernels": summ}), flush=True)
+    print(json.dumps({"timeline": cfg.name, "key_bits": args.key_bits, "passes": args.timeline, "kernels": summ}),
+          flush=True)
     for k, v in summ.items():
         ph = ", ".join(f"{n} {x['median']:.2f} (p90 {x['p90']:.2f}, {x['workgroups']} wg)"
                        for n, x in v["phases_us"].items())
@@ -391,7 +434,7 @@ def main():
     layerwise = host_bytes > 24e9
     t0 = time.time()
     if layerwise:
-        args.no_int2, args.page_size, args.no_cpu_baseline = True, 0, True
+        args.no_int2, args.page_size, args.no_cpu_baseline, args.no_anchor = True, 0, True, True
         wl = W.generate(cfg, layers=[0])
         lens_d = torch.from_numpy(wl.seq_lens).cuda()
         K0 = dev(wl.K[0])
@@ -444,6 +487,13 @@ def main():
                 assert set(ii[b, g][ii[b, g] >= 0].tolist()) <= set(pool[b, g].tolist())
 
     if args.timeline:
+        if args.key_bits == 2:  # the same steps over INT2 proposal keys
+            K0 = dev(w.K[0])
+            Kq2, sc2 = PB.quantize_keys_int2(K0, seq_lens=lens_d)
+            del K0
+            steps = [PrismStep(s["q0"], Kq2 if j == 0 else Kq2.clone(), sc2 if j == 0 else sc2.clone(),
+                               [LayerInputs(*L) for L in s["layers"]], cfg.kp, cfg.kappa, seq_lens=lens_d,
+                               ws_propose=ws_p, ws_refine=ws_r, key_bits=2) for j, s in enumerate(sets)]
         for i in range(args.warmup):
             steps[i % R]()
         torch.cuda.synchronize()
@@ -540,11 +590,14 @@ def main():
                      for b in range(cfg.B) for _ in range(cfg.Hkv))
     scan_us = kernels.get("k_scan", {}).get("avg_us")
     achieved = scan_bytes / (scan_us * 1e-6) / 1e9 if scan_us else None
-    traffic = None
+    traffic = step_traffic = None
     if os.path.exists(PMC_FILE):
         pmc = json.load(open(PMC_FILE))
-        if pmc.get("source_hash") == kernel_source_hash() and pmc.get("workload") == cfg.name:
-            traffic = pmc.get("traffic_bytes_per_launch")
+        if pmc.get("workload") == cfg.name:
+            if pmc.get("source_hash") == kernel_source_hash():
+                traffic = pmc.get("traffic_bytes_per_launch")
+            if pmc.get("all_sources_hash") == all_sources_hash():
+                step_traffic = pmc.get("traffic_bytes_per_step")
     roofline = {"kernel": "k_scan", "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4) if achieved else None,
@@ -567,6 +620,53 @@ def main():
             secondary[kname] = {"bound": "hbm", "limited_by": "gather latency", "achieved": round(ach, 1),
                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
                                 "algorithmic_bytes_per_launch": int(kb), "avg_launch_us": round(kus, 3)}
+
+    # the whole step against the same roof: algorithmic bytes per step over the timed step time,
+    # the bar set for this workload (0.6 of 8 TB/s), every kernel's own fraction (algorithmic
+    # bytes per launch over its event-timed duration; the selection kernels move no algorithmic
+    # bytes), and the counters' HBM bytes per step over every launch of the step
+    kb_launch = {"k_scan": scan_bytes, "k_cand": 0, "k_compact": 4 * cfg.kp * cfg.units}
+    for kname in ("k_rscore", "k_attend"):
+        if kname in secondary:
+            kb_launch[kname] = secondary[kname]["algorithmic_bytes_per_launch"]
+    step_ach = ab["step"] / (ms_per_step * 1e-3) / 1e9
+    step_roofline = {
+        "bound": "hbm", "achieved": round(step_ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        "frac": round(step_ach / PEAK_HBM_GBPS, 4), "algorithmic_bytes_per_step": int(ab["step"]),
+        "traffic": step_traffic,
+        "traffic_over_algorithmic": round(step_traffic / ab["step"], 4) if step_traffic else None,
+        "target_frac": 0.6, "target_met": bool(step_ach / PEAK_HBM_GBPS >= 0.6),
+        "ms_per_step_at_target": round(ab["step"] / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e3, 5),
+        "kernels_frac": {k: round(kb_launch[k] / (kernels[k]["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+                         for k in kb_launch if k in kernels},
+    }
+
+    # the step variant in which the anchor layer also attends (its own pool on its exact K and V,
+    # right after the proposal); the default step leaves it out (the pages give the anchor only the
+    # proposing role)
+    anchor = None
+    if not args.no_anchor and not layerwise:
+        w0 = W.generate(cfg.with_(anchor_v=True), layers=[0])
+        K0d, V0d = dev(w0.K[0]), dev(w0.V[0])
+        del w0
+        steps_a = []
+        for j, s_ in enumerate(sets):
+            k0, v0 = (K0d, V0d) if j == 0 else (K0d.clone(), V0d.clone())
+            steps_a.append(PrismStep(s_["q0"], s_["Kq"], s_["sc"], [LayerInputs(*L) for L in s_["layers"]], cfg.kp,
+                                     cfg.kappa, seq_lens=lens_d, ws_propose=ws_p, ws_refine=ws_r,
+                                     anchor=LayerInputs(s_["q0"], k0, v0)))
+        for i in range(args.warmup):
+            steps_a[i % R]()
+        reps_a = sorted(timed(lambda i: steps_a[i % R]())[0] for _ in range(args.repeats))
+        ms_a = float(np.median(reps_a))
+        ab_a = ab["step"] + ab["refine_per_layer"]
+        anchor = {"ms_per_step": round(ms_a, 5), "steps_per_s": round(1000.0 / ms_a, 2), "launch": "stream",
+                  "ms_per_step_p10": round(float(np.percentile(reps_a, 10)), 5),
+                  "ms_per_step_p90": round(float(np.percentile(reps_a, 90)), 5),
+                  "algorithmic_bytes_per_step": int(ab_a), "hbm_GBps": round(ab_a / (ms_a * 1e-3) / 1e9, 1),
+                  "added_us_vs_default": round(1000.0 * (ms_a - med["stream"]), 3),
+                  "layers": f"proposal + anchor attention + {cfg.n_refined} refined layers"}
+        del steps_a, K0d, V0d
 
     # the same step with INT2 proposal keys (a second key format; the headline above is int8):
     # stream-launched, same buffer rotation and workspaces, plus how its pools compare with int8's
@@ -722,9 +822,12 @@ def main():
                     break
         except OSError:
             pass
-        cpu = {"value": round(n / cs, 3), "unit": "steps/s", "cores": threads, "kind": "oracle",
+        cpu = {"value": round(n / cs, 3), "unit": "steps/s", "cores": threads,
+               "host_cores": len(os.sched_getaffinity(0)), "host_cpus_total": os.cpu_count(), "kind": "oracle",
                "sample": f"{n} full steps of the same workload ({cfg.units} units, proposal + "
-                         f"{cfg.n_refined} refined layers) in {cs:.1f} s, OpenMP over units",
+                         f"{cfg.n_refined} refined layers) in {cs:.1f} s, OpenMP over the units: {threads} "
+                         f"threads on a host with {len(os.sched_getaffinity(0))} cores available "
+                         f"({os.cpu_count()} CPUs in all); the oracle has no finer parallelism than a unit",
                "value_1_thread": round(1.0 / cs1, 3), "cpu_model": model}
         assert np.array_equal(opool, pool), "oracle and GPU pools differ"
 
@@ -743,7 +846,9 @@ def main():
         "hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(ab["step"]),
         "roofline": roofline,
+        "step_roofline": step_roofline,
         "refine_rooflines": secondary,
+        "anchor_attention": anchor,
         "launch": launch,
         "repeats": len(rep_ms), "ms_per_step_p10": round(ms_p10, 5), "ms_per_step_p90": round(ms_p90, 5),
         "tokens_per_s": round(cfg.B * steps_per_s, 2),

@@ -7,6 +7,9 @@ Usage: python -m token_level_sparse_prism_amd.build   (or python token_level_spa
        python -m token_level_sparse_prism_amd.build --timeline
            also builds lib/libprism_tl.so: the same sources with PRISM_TIMELINE=1, whose kernels
            record per-workgroup phase timestamps (a diagnostics build; bench.py --timeline loads it)
+       python -m token_level_sparse_prism_amd.build --only-timeline --define NAME=VALUE ... --out FILE
+           builds only a timeline library, with extra build settings (for example
+           PRISM_SELECT_LEAN=0, the general selection path), as lib/FILE (bench.py --lib loads it)
 """
 import concurrent.futures as cf
 import glob
@@ -39,9 +42,12 @@ def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 0, timeline: bool = False) -> str:
+def build(verbose: bool = False, jobs: int = 0, timeline: bool = False, defines=(), out: str = "") -> str:
     build_dir, lib = (BUILD_TL, LIB_TL) if timeline else (BUILD, LIB)
-    extra = ("-DPRISM_TIMELINE=1",) if timeline else ()
+    if out:
+        lib = os.path.join(LIBDIR, os.path.basename(out))
+        build_dir = os.path.join(PKG, "_build_" + os.path.splitext(os.path.basename(out))[0])
+    extra = (("-DPRISM_TIMELINE=1",) if timeline else ()) + tuple(f"-D{d}" for d in defines)
     os.makedirs(build_dir, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -61,7 +67,15 @@ def build(verbose: bool = False, jobs: int = 0, timeline: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
-    if "--timeline" in sys.argv[1:]:
-        build(verbose=True, timeline=True)
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--timeline", action="store_true")
+    ap.add_argument("--only-timeline", action="store_true")
+    ap.add_argument("--define", action="append", default=[])
+    ap.add_argument("--out", default="")
+    opts = ap.parse_args()
+    if not opts.only_timeline:
+        build(verbose=True)
+    if opts.timeline or opts.only_timeline:
+        build(verbose=True, timeline=True, defines=opts.define, out=opts.out)
     sys.exit(0)

@@ -10,6 +10,10 @@
 #include "prism_device.hpp"
 #include "prism_prof.hpp"
 
+#ifndef PRISM_SCAN_Q_FIRST
+#define PRISM_SCAN_Q_FIRST 0  // 1: SUM wide scan requests its first rows only after the query has arrived
+#endif
+
 namespace prism {
 
 template <int CH>
@@ -79,6 +83,13 @@ __device__ __forceinline__ int lane_dot(const int* qw, uint4 k, int c3) {
 template <int KB>
 __device__ __forceinline__ int lane_dot(const int* qw, uint32_t w, int c3) {
     return 2 * dot_2bit_word(qw, w, 0) + c3;
+}
+
+// The query quantizer: clamp(rint(x * inv), -127, 127) with inv = 127 / absmax (one fp32 product,
+// round half to even), as for the keys.
+__device__ __forceinline__ int scan_qcode(float x, float inv) {
+    const float r = __builtin_rintf(x * inv);
+    return int(fminf(fmaxf(r, -127.0f), 127.0f));
 }
 
 // kPg: 0 contiguous caches; 1 paged, a page id per row; 2 paged with pages of at least TPR tokens,
@@ -360,8 +371,11 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
 
     __shared__ uint32_t s_hist[kHistBins];
     __shared__ uint32_t s_key[CHW];  // aggregated int32 dot products, each batch's by its wave
-    __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
+    __shared__ __attribute__((aligned(16))) int8_t s_q[kMax ? NQ : 1][D];
     __shared__ float s_red[NW];
+    // SUM: the group's query (fp32) for every wave, and each wave's own codes
+    __shared__ float s_qs[kMax ? 1 : kMaxG * 256];
+    __shared__ __attribute__((aligned(16))) int8_t s_qw[kMax ? 1 : NW][kMax ? 1 : NQ][D];
     __shared__ int32_t s_pg[paged ? CHW / TPW + 2 : 1];
     __shared__ uint32_t s_next;
 
@@ -386,7 +400,7 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
         for (int i = tid; i < kHistBins; i += NT) h2[i] = 0u;
         if (tid < kCandLists) a.cand_cnt[(int64_t(unit) * kCandLists + tid) * kCtrStride] = 0u;
     }
-    float* s_qf = reinterpret_cast<float*>(s_hist);
+    float* s_qf = kMax ? reinterpret_cast<float*>(s_hist) : s_qs;
     const int64_t qoff = (int64_t(b) * d.Hq + int64_t(g) * G) * D;
     const int qe = a.q_bf16 ? 8 : 4;
     constexpr int QP = (kMaxG * 256 / 4 + NT - 1) / NT;
@@ -448,68 +462,110 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
     int bcur = wave;                  // wave w starts on batch w
     float sc_cur[SPL], sc_nxt[SPL];   // scales of batch bcur and of the batch being loaded
     typename SR::R kv[U];
-    load_scales(bcur, sc_cur);        // before the rows: loads complete in issue order
+    auto load_first = [&]() {
+        load_scales(bcur, sc_cur);    // before the rows: loads complete in issue order
 #pragma unroll
-    for (int u = 0; u < U; ++u) kv[u] = load_item(bcur * U + u);
+        for (int u = 0; u < U; ++u) kv[u] = load_item(bcur * U + u);
+    };
+    if constexpr (kMax || !PRISM_SCAN_Q_FIRST) load_first();
     if (tid == 0) s_next = NW;
 
-    float amax = 0.0f;
+    int qv[NQ][QW];
+    int c3[NQ];
+    if constexpr (kMax) {
+        // MAX: one code vector per head, quantized once by the workgroup
+        float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < QP; ++i) {
-        const int p = tid + i * NT;
-        float x[8];
-        if (a.q_bf16) unpack16<uint16_t>(qraw[i], x);
-        else unpack16<float>(qraw[i], x);
-        if (p < npieces) {
-            for (int e = 0; e < qe; ++e) {
-                s_qf[p * qe + e] = x[e];
-                amax = fmaxf(amax, fabsf(x[e]));
+        for (int i = 0; i < QP; ++i) {
+            const int p = tid + i * NT;
+            float x[8];
+            if (a.q_bf16) unpack16<uint16_t>(qraw[i], x);
+            else unpack16<float>(qraw[i], x);
+            if (p < npieces) {
+                for (int e = 0; e < qe; ++e) {
+                    s_qf[p * qe + e] = x[e];
+                    amax = fmaxf(amax, fabsf(x[e]));
+                }
+            }
+        }
+        amax = wave_max(amax);
+        if (lane == 0) s_red[wave] = amax;
+        __syncthreads();
+        amax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) amax = fmaxf(amax, s_red[w]);
+        const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+        for (int dd = tid; dd < D; dd += NT) {
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) s_q[h][dd] = int8_t(h < G ? scan_qcode(s_qf[h * D + dd], inv) : 0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+            for (int m = 0; m < QW / 4; ++m) {
+                const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * DPL + 16 * m]);
+                qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
+            }
+        }
+        for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+        __syncthreads();
+    } else {
+        // SUM: one barrier.  The group's query goes to LDS as fp32 and the histogram is cleared;
+        // then every wave takes the group's absmax and the codes of every dim on its own (the
+        // same values in every wave), writes them to its own LDS rows and reads back its lanes'
+        // words, so no wave waits for another after the barrier.
+#pragma unroll
+        for (int i = 0; i < QP; ++i) {
+            const int p = tid + i * NT;
+            float x[8];
+            if (a.q_bf16) unpack16<uint16_t>(qraw[i], x);
+            else unpack16<float>(qraw[i], x);
+            if (p < npieces)
+                for (int e = 0; e < qe; ++e) s_qf[p * qe + e] = x[e];
+        }
+        // the work item's first rows are requested once the query is in: issued at the kernel's
+        // start they flood the memory system, and the query's few loads wait behind the flood
+        PRISM_TL(kTlScan, 1);
+        if constexpr (PRISM_SCAN_Q_FIRST) {
+            __builtin_amdgcn_sched_barrier(0);  // keep the row loads behind the query's use
+            load_first();
+        }
+        for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+        __syncthreads();
+        PRISM_TL(kTlScan, 2);
+        float amax = 0.0f;
+        for (int i = lane; i < G * D; i += 64) amax = fmaxf(amax, fabsf(s_qf[i]));
+        amax = wave_max(amax);
+        const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+        for (int dd = lane; dd < D; dd += 64) {
+            if constexpr (NQ == 1) {
+                s_qw[wave][0][dd] = int8_t(scan_qcode(s_qf[dd], inv));
+            } else {
+                int qs = 0;
+                for (int h = 0; h < G; ++h) qs += scan_qcode(s_qf[h * D + dd], inv);
+                const int lo = ((qs + 8) & 15) - 8;
+                s_qw[wave][0][dd] = int8_t((qs - lo) >> 4);
+                s_qw[wave][1][dd] = int8_t(lo);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();  // the wave's LDS writes above precede its reads below
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+            for (int m = 0; m < QW / 4; ++m) {
+                const uint4 w = *reinterpret_cast<const uint4*>(&s_qw[wave][n][sub * DPL + 16 * m]);
+                qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
             }
         }
     }
-    amax = wave_max(amax);
-    if (lane == 0) s_red[wave] = amax;
-    __syncthreads();
-    amax = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) amax = fmaxf(amax, s_red[w]);
-    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-    auto code = [&](float x) -> int {
-        float r = __builtin_rintf(x * inv);
-        return int(fminf(fmaxf(r, -127.0f), 127.0f));
-    };
-    for (int dd = tid; dd < D; dd += NT) {
-        if constexpr (kMax) {
-#pragma unroll
-            for (int h = 0; h < NQ; ++h) s_q[h][dd] = int8_t(h < G ? code(s_qf[h * D + dd]) : 0);
-        } else if constexpr (NQ == 1) {
-            s_q[0][dd] = int8_t(code(s_qf[dd]));
-        } else {
-            int qs = 0;
-            for (int h = 0; h < G; ++h) qs += code(s_qf[h * D + dd]);
-            const int lo = ((qs + 8) & 15) - 8;
-            const int hi = (qs - lo) >> 4;
-            s_q[0][dd] = int8_t(hi);
-            s_q[1][dd] = int8_t(lo);
-        }
-    }
-    __syncthreads();
-    int qv[NQ][QW];
-    int c3[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
         int qs = 0;
 #pragma unroll
-        for (int m = 0; m < QW / 4; ++m) {
-            const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * DPL + 16 * m]);
-            qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
-        }
-#pragma unroll
         for (int i = 0; i < QW; ++i) qs = __builtin_amdgcn_sdot4(qv[n][i], 0x01010101, qs, false);
         c3[n] = -3 * qs;
     }
-    for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
-    __syncthreads();
 
     auto claim = [&]() -> int {
         uint32_t v = 0u;
@@ -552,7 +608,7 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
             }
         }
     };
-    PRISM_TL(kTlScan, 1);
+    PRISM_TL(kTlScan, 3);
     for (;;) {  // work items of this workgroup; the rows of its first batch per wave are in flight
         if (nvalid == 0) break;  // later work items are past T_b too
         nb = __builtin_amdgcn_readfirstlane(nb);
@@ -593,13 +649,13 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) kv[u] = load_item(bcur * U + u);
     }
-    PRISM_TL(kTlScan, 2);
+    PRISM_TL(kTlScan, 4);
     uint32_t* gh = a.hist1 + (int64_t(unit) * a.hist_rep + ui.x % a.hist_rep) * kHistBins;
     for (int i = tid; i < kHistBins; i += NT) {
         const uint32_t c = s_hist[i];
         if (c) atomicAdd(&gh[i], c);
     }
-    PRISM_TL(kTlScan, 3);
+    PRISM_TL(kTlScan, 5);
 }
 
 // ---------------------------------------------------------------------------------------------
