@@ -245,7 +245,8 @@ def timeline_summary(recs, kernels):
     the 90th percentile) over workgroups of the time between consecutive stamps (phases a
     workgroup did not reach are left out).  Stamps tick at 100 MHz."""
     import numpy as np
-    per = {k: {"span": [], "gap_before": [], "wgs": [], "phases": {}} for k in kernels}
+    per = {k: {"span": [], "gap_before": [], "wgs": [], "phases": {}, "start_spread": [], "wg_time": []}
+           for k in kernels}
     for rec in recs:
         prev_end = None
         for k in kernels:
@@ -258,6 +259,8 @@ def timeline_summary(recs, kernels):
             end = a.max()
             per[k]["span"].append((end - t0) / 100.0)
             per[k]["wgs"].append(int(live.sum()))
+            per[k]["start_spread"].append(float(np.percentile(a[:, 0] - t0, 90)) / 100.0)
+            per[k]["wg_time"].append(float(np.median(a.max(axis=1) - a[:, 0])) / 100.0)
             if prev_end is not None:
                 per[k]["gap_before"].append((t0 - prev_end) / 100.0)
             prev_end = end
@@ -274,6 +277,8 @@ def timeline_summary(recs, kernels):
         if not v["span"]:
             continue
         out[k] = {"workgroups": int(np.median(v["wgs"])), "span_us": round(float(np.median(v["span"])), 2),
+                  "start_spread_p90_us": round(float(np.median(v["start_spread"])), 2),
+                  "wg_time_median_us": round(float(np.median(v["wg_time"])), 2),
                   "gap_before_us": round(float(np.median(v["gap_before"])), 2) if v["gap_before"] else None,
                   "phases_us": {n: {"median": round(float(np.median([x[0] for x in L])), 2),
                                     "p90": round(float(np.median([x[1] for x in L])), 2),
@@ -302,7 +307,8 @@ def timeline_readout(args, cfg, steps, R):
         ph = ", ".join(f"{n} {x['median']:.2f} (p90 {x['p90']:.2f}, {x['workgroups']} wg)"
                        for n, x in v["phases_us"].items())
         gap = f"gap before {v['gap_before_us']:.2f} us, " if v["gap_before_us"] is not None else ""
-        print(f"{k:10s} {v['workgroups']:5d} wg  span {v['span_us']:6.2f} us  {gap}{ph}", flush=True)
+        print(f"{k:10s} {v['workgroups']:5d} wg  span {v['span_us']:6.2f} us  (starts within {v['start_spread_p90_us']:.2f} "
+              f"us for 90%, median workgroup {v['wg_time_median_us']:.2f} us)  {gap}{ph}", flush=True)
     return 0
 
 

@@ -160,6 +160,59 @@ __device__ __forceinline__ void block_excl_scan1_n(const uint32_t* v, uint32_t* 
     }
 }
 
+// Ranks in slot order of one tile's selected slots when every key at or above tau is taken:
+// thread t holds slots slot0 + 2 NT r + 2 t + e in kv[r] (keys .x/.z, ids .y/.w).  Per row, two
+// wave ballots give every slot's rank among the wave's slots; the waves' counts per row are
+// exchanged once (one barrier) and prefixed with a 16-lane DPP scan.  Slots of ranks
+// [r0, r0 + n) land in s_slot / s_tok.  Returns base plus the tile's selected count; ends with a
+// barrier (s_tmp, ROWS * NT/64 words, is free again).
+template <int NT>
+__device__ __forceinline__ uint32_t sel_rank_ge_tile(const uint4* kv, uint32_t tau, int32_t slot_t0, uint32_t base,
+                                                     int r0, int n, uint32_t* s_tmp, int32_t* s_slot,
+                                                     int32_t* s_tok) {
+    constexpr int NW = NT / 64;
+    constexpr int ROWS = sel_rows<NT>();
+    static_assert(NW <= 16 && ROWS * NW <= sel_tmp_words<NT>(), "wave counts fit s_tmp");
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    uint64_t m0[ROWS], m1[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        m0[r] = ballot64(kv[r].x >= tau);
+        m1[r] = ballot64(kv[r].z >= tau);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) s_tmp[r * NW + wave] = uint32_t(__popcll(m0[r]) + __popcll(m1[r]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        uint32_t x = lane < NW ? s_tmp[r * NW + lane] : 0u;
+        x += dpp_u32<0x111>(x);
+        x += dpp_u32<0x112>(x);
+        x += dpp_u32<0x114>(x);
+        x += dpp_u32<0x118>(x);
+        const uint32_t before = wu > 0 ? readlane_u32(x, wu - 1) : 0u;
+        const uint32_t rank0 = base + before + lanes_below(m0[r]) + lanes_below(m1[r]);
+        const bool s0 = kv[r].x >= tau, s1 = kv[r].z >= tau;
+        const int32_t slot0 = slot_t0 + r * 2 * NT + tid * 2;
+        const uint32_t off0 = rank0 - uint32_t(r0);  // wraps for ranks below r0
+        const uint32_t off1 = off0 + (s0 ? 1u : 0u);
+        if (s0 && off0 < uint32_t(n)) {
+            s_slot[off0] = slot0;
+            s_tok[off0] = int32_t(kv[r].y);
+        }
+        if (s1 && off1 < uint32_t(n)) {
+            s_slot[off1] = slot0 + 1;
+            s_tok[off1] = int32_t(kv[r].w);
+        }
+        base += readlane_u32(x, NW - 1);
+    }
+    __syncthreads();  // s_tmp is free again, s_slot / s_tok complete
+    return base;
+}
+
 // Single-tile selection (kp <= kSelTile, NT * 8 == kSelTile).  Thread t holds slots
 // 2 NT r + 2 t + e (rows r < 4, e < 2) in registers for the whole selection, loaded as one
 // coalesced 16-byte {key, id} pair per row.
@@ -281,10 +334,17 @@ __device__ __forceinline__ bool select_ranks_lean(const uint2* __restrict__ gk, 
     }
     PRISM_TL(kTlSelect, 4);
 
-    // ranks in slot order (row-major over the tile): per thread and row the keys taken (above
-    // tau, or at least tau when every key equal to tau is taken) and, when only some ties are
-    // taken, the keys equal to tau; two rows per 16-bit-packed word, one workgroup scan
     const bool take_all_eq = need >= eq_total;
+    const int n = int(kap) - r0 <= 0 ? 0 : (int(kap) - r0 > nmax ? nmax : int(kap) - r0);
+    if (take_all_eq) {  // every key at or above tau is taken: ballot ranks
+        sel_rank_ge_tile<NT>(kv, tau, 0, 0u, r0, n, s_tmp, s_slot, s_tok);
+        PRISM_TL(kTlSelect, 5);
+        out->n = n;
+        return true;
+    }
+    // some keys equal to tau are left out: ranks in slot order (row-major over the tile) from the
+    // per-thread and per-row counts of keys above tau and keys equal to tau, two rows per
+    // 16-bit-packed word, one workgroup scan
     uint32_t v[4], pre[4], tot[4];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -294,32 +354,27 @@ __device__ __forceinline__ bool select_ranks_lean(const uint2* __restrict__ gk, 
             const uint4 k = kv[2 * p + h];
             const uint32_t gt = (k.x > tau ? 1u : 0u) + (k.z > tau ? 1u : 0u);
             const uint32_t e = (k.x == tau ? 1u : 0u) + (k.z == tau ? 1u : 0u);
-            sel += (take_all_eq ? gt + e : gt) << (16 * h);
+            sel += gt << (16 * h);
             eq += e << (16 * h);
         }
         v[p] = sel;
         v[2 + p] = eq;
     }
     // s_tmp's words from the crossing scan were last read before the barriers above
-    if (take_all_eq) {
-        block_excl_scan1_n<2, NT>(v, pre, tot, s_tmp);
-    } else {
-        block_excl_scan1_n<4, NT>(v, pre, tot, s_tmp);
-    }
-    const int n = int(kap) - r0 <= 0 ? 0 : (int(kap) - r0 > nmax ? nmax : int(kap) - r0);
+    block_excl_scan1_n<4, NT>(v, pre, tot, s_tmp);
     uint32_t rows_sel = 0, rows_eq = 0;  // taken keys and ties of the rows before
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
         const int p = r / 2, sh = 16 * (r % 2);
         const uint32_t sel_before = rows_sel + ((pre[p] >> sh) & 0xFFFFu);
-        uint32_t eqi = take_all_eq ? 0u : rows_eq + ((pre[2 + p] >> sh) & 0xFFFFu);
-        uint32_t rank = sel_before + (take_all_eq ? 0u : (eqi < need ? eqi : need));
+        uint32_t eqi = rows_eq + ((pre[2 + p] >> sh) & 0xFFFFu);  // ties before this row's slots
+        uint32_t rank = sel_before + (eqi < need ? eqi : need);
         const uint32_t k2[2] = {kv[r].x, kv[r].z};
         const int32_t t2[2] = {int32_t(kv[r].y), int32_t(kv[r].w)};
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const bool eqk = k2[e] == tau;
-            const bool take = k2[e] > tau || (eqk && (take_all_eq || eqi < need));
+            const bool take = k2[e] > tau || (eqk && eqi < need);
             eqi += eqk ? 1u : 0u;
             const uint32_t off = rank - uint32_t(r0);  // wraps for ranks below r0
             if (take && off < uint32_t(n)) {
@@ -329,7 +384,7 @@ __device__ __forceinline__ bool select_ranks_lean(const uint2* __restrict__ gk, 
             rank += take ? 1u : 0u;
         }
         rows_sel += (tot[p] >> sh) & 0xFFFFu;
-        if (!take_all_eq) rows_eq += (tot[2 + p] >> sh) & 0xFFFFu;
+        rows_eq += (tot[2 + p] >> sh) & 0xFFFFu;
     }
     __syncthreads();
     PRISM_TL(kTlSelect, 5);
@@ -517,49 +572,10 @@ __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, 
     // ---- ranks in slot order; ranks [r0, r0 + n) land in s_slot / s_tok ----
     const bool take_all_eq = need >= eq_total;  // every key equal to tau is taken: select key >= tau
     if (take_all_eq) {
-        // every selected key is >= tau: per row, two wave ballots give every slot's rank among the
-        // wave's slots; the waves' counts per row are exchanged once per tile and prefixed with a
-        // 16-lane DPP scan; tiles follow one another in slot order
-        static_assert(NW <= 16 && ROWS * NW <= sel_tmp_words<NT>(), "wave counts fit s_tmp");
         uint32_t base = 0;
-        const int wu = __builtin_amdgcn_readfirstlane(wave);
         for (int t = 0; t < ntiles && base < uint32_t(r0 + n); ++t) {
             if (t > 0) sel_load_tile<NT>(gk, kp, int64_t(t) * kSelTile, kv);
-            uint64_t m0[ROWS], m1[ROWS];
-#pragma unroll
-            for (int r = 0; r < ROWS; ++r) {
-                m0[r] = ballot64(kv[r].x >= tau);
-                m1[r] = ballot64(kv[r].z >= tau);
-            }
-            if (lane == 0) {
-#pragma unroll
-                for (int r = 0; r < ROWS; ++r) s_tmp[r * NW + wave] = uint32_t(__popcll(m0[r]) + __popcll(m1[r]));
-            }
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < ROWS; ++r) {
-                uint32_t x = lane < NW ? s_tmp[r * NW + lane] : 0u;
-                x += dpp_u32<0x111>(x);
-                x += dpp_u32<0x112>(x);
-                x += dpp_u32<0x114>(x);
-                x += dpp_u32<0x118>(x);
-                const uint32_t before = wu > 0 ? readlane_u32(x, wu - 1) : 0u;
-                const uint32_t rank0 = base + before + lanes_below(m0[r]) + lanes_below(m1[r]);
-                const bool s0 = kv[r].x >= tau, s1 = kv[r].z >= tau;
-                const int32_t slot0 = int32_t(int64_t(t) * kSelTile + r * 2 * NT + tid * 2);
-                const uint32_t off0 = rank0 - uint32_t(r0);  // wraps for ranks below r0
-                const uint32_t off1 = off0 + (s0 ? 1u : 0u);
-                if (s0 && off0 < uint32_t(n)) {
-                    s_slot[off0] = slot0;
-                    s_tok[off0] = int32_t(kv[r].y);
-                }
-                if (s1 && off1 < uint32_t(n)) {
-                    s_slot[off1] = slot0 + 1;
-                    s_tok[off1] = int32_t(kv[r].w);
-                }
-                base += readlane_u32(x, NW - 1);
-            }
-            __syncthreads();  // s_tmp is rewritten by the next tile
+            base = sel_rank_ge_tile<NT>(kv, tau, int32_t(int64_t(t) * kSelTile), base, r0, n, s_tmp, s_slot, s_tok);
         }
         PRISM_TL(kTlSelect, 5);
         return res;

@@ -10,6 +10,9 @@
 #include "prism_device.hpp"
 #include "prism_prof.hpp"
 
+#ifndef PRISM_SCAN_NIBBLE
+#define PRISM_SCAN_NIBBLE 1  // 2-bit keys, SUM: the wide scan's dot products on 4-bit digits (v_dot8_i32_i4)
+#endif
 #ifndef PRISM_SCAN_Q_FIRST
 #define PRISM_SCAN_Q_FIRST 0  // 1: SUM wide scan requests its first rows only after the query has arrived
 #endif
@@ -83,6 +86,26 @@ __device__ __forceinline__ int lane_dot(const int* qw, uint4 k, int c3) {
 template <int KB>
 __device__ __forceinline__ int lane_dot(const int* qw, uint32_t w, int c3) {
     return 2 * dot_2bit_word(qw, w, 0) + c3;
+}
+
+// 2-bit keys against three signed base-16 digit vectors of the summed query codes (8 nibble words
+// each): a 32-bit key word gives two nibble words under the masks 0x33333333 and
+// (w >> 2) & 0x33333333 (codes 0..3, non-negative as signed 4-bit values), and each meets one
+// v_dot8_i32_i4 per digit.  sum_d qs_d b_d = 256 S2 + 16 S1 + S0 exactly in int32.
+__device__ __forceinline__ int lane_dot_nib(const int (*qn)[8], uint4 k, int c3) {
+    const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+    int s0 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int lo = int(w[m] & 0x33333333u), hi = int((w[m] >> 2) & 0x33333333u);
+        s0 = __builtin_amdgcn_sdot8(qn[0][2 * m], lo, s0, false);
+        s1 = __builtin_amdgcn_sdot8(qn[1][2 * m], lo, s1, false);
+        s2 = __builtin_amdgcn_sdot8(qn[2][2 * m], lo, s2, false);
+        s0 = __builtin_amdgcn_sdot8(qn[0][2 * m + 1], hi, s0, false);
+        s1 = __builtin_amdgcn_sdot8(qn[1][2 * m + 1], hi, s1, false);
+        s2 = __builtin_amdgcn_sdot8(qn[2][2 * m + 1], hi, s2, false);
+    }
+    return 2 * (256 * s2 + 16 * s1 + s0) + c3;
 }
 
 // The query quantizer: clamp(rint(x * inv), -127, 127) with inv = 127 / absmax (one fp32 product,
@@ -358,12 +381,15 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
     constexpr int NW = NT / 64;
     constexpr bool paged = kPg != 0;
     static_assert(kPg != 1, "pages smaller than a wave-load use k_scan");
-    constexpr int DPL = (KB == 2 && NQ <= 2) ? 64 : 16;
+    // NQ == 3 (2-bit keys, SUM): the group's summed query codes as three signed base-16 digits,
+    // each dotted with the keys' 2-bit codes eight dims at a time (v_dot8_i32_i4)
+    constexpr bool kNib = KB == 2 && NQ == 3 && !kMax;
+    constexpr int DPL = (KB == 2 && (NQ <= 2 || kNib)) ? 64 : 16;
     using SR = ScanRow<KB, DPL>;
     constexpr int QW = DPL / 4;
     constexpr int LPT = D / DPL;
     constexpr int TPW = 64 / LPT;          // tokens per wave-load
-    constexpr int U = KB == 8 ? SR::kLoads : (NQ <= 2 ? SR::kLoads : (NQ <= 8 ? SR::kLoads / 2 : SR::kLoads / 4));
+    constexpr int U = KB == 8 ? SR::kLoads : ((NQ <= 2 || kNib) ? SR::kLoads : (NQ <= 8 ? SR::kLoads / 2 : SR::kLoads / 4));
     constexpr int BT = U * TPW;            // tokens per batch
     constexpr int SPL = (BT + 63) / 64;    // a batch's scales (and keys) per lane
     static_assert(CHW % BT == 0 && CHW / BT >= NW, "every wave starts on a batch of its own");
@@ -376,6 +402,7 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
     // SUM: the group's query (fp32) for every wave, and each wave's own codes
     __shared__ float s_qs[kMax ? 1 : kMaxG * 256];
     __shared__ __attribute__((aligned(16))) int8_t s_qw[kMax ? 1 : NW][kMax ? 1 : NQ][D];
+    __shared__ __attribute__((aligned(16))) uint32_t s_qn[kNib ? NW : 1][kNib ? (D / DPL) * 24 : 4];
     __shared__ int32_t s_pg[paged ? CHW / TPW + 2 : 1];
     __shared__ uint32_t s_next;
 
@@ -470,7 +497,8 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
     if constexpr (kMax || !PRISM_SCAN_Q_FIRST) load_first();
     if (tid == 0) s_next = NW;
 
-    int qv[NQ][QW];
+    constexpr int QV = kNib ? 8 : QW;      // q words per vector and lane (nibble words: 8 per digit)
+    int qv[NQ][QV];
     int c3[NQ];
     if constexpr (kMax) {
         // MAX: one code vector per head, quantized once by the workgroup
@@ -539,7 +567,17 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
         amax = wave_max(amax);
         const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
         for (int dd = lane; dd < D; dd += 64) {
-            if constexpr (NQ == 1) {
+            if constexpr (kNib) {
+                // qs = 256 d2 + 16 d1 + d0 with every digit in [-8, 7] (|qs| <= 15 * 127)
+                int qs = 0;
+                for (int h = 0; h < G; ++h) qs += scan_qcode(s_qf[h * D + dd], inv);
+                const int d0 = ((qs + 8) & 15) - 8;
+                const int r1 = (qs - d0) >> 4;
+                const int d1 = ((r1 + 8) & 15) - 8;
+                s_qw[wave][0][dd] = int8_t(d0);
+                s_qw[wave][1][dd] = int8_t(d1);
+                s_qw[wave][2][dd] = int8_t((r1 - d1) >> 4);
+            } else if constexpr (NQ == 1) {
                 s_qw[wave][0][dd] = int8_t(scan_qcode(s_qf[dd], inv));
             } else {
                 int qs = 0;
@@ -550,21 +588,55 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
             }
         }
         __builtin_amdgcn_wave_barrier();  // the wave's LDS writes above precede its reads below
+        if constexpr (kNib) {
+            // nibble k of word 2m holds the digit of dim 16m + 8 (k & 1) + (k >> 1), of word 2m + 1
+            // that of dim 16m + 4 + 8 (k & 1) + (k >> 1): the order in which the 2-bit codes of one
+            // 32-bit key word land in nibbles under the masks 0x33333333 and 0x33333333 << 2.
+            // The wave packs each of its LPT * 24 distinct words once (lane l takes word l, l + 64),
+            // then every lane reads the 24 words of its dims.
+            constexpr int NWD = LPT * 24;
+            for (int l = lane; l < NWD; l += 64) {
+                const int sb = l / 24, n = (l % 24) / 8, m = (l % 8) / 2, hf = l % 2;
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(&s_qw[wave][n][sb * DPL + 16 * m]);
+                s_qn[wave][l] = (src[hf] & 0x0F0F0F0Fu) | ((src[2 + hf] & 0x0F0F0F0Fu) << 4);
+            }
+            __builtin_amdgcn_wave_barrier();  // the packed words precede their reads
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
+            for (int n = 0; n < 3; ++n) {
 #pragma unroll
-            for (int m = 0; m < QW / 4; ++m) {
-                const uint4 w = *reinterpret_cast<const uint4*>(&s_qw[wave][n][sub * DPL + 16 * m]);
-                qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
+                for (int m = 0; m < 2; ++m) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(&s_qn[wave][sub * 24 + 8 * n + 4 * m]);
+                    qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+                for (int m = 0; m < QW / 4; ++m) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(&s_qw[wave][n][sub * DPL + 16 * m]);
+                    qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
+                }
             }
         }
     }
+    if constexpr (kNib) {  // -3 * (the sum of the lane's summed query codes), from the digits
+        int sd[3];
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-        int qs = 0;
+        for (int n = 0; n < 3; ++n) {
+            sd[n] = 0;
 #pragma unroll
-        for (int i = 0; i < QW; ++i) qs = __builtin_amdgcn_sdot4(qv[n][i], 0x01010101, qs, false);
-        c3[n] = -3 * qs;
+            for (int i = 0; i < 8; ++i) sd[n] = __builtin_amdgcn_sdot8(qv[n][i], 0x11111111, sd[n], false);
+        }
+        c3[0] = -3 * (256 * sd[2] + 16 * sd[1] + sd[0]);
+    } else {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            int qs = 0;
+#pragma unroll
+            for (int i = 0; i < QW; ++i) qs = __builtin_amdgcn_sdot4(qv[n][i], 0x01010101, qs, false);
+            c3[n] = -3 * qs;
+        }
     }
 
     auto claim = [&]() -> int {
@@ -585,9 +657,13 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
             }
             A = best;
         } else {
-            int acc0 = lane_dot<KB>(qv[0], kv[u], c3[0]);
-            if constexpr (NQ == 2) acc0 = acc0 * 16 + lane_dot<KB>(qv[1], kv[u], c3[1]);
-            A = group_sum_i<LPT>(acc0);
+            if constexpr (kNib) {
+                A = group_sum_i<LPT>(lane_dot_nib(qv, kv[u], c3[0]));
+            } else {
+                int acc0 = lane_dot<KB>(qv[0], kv[u], c3[0]);
+                if constexpr (NQ == 2) acc0 = acc0 * 16 + lane_dot<KB>(qv[1], kv[u], c3[1]);
+                A = group_sum_i<LPT>(acc0);
+            }
         }
         if (sub == 0 && tok < nvalid) s_key[tok] = uint32_t(A);
     };
@@ -694,6 +770,13 @@ static hipError_t launch_scan_w_p(const ProposeArgs& a, int agg_max, dim3 grid, 
     const dim3 blk(kScanWideThreads);
     const int G = a.d.G;
     if (!agg_max) {
+        // 2-bit keys with at most 15 heads per group: the summed codes fit three base-16 digits
+        if constexpr (KB == 2 && PRISM_SCAN_NIBBLE) {
+            if (G <= 15) {
+                launch_k("k_scan", (k_scan_w<D, 3, false, KB, P, C>), grid, blk, st, a);
+                return hipGetLastError();
+            }
+        }
         if (G == 1) launch_k("k_scan", (k_scan_w<D, 1, false, KB, P, C>), grid, blk, st, a);
         else launch_k("k_scan", (k_scan_w<D, 2, false, KB, P, C>), grid, blk, st, a);
     } else {
