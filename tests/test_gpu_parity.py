@@ -236,7 +236,9 @@ REFINE_CASES = [
     (64, 1, 1, PB.AGG_SUM, "f32", 3000, 800, 700, None),         # head-dim split: 4 values per lane
     (64, 16, 2, PB.AGG_SUM, "bf16", 1200, 1024, 300, [1200, 0]), # rank split (G > 8): empty sequence
     (128, 16, 1, PB.AGG_SUM, "f32", 3000, 2000, 1200, None),       # column halves of V, fp32
-    (256, 4, 1, PB.AGG_SUM, "bf16", 4000, 3000, 2000, None),       # column quarters of 256-dim rows
+    (256, 4, 1, PB.AGG_SUM, "bf16", 4000, 3000, 2100, None),       # column quarters of 256-dim rows
+    (128, 4, 1, PB.AGG_SUM, "bf16", 6000, 4096, 2048, None),       # head-dim split: most rows (2048)
+    (64, 8, 1, PB.AGG_MAX, "f32", 4000, 3000, 1025, None),         # head-dim split: 2048-row variant
     (256, 8, 1, PB.AGG_MAX, "bf16", 9000, 8000, 4000, None),       # column quarters, two-level merge
     (128, 4, 1, PB.AGG_SUM, "bf16", 8000, 6000, 3000, None),       # column halves, two-level merge
     (64, 2, 16, PB.AGG_SUM, "bf16", 1500, 1024, 1024, [1500] * 8),  # 128 units: 512 ranks per workgroup

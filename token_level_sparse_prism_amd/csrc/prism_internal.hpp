@@ -35,10 +35,7 @@ constexpr int kRscoreThreads = PRISM_RSCORE_THREADS;  // matrix-core pool scorin
 constexpr int kAttendRanks = 128;      // selected rows per workgroup in sparse attention
 constexpr int kHistRep = 8;            // most copies of a unit's key histogram (see ScanPlan)
 constexpr int kMergeGroup = 16;        // partials merged by one workgroup (two levels above it)
-#ifndef PRISM_ATTEND_DRANKS
-#define PRISM_ATTEND_DRANKS 1024
-#endif
-constexpr int kAttendDRanks = PRISM_ATTEND_DRANKS;  // most selected rows of the head-dimension split attention
+constexpr int kAttendDRanks = 2048;   // most selected rows of the head-dimension split attention
 constexpr int kAttendThreads = 1024;   // 16 waves: the selection's latency is shared by 4 waves per SIMD
 constexpr int kDenseChunk = 256;       // tokens per workgroup in dense attention
 constexpr int kCtrStride = 16;         // counters sit 64 bytes apart (no shared cache line)

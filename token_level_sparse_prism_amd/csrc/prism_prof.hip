@@ -135,11 +135,11 @@ void prism_profile_reset(void) {
     std::lock_guard<std::mutex> lk(prism::g_mu);
     for (auto& r : prism::g_recs) {
         if (r.b) {
-            hipEventSynchronize(r.b);
+            (void)hipEventSynchronize(r.b);
             prism::g_free.push_back(r.b);
         }
         if (r.e) {
-            hipEventSynchronize(r.e);
+            (void)hipEventSynchronize(r.e);
             prism::g_free.push_back(r.e);
         }
     }

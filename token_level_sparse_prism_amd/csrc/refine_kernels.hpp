@@ -13,7 +13,7 @@
 //             slots in slot order (ties to the lower slot), writes idx for its ranks, gathers
 //             their V rows and forms a softmax(.)V partial from the stored logits.  The unit's
 //             last workgroup merges the partials (log-sum-exp) into out and lse.
-//   k_attend_d  in place of k_attend for kappa <= 1024, G <= 8 and small grids: grid (16-byte
+//   k_attend_d  in place of k_attend for kappa <= 2048, G <= 8 and small grids: grid (16-byte
 //             pieces of a V row) x units.  Every workgroup takes the whole selection and writes
 //             its columns of out directly (no partials, no merge).
 // The kernels and their launch templates; k_refine.hip (bf16) and k_refine_f32.hip (fp32)
@@ -334,26 +334,26 @@ __device__ __forceinline__ void wave_reduce_scatter(float (&v)[NV]) {
     for (int j = 0; j < R; ++j) v[j] = group_sum<(64 >> S)>(v[j]);
 }
 
-// Refined attention split over the head dimension, for kappa <= kAttendDRanks and GP <= 8:
+// Refined attention split over the head dimension, for kappa <= KM <= kAttendDRanks and GP <= 8:
 // grid (D / DS column pieces) x units, 1024 threads, DS = 16 bytes of a V row.  Every workgroup
 // derives the unit's whole selection (the same exact top-kappa and slot-order ranks as k_attend)
 // and the softmax statistics over all selected rows, so it writes its DS columns of out and lse
 // directly: no partials and no merge.  When units is a multiple of 8 the unit's workgroups share
 // one XCD (unit_major), so a V row is fetched into that XCD's L2 once and each workgroup reads its
 // 16-byte piece from there.
-// Thread t takes rank t; the waves' sums are combined in LDS in wave order.
-template <typename T, int D, int GP>
+// Thread t takes ranks t, t + 1024, ...; each wave weights its rows by its own maximum and the
+// waves' sums are rescaled to the workgroup maximum and combined in LDS in wave order.
+template <typename T, int D, int GP, int KM>
 __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     constexpr int NT = kAttendThreads;
     constexpr int NW = NT / 64;
     constexpr int DS = Elem<T>::kPerLane;
     constexpr int NS = D / DS;
-    constexpr int KM = kAttendDRanks;
     constexpr int RPT = KM / NT;
     constexpr int NV = GP * DS;
     constexpr int LS = GP < 4 ? 4 : GP;  // logit stride
     constexpr int L4 = LS / 4;           // 16-byte logit pieces per slot
-    static_assert(GP <= 8 && NV <= 64 && KM % NT == 0 && NS >= 2, "head-dimension split shape");
+    static_assert(GP <= 8 && NV <= 64 && KM % NT == 0 && KM <= kAttendDRanks && NS >= 2, "head-dimension split shape");
     static_assert(kHistPadded <= kRowsAccFloats && kSelHistWords <= kRowsAccFloats, "LDS buffer too small");
     __shared__ __align__(16) uint32_t s_big[kRowsAccFloats];  // selection histograms
     __shared__ __align__(16) uint32_t s_cand[kSelCandTotal];
@@ -426,28 +426,21 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
             y[i][h] = (valid && h < G) ? c * a.y_scale : -INFINITY;
         }
     }
+    // each wave weights its rows by its own maximum per head (a wave without rows holds -inf and
+    // weight 0); the cross-wave sum below rescales to the workgroup maximum, so no barrier stands
+    // between a wave's loads and its accumulation
+    float M[GP];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
         float m = y[0][h];
 #pragma unroll
         for (int i = 1; i < RPT; ++i) m = fmaxf(m, y[i][h]);
-        m = wave_max(m);
-        if (lane == 0) s_max[wave * GP + h] = m;
+        M[h] = wave_max(m);
+        if (lane == 0) s_max[wave * GP + h] = M[h];
     }
     PRISM_TL(kTlAttend, 2);
-    __syncthreads();
     PRISM_TL(kTlAttend, 3);
-    // the block maximum per head: lane l reads wave l % 16 of head l / 16, a row-wide DPP max
-    static_assert(NW == 16, "the wave maxima fill one DPP row per head");
-    float M[GP];
-#pragma unroll
-    for (int hb = 0; hb < GP; hb += 4) {  // four heads per round
-        const int hq = hb + (lane >> 4);
-        const float m = group_max<16>(hq < G && hq < GP ? s_max[(lane & 15) * GP + hq] : -INFINITY);
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4)
-            if (hb + h4 < GP) M[hb + h4] = readlane_f32(m, 16 * h4);
-    }
+    static_assert(NW == 16, "one wave maximum per DPP lane");
     float acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
@@ -456,7 +449,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
         float l = 0.0f;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const float p = (tid + i * NT < n && h < G) ? exp2_le0(y[i][h] - M[h]) : 0.0f;
+            const float p = (tid + i * NT < n && h < G) ? exp2_le0(y[i][h] - M[h]) : 0.0f;  // M finite there
             l += p;
             float x[DS];
             unpack16<T>(vraw[i], x);
@@ -480,18 +473,19 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     if (tid < NV) {
         const int h = tid / DS, e = tid % DS;
         if (h < G) {
-            float sacc = s_part[tid], L = s_sum[h];
+            float Mh = -INFINITY;
 #pragma unroll
-            for (int w = 1; w < NW; ++w) {
-                sacc += s_part[w * NV + tid];
-                L += s_sum[w * GP + h];
+            for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_max[w * GP + h]);  // finite: n >= 1
+            float sacc = 0.0f, L = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float c = exp2_le0(s_max[w * GP + h] - Mh);  // 0 for a wave without rows
+                sacc = fmaf(s_part[w * NV + tid], c, sacc);
+                L = fmaf(s_sum[w * GP + h], c, L);
             }
             store_elem<T>(&out[int64_t(h) * D + e], sacc / L);
             if (e == 0 && piece == 0 && lse) {
                 constexpr float kLn2 = 0.6931471805599453f;
-                float Mh = M[0];
-#pragma unroll
-                for (int k = 1; k < GP; ++k) Mh = h == k ? M[k] : Mh;
                 lse[h] = (Mh + log2f(L)) * kLn2;
             }
         }
@@ -536,11 +530,14 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     if (e != hipSuccess) return e;
     if constexpr (PRISM_ATTEND_DSPLIT && GP <= 8) {
         // head-dimension split while its grid (D / 16-byte pieces per unit) fits one workgroup per
-        // CU: every workgroup gathers all kappa rows, so on fuller grids, and for kappa above 1024
-        // with V rows coming from HBM, the rank split is faster
+        // CU: every workgroup gathers all kappa rows, so on fuller grids the rank split is faster
         constexpr int ns = D / Elem<T>::kPerLane;
         if (a.kappa <= kAttendDRanks && int64_t(units) * ns <= int64_t(device_cus())) {
-            launch_k("k_attend", (k_attend_d<T, D, GP>), dim3(ns, units), dim3(kAttendThreads), st, a);
+            if (a.kappa <= kAttendDRanks / 2)
+                launch_k("k_attend", (k_attend_d<T, D, GP, kAttendDRanks / 2>), dim3(ns, units), dim3(kAttendThreads),
+                         st, a);
+            else
+                launch_k("k_attend", (k_attend_d<T, D, GP, kAttendDRanks>), dim3(ns, units), dim3(kAttendThreads), st, a);
             return hipGetLastError();
         }
     }
