@@ -54,7 +54,7 @@ def parse():
                    help="the two rocprofv3 command lines, recorded beside the ingested figures")
     p.add_argument("--timeline", type=int, default=0, metavar="REPS",
                    help="phase timeline instead of the benchmark: REPS passes of one proposal and one refined "
-                        "layer through the timeline build (lib/libprism_tl.so, built by "
+                        "layer, each behind a whole step (so the kernels start back to back), through the timeline build (lib/libprism_tl.so, built by "
                         "`python -m token_level_sparse_prism_amd.build --timeline`); prints per-kernel spans, "
                         "launch gaps and per-phase medians over the workgroups")
     p.add_argument("--key-bits", type=int, default=8, choices=(8, 2),
@@ -236,7 +236,10 @@ TL_PHASE_NAMES = {
     "k_attend": ["selection", "rows + statistics", "accumulate + partial", "arrival", "merge"],
     "k_select": ["keys + level-1 histogram", "crossing", "candidate lists", "exact threshold", "ranks"],
     "k_rows": ["logits + V issue + wave max", "max barrier", "softmax + accumulate"],
+    "k_attend_d": ["selection", "logits + V issue + wave max", "accumulate", "reduce + partials", "barrier",
+                   "sum + store"],
 }
+TL_LAUNCHED = ("k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_attend_d")  # in launch order
 
 
 def timeline_summary(recs, kernels):
@@ -247,9 +250,10 @@ def timeline_summary(recs, kernels):
     import numpy as np
     per = {k: {"span": [], "gap_before": [], "wgs": [], "phases": {}, "start_spread": [], "wg_time": []}
            for k in kernels}
+    order = [k for k in TL_LAUNCHED if k in kernels] + [k for k in kernels if k not in TL_LAUNCHED]
     for rec in recs:
         prev_end = None
-        for k in kernels:
+        for k in order:
             a = rec[k].astype(np.int64)
             live = a[:, 0] > 0
             if not live.any():
@@ -261,9 +265,10 @@ def timeline_summary(recs, kernels):
             per[k]["wgs"].append(int(live.sum()))
             per[k]["start_spread"].append(float(np.percentile(a[:, 0] - t0, 90)) / 100.0)
             per[k]["wg_time"].append(float(np.median(a.max(axis=1) - a[:, 0])) / 100.0)
-            if prev_end is not None:
-                per[k]["gap_before"].append((t0 - prev_end) / 100.0)
-            prev_end = end
+            if k in TL_LAUNCHED:  # phases inside a kernel have no gap of their own
+                if prev_end is not None:
+                    per[k]["gap_before"].append((t0 - prev_end) / 100.0)
+                prev_end = end
             names = TL_PHASE_NAMES.get(k, [])
             for p, name in enumerate(names):
                 ok = (a[:, p] > 0) & (a[:, p + 1] > 0)
@@ -272,7 +277,7 @@ def timeline_summary(recs, kernels):
                     per[k]["phases"].setdefault(name, []).append((float(np.median(d)), float(np.percentile(d, 90)),
                                                                   int(ok.sum())))
     out = {}
-    for k in kernels:
+    for k in order:
         v = per[k]
         if not v["span"]:
             continue
@@ -296,6 +301,7 @@ def timeline_readout(args, cfg, steps, R):
     for rep in range(args.timeline):
         st = steps[rep % R]
         PB.timeline_clear()
+        steps[(rep + 1) % R]()  # a whole step first: the recorded launches then follow others back to back
         st.propose()
         st.refine(0)
         torch.cuda.synchronize()

@@ -276,8 +276,8 @@ prism_status prism_read_probe(const void* src, size_t bytes, uint32_t* sink, voi
  * PRISM_ERR_UNSUPPORTED).  Thread 0 of every workgroup of the proposal and refine kernels
  * stores the GPU's 100 MHz real-time counter at the kernel's phase points; each launch
  * overwrites its workgroups' entries.  prism_timeline_read synchronises the device and copies
- * kernel `kernel`'s (0 k_scan, 1 k_cand, 2 k_compact, 3 k_rscore, 4 k_attend; 5 and 6 are the
- * selection and the rows phase inside k_attend) stamps of
+ * kernel `kernel`'s (0 k_scan, 1 k_cand, 2 k_compact, 3 k_rscore, 4 k_attend, 7 k_attend_d; 5
+ * and 6 are the selection inside either attention kernel and the rows phase of k_attend) stamps of
  * workgroups [0, max_wgs) (linear workgroup id, at most 8192) into out[max_wgs][8]; 0 marks a
  * phase a workgroup did not reach.  prism_timeline_clear zeroes every stamp.
  */

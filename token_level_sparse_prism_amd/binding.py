@@ -394,7 +394,7 @@ def profile_query(name: str) -> Tuple[int, float]:
     return n.value, ms.value
 
 
-TL_KERNELS = ("k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_select", "k_rows")
+TL_KERNELS = ("k_scan", "k_cand", "k_compact", "k_rscore", "k_attend", "k_select", "k_rows", "k_attend_d")
 TL_PHASES = 8
 
 

@@ -21,7 +21,7 @@ bool prof_pair(const char* name, hipEvent_t* begin, hipEvent_t* end);
 // into a device array of its translation unit: [kernel slot][workgroup][phase].  Each launch
 // overwrites its workgroups' entries; prism_timeline_read merges the translation units' arrays.
 // The normal library build compiles every stamp to nothing.
-enum TlKernel { kTlScan = 0, kTlCand, kTlCompact, kTlRscore, kTlAttend, kTlSelect, kTlRows, kTlKernels };
+enum TlKernel { kTlScan = 0, kTlCand, kTlCompact, kTlRscore, kTlAttend, kTlSelect, kTlRows, kTlAttendD, kTlKernels };
 constexpr int kTlWgs = 8192;
 constexpr int kTlPhases = 8;
 #ifndef PRISM_TIMELINE

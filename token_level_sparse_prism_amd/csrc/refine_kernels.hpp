@@ -13,7 +13,7 @@
 //             slots in slot order (ties to the lower slot), writes idx for its ranks, gathers
 //             their V rows and forms a softmax(.)V partial from the stored logits.  The unit's
 //             last workgroup merges the partials (log-sum-exp) into out and lse.
-//   k_attend_d  in place of k_attend for kappa <= 2048, G <= 8 and small grids: grid (16-byte
+//   k_attend_d  in place of k_attend for kappa <= 2048, G <= 8 and small grids: grid (16- or 8-byte
 //             pieces of a V row) x units.  Every workgroup takes the whole selection and writes
 //             its columns of out directly (no partials, no merge).
 // The kernels and their launch templates; k_refine.hip (bf16) and k_refine_f32.hip (fp32)
@@ -24,6 +24,9 @@
 #include "prism_prof.hpp"
 #include "prism_select.hpp"
 
+#ifndef PRISM_ATTEND_D8
+#define PRISM_ATTEND_D8 1  // the head-dimension split takes 8-byte pieces where twice the grid fits
+#endif
 #ifndef PRISM_ATTEND_COLSPLIT
 #define PRISM_ATTEND_COLSPLIT 1  // split the rank-split attention's columns in two on small grids
 #endif
@@ -335,25 +338,28 @@ __device__ __forceinline__ void wave_reduce_scatter(float (&v)[NV]) {
 }
 
 // Refined attention split over the head dimension, for kappa <= KM <= kAttendDRanks and GP <= 8:
-// grid (D / DS column pieces) x units, 1024 threads, DS = 16 bytes of a V row.  Every workgroup
+// grid (D / DS column pieces) x units, 1024 threads, DS = PB bytes (16 or 8) of a V row.  Every workgroup
 // derives the unit's whole selection (the same exact top-kappa and slot-order ranks as k_attend)
 // and the softmax statistics over all selected rows, so it writes its DS columns of out and lse
 // directly: no partials and no merge.  When units is a multiple of 8 the unit's workgroups share
 // one XCD (unit_major), so a V row is fetched into that XCD's L2 once and each workgroup reads its
-// 16-byte piece from there.
+// piece from there.  8-byte pieces halve each workgroup's multiply-adds and lane reductions (the
+// part of the work that is not repeated per workgroup) where twice the workgroups still fit the CUs.
 // Thread t takes ranks t, t + 1024, ...; each wave weights its rows by its own maximum and the
 // waves' sums are rescaled to the workgroup maximum and combined in LDS in wave order.
-template <typename T, int D, int GP, int KM>
+template <typename T, int D, int GP, int KM, int PB>
 __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     constexpr int NT = kAttendThreads;
     constexpr int NW = NT / 64;
-    constexpr int DS = Elem<T>::kPerLane;
+    constexpr int DS = PB / int(sizeof(T));
+    using VR = std::conditional_t<PB == 16, uint4, uint2>;
     constexpr int NS = D / DS;
     constexpr int RPT = KM / NT;
     constexpr int NV = GP * DS;
     constexpr int LS = GP < 4 ? 4 : GP;  // logit stride
     constexpr int L4 = LS / 4;           // 16-byte logit pieces per slot
-    static_assert(GP <= 8 && NV <= 64 && KM % NT == 0 && KM <= kAttendDRanks && NS >= 2, "head-dimension split shape");
+    static_assert((PB == 16 || PB == 8) && GP <= 8 && NV >= 4 && NV <= 64 && KM % NT == 0 && KM <= kAttendDRanks &&
+                  NS >= 2, "head-dimension split shape");
     static_assert(kHistPadded <= kRowsAccFloats && kSelHistWords <= kRowsAccFloats, "LDS buffer too small");
     __shared__ __align__(16) uint32_t s_big[kRowsAccFloats];  // selection histograms
     __shared__ __align__(16) uint32_t s_cand[kSelCandTotal];
@@ -375,12 +381,12 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     const int G = d.G;
     const int64_t kp = a.kp;
 
-    PRISM_TL(kTlAttend, 0);
+    PRISM_TL(kTlAttendD, 0);
     const SelResult sr = select_ranks<NT>(a.skey + int64_t(unit) * a.kstride, kp, uint32_t(a.kappa), 0, KM, s_big,
                                           s_tmp, s_res, s_cand, s_ccount, s_slot, s_tok);
     const int n = sr.n;
     const bool paged = d.pg.table != nullptr;
-    PRISM_TL(kTlAttend, 1);
+    PRISM_TL(kTlAttendD, 1);
 
     // idx: piece p writes ranks [p * per, (p + 1) * per); ranks at or beyond n hold -1
     {
@@ -406,14 +412,14 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     const float* lg = a.logits + int64_t(unit) * kp * LS;
     const T* Vb = static_cast<const T*>(a.V) + cache_row0(d, b, g) * D + piece * DS;
     float4 lraw[RPT][L4];
-    uint4 vraw[RPT];
+    VR vraw[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = tid + i * NT;
         const int rr = r < n ? r : 0;
 #pragma unroll
         for (int j = 0; j < L4; ++j) lraw[i][j] = reinterpret_cast<const float4*>(lg + int64_t(s_slot[rr]) * LS)[j];
-        vraw[i] = *reinterpret_cast<const uint4*>(Vb + int64_t(uint32_t(s_tok[rr])) * D);
+        vraw[i] = *reinterpret_cast<const VR*>(Vb + int64_t(uint32_t(s_tok[rr])) * D);
     }
     float y[RPT][GP];
 #pragma unroll
@@ -438,8 +444,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
         M[h] = wave_max(m);
         if (lane == 0) s_max[wave * GP + h] = M[h];
     }
-    PRISM_TL(kTlAttend, 2);
-    PRISM_TL(kTlAttend, 3);
+    PRISM_TL(kTlAttendD, 2);
     static_assert(NW == 16, "one wave maximum per DPP lane");
     float acc[NV];
 #pragma unroll
@@ -451,15 +456,16 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
         for (int i = 0; i < RPT; ++i) {
             const float p = (tid + i * NT < n && h < G) ? exp2_le0(y[i][h] - M[h]) : 0.0f;  // M finite there
             l += p;
-            float x[DS];
-            unpack16<T>(vraw[i], x);
+            float x[Elem<T>::kPerLane];
+            if constexpr (PB == 16) unpack16<T>(vraw[i], x);
+            else unpack16<T>(make_uint4(vraw[i].x, vraw[i].y, 0u, 0u), x);  // the first DS values
 #pragma unroll
             for (int e = 0; e < DS; ++e) acc[h * DS + e] = fmaf(p, x[e], acc[h * DS + e]);
         }
         l = wave_sum(l);
         if (lane == 0) s_sum[wave * GP + h] = l;
     }
-    PRISM_TL(kTlAttend, 4);
+    PRISM_TL(kTlAttendD, 3);
     wave_reduce_scatter<NV>(acc);
     {
         constexpr int S = NV >= 16 ? 4 : NV == 8 ? 3 : 2;
@@ -469,7 +475,9 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
             for (int j = 0; j < R; ++j) s_part[wave * NV + (lane >> (6 - S)) * R + j] = acc[j];
         }
     }
+    PRISM_TL(kTlAttendD, 4);
     __syncthreads();
+    PRISM_TL(kTlAttendD, 5);
     if (tid < NV) {
         const int h = tid / DS, e = tid % DS;
         if (h < G) {
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
             }
         }
     }
-    PRISM_TL(kTlAttend, 5);
+    PRISM_TL(kTlAttendD, 6);
 }
 
 // Compute units of the current device (cached per device).
@@ -531,13 +539,21 @@ static hipError_t launch_refine_t(const RefineArgs& a, int agg_max, hipStream_t 
     if constexpr (PRISM_ATTEND_DSPLIT && GP <= 8) {
         // head-dimension split while its grid (D / 16-byte pieces per unit) fits one workgroup per
         // CU: every workgroup gathers all kappa rows, so on fuller grids the rank split is faster
-        constexpr int ns = D / Elem<T>::kPerLane;
+        constexpr int ns = D / Elem<T>::kPerLane;  // 16-byte pieces
+        constexpr bool half_ok = PRISM_ATTEND_D8 && GP * Elem<T>::kPerLane / 2 >= 4;
         if (a.kappa <= kAttendDRanks && int64_t(units) * ns <= int64_t(device_cus())) {
-            if (a.kappa <= kAttendDRanks / 2)
-                launch_k("k_attend", (k_attend_d<T, D, GP, kAttendDRanks / 2>), dim3(ns, units), dim3(kAttendThreads),
-                         st, a);
-            else
-                launch_k("k_attend", (k_attend_d<T, D, GP, kAttendDRanks>), dim3(ns, units), dim3(kAttendThreads), st, a);
+            const bool small = a.kappa <= kAttendDRanks / 2;
+            if constexpr (half_ok) {
+                if (int64_t(units) * 2 * ns <= int64_t(device_cus())) {
+                    const dim3 gd(2 * ns, units);
+                    if (small) launch_k("k_attend", (k_attend_d<T, D, GP, kAttendDRanks / 2, 8>), gd, dim3(kAttendThreads), st, a);
+                    else launch_k("k_attend", (k_attend_d<T, D, GP, kAttendDRanks, 8>), gd, dim3(kAttendThreads), st, a);
+                    return hipGetLastError();
+                }
+            }
+            const dim3 gd(ns, units);
+            if (small) launch_k("k_attend", (k_attend_d<T, D, GP, kAttendDRanks / 2, 16>), gd, dim3(kAttendThreads), st, a);
+            else launch_k("k_attend", (k_attend_d<T, D, GP, kAttendDRanks, 16>), gd, dim3(kAttendThreads), st, a);
             return hipGetLastError();
         }
     }

@@ -38,15 +38,21 @@ __device__ __forceinline__ int scan_chunk_tokens(int64_t Tb, int64_t c0) {
 // four byte-wise dot products of its bit pairs.  Workgroup x of unit y handles chunks
 // x, x + gridDim.x, ...
 template <int KB, int DPL> struct ScanRow;
+#ifndef PRISM_SCAN_LOADS8
+#define PRISM_SCAN_LOADS8 8
+#endif
+#ifndef PRISM_SCAN_LOADS2
+#define PRISM_SCAN_LOADS2 4
+#endif
 template <> struct ScanRow<8, 16> {
     using R = uint4;
-    static constexpr int kLoads = 8;  // loads in flight per lane
+    static constexpr int kLoads = PRISM_SCAN_LOADS8;  // loads in flight per lane
     static __device__ __forceinline__ R load(const int8_t* p) { return load16_stream(p); }
     static __device__ __forceinline__ R zero() { return make_uint4(0u, 0u, 0u, 0u); }
 };
 template <> struct ScanRow<2, 64> {
     using R = uint4;
-    static constexpr int kLoads = 4;  // the q words take the registers of the other four
+    static constexpr int kLoads = PRISM_SCAN_LOADS2;  // the q words take the registers of the other four
     static __device__ __forceinline__ R load(const int8_t* p) { return load16_stream(p); }
     static __device__ __forceinline__ R zero() { return make_uint4(0u, 0u, 0u, 0u); }
 };
@@ -389,7 +395,8 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
     constexpr int QW = DPL / 4;
     constexpr int LPT = D / DPL;
     constexpr int TPW = 64 / LPT;          // tokens per wave-load
-    constexpr int U = KB == 8 ? SR::kLoads : ((NQ <= 2 || kNib) ? SR::kLoads : (NQ <= 8 ? SR::kLoads / 2 : SR::kLoads / 4));
+    constexpr int U0 = KB == 8 ? SR::kLoads : ((NQ <= 2 || kNib) ? SR::kLoads : (NQ <= 8 ? SR::kLoads / 2 : SR::kLoads / 4));
+    constexpr int U = U0 * TPW * NW <= CHW ? U0 : CHW / (TPW * NW);  // a batch per wave to start on
     constexpr int BT = U * TPW;            // tokens per batch
     constexpr int SPL = (BT + 63) / 64;    // a batch's scales (and keys) per lane
     static_assert(CHW % BT == 0 && CHW / BT >= NW, "every wave starts on a batch of its own");
@@ -397,12 +404,11 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
 
     __shared__ uint32_t s_hist[kHistBins];
     __shared__ uint32_t s_key[CHW];  // aggregated int32 dot products, each batch's by its wave
-    __shared__ __attribute__((aligned(16))) int8_t s_q[kMax ? NQ : 1][D];
+    // the query's code vectors (MAX: one per head; SUM: the summed codes or their digits)
+    __shared__ __attribute__((aligned(16))) int8_t s_q[NQ][D];
     __shared__ float s_red[NW];
-    // SUM: the group's query (fp32) for every wave, and each wave's own codes
-    __shared__ float s_qs[kMax ? 1 : kMaxG * 256];
-    __shared__ __attribute__((aligned(16))) int8_t s_qw[kMax ? 1 : NW][kMax ? 1 : NQ][D];
-    __shared__ __attribute__((aligned(16))) uint32_t s_qn[kNib ? NW : 1][kNib ? (D / DPL) * 24 : 4];
+    __shared__ float s_qs[kMax ? 1 : kMaxG * 256];  // SUM: the group's query (fp32)
+    __shared__ __attribute__((aligned(16))) uint32_t s_qn[kNib ? (D / DPL) * 24 : 4];
     __shared__ int32_t s_pg[paged ? CHW / TPW + 2 : 1];
     __shared__ uint32_t s_next;
 
@@ -539,19 +545,30 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
         for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
         __syncthreads();
     } else {
-        // SUM: one barrier.  The group's query goes to LDS as fp32 and the histogram is cleared;
-        // then every wave takes the group's absmax and the codes of every dim on its own (the
-        // same values in every wave), writes them to its own LDS rows and reads back its lanes'
-        // words, so no wave waits for another after the barrier.
+        // SUM: the group's query goes to LDS as fp32 with each wave's absmax, and the histogram
+        // is cleared; after the barrier, thread dd < D forms dim dd's summed code (and its
+        // digits), so the quantization is done once per workgroup rather than once per wave
+        // (16 waves repeating it cost more VALU issue time than the barriers it saved)
+        float amax = 0.0f;
+        const int wu = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
         for (int i = 0; i < QP; ++i) {
+            // a wave without pieces skips the wait for its (clamped, unused) query load, which
+            // sits behind the other waves' row loads
+            if (i * NT + wu * 64 >= npieces) continue;
             const int p = tid + i * NT;
             float x[8];
             if (a.q_bf16) unpack16<uint16_t>(qraw[i], x);
             else unpack16<float>(qraw[i], x);
-            if (p < npieces)
-                for (int e = 0; e < qe; ++e) s_qf[p * qe + e] = x[e];
+            if (p < npieces) {
+                for (int e = 0; e < qe; ++e) {
+                    s_qf[p * qe + e] = x[e];
+                    amax = fmaxf(amax, fabsf(x[e]));
+                }
+            }
         }
+        amax = wave_max(amax);
+        if (lane == 0) s_red[wave] = amax;
         // the work item's first rows are requested once the query is in: issued at the kernel's
         // start they flood the memory system, and the query's few loads wait behind the flood
         PRISM_TL(kTlScan, 1);
@@ -562,50 +579,51 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
         for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
         __syncthreads();
         PRISM_TL(kTlScan, 2);
-        float amax = 0.0f;
-        for (int i = lane; i < G * D; i += 64) amax = fmaxf(amax, fabsf(s_qf[i]));
-        amax = wave_max(amax);
+        amax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) amax = fmaxf(amax, s_red[w]);
         const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-        for (int dd = lane; dd < D; dd += 64) {
-            if constexpr (kNib) {
-                // qs = 256 d2 + 16 d1 + d0 with every digit in [-8, 7] (|qs| <= 15 * 127)
-                int qs = 0;
-                for (int h = 0; h < G; ++h) qs += scan_qcode(s_qf[h * D + dd], inv);
-                const int d0 = ((qs + 8) & 15) - 8;
-                const int r1 = (qs - d0) >> 4;
-                const int d1 = ((r1 + 8) & 15) - 8;
-                s_qw[wave][0][dd] = int8_t(d0);
-                s_qw[wave][1][dd] = int8_t(d1);
-                s_qw[wave][2][dd] = int8_t((r1 - d1) >> 4);
-            } else if constexpr (NQ == 1) {
-                s_qw[wave][0][dd] = int8_t(scan_qcode(s_qf[dd], inv));
+        if (tid < D) {
+            const int dd = tid;
+            if constexpr (NQ == 1) {
+                s_q[0][dd] = int8_t(scan_qcode(s_qf[dd], inv));
             } else {
                 int qs = 0;
                 for (int h = 0; h < G; ++h) qs += scan_qcode(s_qf[h * D + dd], inv);
-                const int lo = ((qs + 8) & 15) - 8;
-                s_qw[wave][0][dd] = int8_t((qs - lo) >> 4);
-                s_qw[wave][1][dd] = int8_t(lo);
+                const int d0 = ((qs + 8) & 15) - 8;
+                if constexpr (kNib) {
+                    // qs = 256 d2 + 16 d1 + d0 with every digit in [-8, 7] (|qs| <= 15 * 127)
+                    const int r1 = (qs - d0) >> 4;
+                    const int d1 = ((r1 + 8) & 15) - 8;
+                    s_q[0][dd] = int8_t(d0);
+                    s_q[1][dd] = int8_t(d1);
+                    s_q[2][dd] = int8_t((r1 - d1) >> 4);
+                } else {  // qs = 16 hi + lo
+                    s_q[0][dd] = int8_t((qs - d0) >> 4);
+                    s_q[1][dd] = int8_t(d0);
+                }
             }
         }
-        __builtin_amdgcn_wave_barrier();  // the wave's LDS writes above precede its reads below
+        __syncthreads();
         if constexpr (kNib) {
             // nibble k of word 2m holds the digit of dim 16m + 8 (k & 1) + (k >> 1), of word 2m + 1
             // that of dim 16m + 4 + 8 (k & 1) + (k >> 1): the order in which the 2-bit codes of one
             // 32-bit key word land in nibbles under the masks 0x33333333 and 0x33333333 << 2.
-            // The wave packs each of its LPT * 24 distinct words once (lane l takes word l, l + 64),
-            // then every lane reads the 24 words of its dims.
+            // Thread l < LPT * 24 packs word l once; then every lane reads the 24 words of its dims.
             constexpr int NWD = LPT * 24;
-            for (int l = lane; l < NWD; l += 64) {
+            static_assert(NWD <= NT, "one thread per packed word");
+            if (tid < NWD) {
+                const int l = tid;
                 const int sb = l / 24, n = (l % 24) / 8, m = (l % 8) / 2, hf = l % 2;
-                const uint32_t* src = reinterpret_cast<const uint32_t*>(&s_qw[wave][n][sb * DPL + 16 * m]);
-                s_qn[wave][l] = (src[hf] & 0x0F0F0F0Fu) | ((src[2 + hf] & 0x0F0F0F0Fu) << 4);
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(&s_q[n][sb * DPL + 16 * m]);
+                s_qn[l] = (src[hf] & 0x0F0F0F0Fu) | ((src[2 + hf] & 0x0F0F0F0Fu) << 4);
             }
-            __builtin_amdgcn_wave_barrier();  // the packed words precede their reads
+            __syncthreads();
 #pragma unroll
             for (int n = 0; n < 3; ++n) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    const uint4 w = *reinterpret_cast<const uint4*>(&s_qn[wave][sub * 24 + 8 * n + 4 * m]);
+                    const uint4 w = *reinterpret_cast<const uint4*>(&s_qn[sub * 24 + 8 * n + 4 * m]);
                     qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
                 }
             }
@@ -614,7 +632,7 @@ __global__ __launch_bounds__(kScanWideThreads) void k_scan_w(ProposeArgs a) {
             for (int n = 0; n < NQ; ++n) {
 #pragma unroll
                 for (int m = 0; m < QW / 4; ++m) {
-                    const uint4 w = *reinterpret_cast<const uint4*>(&s_qw[wave][n][sub * DPL + 16 * m]);
+                    const uint4 w = *reinterpret_cast<const uint4*>(&s_q[n][sub * DPL + 16 * m]);
                     qv[n][4 * m] = int(w.x); qv[n][4 * m + 1] = int(w.y); qv[n][4 * m + 2] = int(w.z); qv[n][4 * m + 3] = int(w.w);
                 }
             }
