@@ -2,8 +2,10 @@
 stores, an arrival counter, the last workgroup's merge): a whole step captured in a HIP graph and
 replayed 2000 times per shape, every replay's pools, index sets, outputs and lse compared bit for bit
 with the eager step on the device, checked every 200 replays and at the end (the first bad batch
-fails the test).  Shapes: one unit and five units (their attention workgroups fall on several XCDs, so
-partials cross XCDs) and 64 units (each unit's workgroups on one XCD)."""
+fails the test).  Every shape takes the rank-split attention, the one with the hand-off (kappa above
+what the head-dimension split takes, or more units than its grid fits): one unit and five units at
+kappa = 4096 (their attention workgroups fall on several XCDs, so partials cross XCDs, and 32 slices
+per unit take the two-level merge) and 64 units at kappa = 1024 (each unit's workgroups on one XCD)."""
 import pytest
 import torch
 
@@ -15,8 +17,8 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [
     # name, config overrides
-    ("1 unit", dict(B=1, Hq=8, Hkv=1, T=65536, kp=8192, kappa=2048, n_refined=3)),
-    ("5 units", dict(B=1, Hq=20, Hkv=5, T=32768, kp=4096, kappa=2048, n_refined=3)),
+    ("1 unit", dict(B=1, Hq=8, Hkv=1, T=65536, kp=8192, kappa=4096, n_refined=3)),
+    ("5 units", dict(B=1, Hq=20, Hkv=5, T=32768, kp=8192, kappa=4096, n_refined=3)),
     ("64 units", dict(B=8, Hq=32, Hkv=8, T=20000, kp=4096, kappa=1024, n_refined=3, seq_lens=None)),
 ]
 
@@ -25,6 +27,10 @@ SHAPES = [
 @pytest.mark.parametrize("name,ov", SHAPES, ids=[s[0].replace(" ", "") for s in SHAPES])
 def test_graph_replay_soak(name, ov):
     c = W.CONFIGS["cfg2"].with_(**ov)
+    # the launcher takes the head-dimension split (no hand-off) for kappa <= 2048 when the unit count
+    # times the D / 8 sixteen-byte bf16 pieces fits the CUs; keep every shape off it
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert c.kappa > 2048 or c.B * c.Hkv * (c.D // 8) > cus, "shape would not exercise the hand-off"
     w = W.generate(c)
     dev = lambda x: torch.from_numpy(x).to(device="cuda", dtype=torch.bfloat16)
     ld = torch.from_numpy(w.seq_lens).cuda()
