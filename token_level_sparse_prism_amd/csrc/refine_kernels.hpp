@@ -478,19 +478,18 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_d(RefineArgs a) {
     PRISM_TL(kTlAttendD, 4);
     __syncthreads();
     PRISM_TL(kTlAttendD, 5);
-    if (tid < NV) {
-        const int h = tid / DS, e = tid % DS;
-        if (h < G) {
-            float Mh = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_max[w * GP + h]);  // finite: n >= 1
-            float sacc = 0.0f, L = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float c = exp2_le0(s_max[w * GP + h] - Mh);  // 0 for a wave without rows
-                sacc = fmaf(s_part[w * NV + tid], c, sacc);
-                L = fmaf(s_sum[w * GP + h], c, L);
-            }
+    // the waves' sums: output o = h DS + e takes one row of 16 lanes, lane w holding wave w's
+    // maximum, rescaled sum and weight sum; DPP reductions inside the row
+    static_assert(NW == 16 && NV * NW <= NT, "one DPP row of 16 lanes per output");
+    if (tid < NV * NW) {
+        const int o = tid / NW, w = tid % NW;
+        const int h = o / DS, e = o % DS;
+        const float mw = h < G ? s_max[w * GP + h] : 0.0f;
+        const float Mh = group_max<16>(mw);  // finite where h < G: n >= 1
+        const float c = h < G ? exp2_le0(mw - Mh) : 0.0f;  // 0 for a wave without rows
+        const float sacc = group_sum<16>(s_part[w * NV + o] * c);
+        const float L = group_sum<16>(s_sum[w * GP + h] * c);
+        if (w == 0 && h < G) {
             store_elem<T>(&out[int64_t(h) * D + e], sacc / L);
             if (e == 0 && piece == 0 && lse) {
                 constexpr float kLn2 = 0.6931471805599453f;
