@@ -400,6 +400,7 @@ template <int NT>
 __device__ __forceinline__ SelResult select_ranks(const uint2* __restrict__ gk, int64_t kp, uint32_t kappa, int r0, int nmax, uint32_t* s_hist,
                                                   uint32_t* s_tmp, uint32_t* s_res, uint32_t* s_cand,
                                                   uint32_t* s_ccount, int32_t* s_slot, int32_t* s_tok) {
+    constexpr int NW = NT / 64;
     constexpr int ROWS = sel_rows<NT>();
     constexpr int CPW = sel_cand_per_wave<NT>();
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
