@@ -240,6 +240,8 @@ REFINE_CASES = [
     (128, 4, 1, PB.AGG_SUM, "bf16", 6000, 4096, 2048, None),       # head-dim split: most rows (2048)
     (64, 8, 1, PB.AGG_MAX, "f32", 4000, 3000, 1025, None),         # head-dim split: 2048-row variant
     (128, 2, 16, PB.AGG_SUM, "bf16", 2000, 1500, 700, None),       # head-dim split, 16-byte pieces (16 units)
+    (128, 8, 16, PB.AGG_MAX, "bf16", 1500, 1024, 600, None),       # head-dim split, 16-byte pieces, 8 heads:
+                                                                   # 64 sums per lane, the final sum on all threads
     (256, 8, 1, PB.AGG_MAX, "bf16", 9000, 8000, 4000, None),       # column quarters, two-level merge
     (128, 4, 1, PB.AGG_SUM, "bf16", 8000, 6000, 3000, None),       # column halves, two-level merge
     (64, 2, 16, PB.AGG_SUM, "bf16", 1500, 1024, 1024, [1500] * 8),  # 128 units: 512 ranks per workgroup
